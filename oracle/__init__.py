@@ -1,0 +1,242 @@
+"""CPU oracle of the W8A8 post-training-quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: a plain, slow implementation the GPU library is
+checked against.  Only tests/, the smoke check of __graft_entry__ and the
+CPU-baseline leg of bench.py may import it.  The product path
+(post_int8_quantization_amd) never does, and the two share no code.
+
+The arithmetic lives in ptq_oracle.c (scalar C, fp64 sums, IEEE fp32,
+compiled without fast-math and without FMA contraction); this module is
+ctypes marshalling plus `run_linear`, which chains the steps in the order of
+the PTQ flow (calibrate -> smoothing factors -> weight qparams -> per-token
+activation quantization -> integer GEMM -> dequantization).
+
+Functions with no independent pin: none at present; every step is pinned by
+tests/test_oracle_pins.py (rounding table, closed forms, brute force, exact
+special cases, invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ptq_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so in place with gcc."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build(force=False)
+        lib = ctypes.CDLL(_SO)
+        i64, f32, f64, vp, ci = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+        sig = {
+            "o_absmax_cols": [vp, i64, i64, vp, ci],
+            "o_smooth_factors": [vp, vp, i64, f32, vp],
+            "o_fold_weight": [vp, vp, i64, i64, vp],
+            "o_fold_act": [vp, vp, i64, i64, vp],
+            "o_quant_row": [vp, i64, f32, ci, vp],
+            "o_lsq_scale": [vp, vp, i64],
+            "o_mse_row": [vp, vp, i64, f32],
+            "o_ssz": [vp, vp, i64, i64, ci, ci, f64, f32, vp, vp, vp, vp, vp],
+            "o_minmax_per_tensor": [vp, i64, i64, ci, f32, vp, vp],
+            "o_pack_int4": [vp, i64, i64, vp],
+            "o_quant_per_token": [vp, vp, i64, i64, vp, vp],
+            "o_gemm_i8": [vp, vp, i64, i64, i64, vp],
+            "o_dequant": [vp, vp, vp, i64, i64, vp],
+        }
+        for name, argt in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argt
+            fn.restype = ci
+        lib.o_lsq_scale.restype = f64
+        lib.o_mse_row.restype = f64
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what}: oracle status {rc}")
+
+
+def absmax_cols(x, amax=None):
+    """Column absmax of a [rows, cols] array; folds into `amax` when given."""
+    x = _f32(x)
+    rows, cols = x.shape
+    acc = amax is not None
+    out = _f32(amax).copy() if acc else np.empty(cols, dtype=np.float32)
+    _check(_load().o_absmax_cols(x.ctypes.data, rows, cols, out.ctypes.data, int(acc)), "absmax_cols")
+    return out
+
+
+def smooth_factors(ax, aw, alpha):
+    ax, aw = _f32(ax), _f32(aw)
+    s = np.empty_like(ax)
+    _check(_load().o_smooth_factors(ax.ctypes.data, aw.ctypes.data, ax.size, float(alpha), s.ctypes.data),
+           "smooth_factors")
+    return s
+
+
+def fold_weight(w, s):
+    w = _f32(w)
+    s = None if s is None else _f32(s)
+    out = np.empty_like(w)
+    _check(_load().o_fold_weight(w.ctypes.data, _p(s), w.shape[0], w.shape[1], out.ctypes.data), "fold_weight")
+    return out
+
+
+def fold_act(x, s):
+    x = _f32(x)
+    s = None if s is None else _f32(s)
+    out = np.empty_like(x)
+    _check(_load().o_fold_act(x.ctypes.data, _p(s), x.shape[0], x.shape[1], out.ctypes.data), "fold_act")
+    return out
+
+
+def quant_row(r, S, qmax):
+    r = _f32(r).ravel()
+    q = np.empty(r.size, dtype=np.int8)
+    _check(_load().o_quant_row(r.ctypes.data, r.size, float(S), int(qmax), q.ctypes.data), "quant_row")
+    return q
+
+
+def mse_row(wh, q, S):
+    wh = _f32(wh).ravel()
+    q = np.ascontiguousarray(q, dtype=np.int8).ravel()
+    return _load().o_mse_row(wh.ctypes.data, q.ctypes.data, wh.size, float(S))
+
+
+def lsq_scale(wh, q):
+    wh = _f32(wh).ravel()
+    q = np.ascontiguousarray(q, dtype=np.int8).ravel()
+    return _load().o_lsq_scale(wh.ctypes.data, q.ctypes.data, wh.size)
+
+
+def ssz(w, s=None, bits=8, max_iter=20, thr=1e-10, min_scale=1e-5, hist=False):
+    """MinMax + SSZ per row.  Returns dict(S, q (codes, one per byte), iters, mse[, hist])."""
+    w = _f32(w)
+    N, K = w.shape
+    s = None if s is None else _f32(s)
+    S = np.empty(N, dtype=np.float32)
+    q = np.empty((N, K), dtype=np.int8)
+    it = np.empty(N, dtype=np.int32)
+    mse = np.empty(N, dtype=np.float64)
+    h = np.full((N, max_iter + 1), np.nan, dtype=np.float64) if hist else None
+    _check(_load().o_ssz(w.ctypes.data, _p(s), N, K, int(bits), int(max_iter), float(thr), float(min_scale),
+                         S.ctypes.data, q.ctypes.data, it.ctypes.data, mse.ctypes.data, _p(h)), "ssz")
+    out = dict(S=S, q=q, iters=it, mse=mse)
+    if hist:
+        out["hist"] = h
+    return out
+
+
+def minmax_per_tensor(w, bits=8, min_scale=1e-5):
+    w = _f32(w)
+    N, K = w.shape
+    S = np.empty(1, dtype=np.float32)
+    q = np.empty((N, K), dtype=np.int8)
+    _check(_load().o_minmax_per_tensor(w.ctypes.data, N, K, int(bits), float(min_scale), S.ctypes.data,
+                                       q.ctypes.data), "minmax_per_tensor")
+    return float(S[0]), q
+
+
+def pack_int4(q):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    N, K = q.shape
+    out = np.empty((N, K // 2), dtype=np.uint8)
+    _check(_load().o_pack_int4(q.ctypes.data, N, K, out.ctypes.data), "pack_int4")
+    return out
+
+
+def quant_per_token(x, s=None):
+    x = _f32(x)
+    T, K = x.shape
+    s = None if s is None else _f32(s)
+    xq = np.empty((T, K), dtype=np.int8)
+    d = np.empty(T, dtype=np.float32)
+    _check(_load().o_quant_per_token(x.ctypes.data, _p(s), T, K, xq.ctypes.data, d.ctypes.data), "quant_per_token")
+    return xq, d
+
+
+def gemm_i8(xq, wq):
+    """acc = Xq Wq^T in int64; raises if any sum leaves int32."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K
+    acc = np.empty((M, N), dtype=np.int64)
+    _check(_load().o_gemm_i8(xq.ctypes.data, wq.ctypes.data, M, N, K, acc.ctypes.data), "gemm_i8")
+    return acc
+
+
+def dequant(acc, delta, S):
+    acc = np.ascontiguousarray(acc, dtype=np.int64)
+    delta, S = _f32(delta), _f32(S)
+    M, N = acc.shape
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load().o_dequant(acc.ctypes.data, delta.ctypes.data, S.ctypes.data, M, N, y.ctypes.data), "dequant")
+    return y
+
+
+def run_linear(x_calib, w, x_eval, alpha=0.5, smooth=True, bits=8, max_iter=20, thr=1e-10, min_scale=1e-5,
+               w_rows=None, x_rows=None):
+    """The whole path for one linear layer, steps in the PTQ-flow order.
+
+    x_calib: list of [T,K] float32 calibration batches; w: [N,K] float32;
+    x_eval: [T,K] float32 forward batch.  w_rows / x_rows restrict the weight
+    quantization and the forward to a subset of rows (all rows are still used
+    for calibration), which is how large shapes are sampled.
+    """
+    out = {}
+    if smooth:
+        ax = None
+        for xb in x_calib:
+            ax = absmax_cols(xb, ax)
+        aw = absmax_cols(w)
+        s = smooth_factors(ax, aw, alpha)
+        out.update(ax=ax, aw=aw, s=s)
+    else:
+        s = None
+        out["s"] = None
+    wsel = w if w_rows is None else w[w_rows]
+    q = ssz(wsel, s, bits, max_iter, thr, min_scale)
+    out.update(S=q["S"], wq=q["q"], iters=q["iters"], mse=q["mse"])
+    if x_eval is not None:
+        xsel = x_eval if x_rows is None else x_eval[x_rows]
+        xq, d = quant_per_token(xsel, s)
+        out.update(xq=xq, delta=d)
+        if bits == 8:
+            acc = gemm_i8(xq, q["q"])
+            out.update(acc=acc, y=dequant(acc, d, q["S"]))
+    return out

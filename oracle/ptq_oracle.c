@@ -1,0 +1,390 @@
+/*
+ * ptq_oracle.c -- the CPU oracle of the W8A8 post-training-quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is a plain, slow, scalar implementation
+ * that the GPU path is checked against.  Only the tests, the smoke check and
+ * the bench's CPU-baseline leg may load it; the product path never does.  It
+ * shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (the pages):
+ *   [PTQ]  tutorial chapter "4. 训练后量化（PTQ）": the four-step flow
+ *          ("PTQ 的基本流程") and per-layer vs per-channel granularity
+ *          ("逐层量化 vs 逐通道量化").
+ *   [SSZ]  msModelSlim document "SSZ：权重量化算法说明": algorithm flow
+ *          ("算法流程"), initialisation ("初始化阶段"), iteration
+ *          ("迭代优化阶段"), convergence ("收敛判断"), limits ("使用限制"),
+ *          constants ("算法参数").
+ *   [SQ]   article "SmoothQuant大模型量化技术深度解析", section
+ *          "一、SmoothQuant技术原理": the smoothing factor s_j and the
+ *          equivalent rescaling of activations and weights.
+ *   [INT8] CSDN article on CUDA INT8 inference: section 2.1 (linear
+ *          quantization Q = round(R/S) + Z, range calibration, parameter
+ *          computation, saturation), 2.2 (granularity), 3.2 (INT8 GEMM with
+ *          integer accumulation), 4.2 (quantize -> op -> dequantize fusion).
+ *
+ * Arithmetic conventions (the pages fix no precision; these readings are the
+ * oracle's definition and the GPU path must reproduce them):
+ *   - fl32(.) is IEEE binary32 round-to-nearest-even.  This file is compiled
+ *     with -O2 -fno-fast-math -ffp-contract=off so no product is fused into a
+ *     following add and float expressions stay in float.
+ *   - R / S is evaluated as fl32(R * fl32(1/S)): the scale's reciprocal is
+ *     rounded to fp32 once, then multiplied.
+ *   - round() is round-half-to-even (nearbyintf under the default rounding
+ *     mode), then saturation to [-qmax, qmax], qmax = 127 (int8) or 7 (int4);
+ *     symmetric, so the zero point Z is 0.
+ *   - sums of squares and cross products are fp64, k ascending.
+ *
+ * Every function takes host pointers to row-major, K-contiguous arrays and
+ * returns 0 on success, a negative value on a bad argument or a non-finite
+ * input.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define O_OK 0
+#define O_EARG -1
+#define O_ENONFINITE -2
+#define O_EOVERFLOW -3
+
+static int all_finite(const float* a, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (!isfinite(a[i])) return 0;
+  return 1;
+}
+
+/* ---------------------------------------------------------------------------
+ * Range calibration: column-wise absolute maximum.
+ * [SQ] max(|X_j|) over the calibration activations of channel j, and
+ * max(|W_j|) over input channel j of the weight (the channel shared with X,
+ * which is the only choice that keeps the rescaling equivalent).  [INT8] 2.1:
+ * the dynamic range comes from statistics over a calibration set.  Several
+ * calibration batches fold in as a running maximum (accumulate != 0).
+ * ------------------------------------------------------------------------- */
+int o_absmax_cols(const float* x, int64_t rows, int64_t cols, float* amax, int accumulate) {
+  if (!x || !amax || rows < 0 || cols <= 0) return O_EARG;
+  if (!all_finite(x, rows * cols)) return O_ENONFINITE;
+  if (!accumulate)
+    for (int64_t j = 0; j < cols; ++j) amax[j] = 0.0f;
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) {
+      float a = fabsf(x[i * cols + j]);
+      if (a > amax[j]) amax[j] = a;
+    }
+  return O_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Smoothing factor.  [SQ] s_j = max|X_j|^alpha / max|W_j|^(1-alpha),
+ * alpha in [0,1].  Evaluated in fp64 and rounded once to fp32.  A channel
+ * whose activation or weight maximum is 0 gets s_j = 1 (no smoothing; the
+ * pages do not cover it).
+ * ------------------------------------------------------------------------- */
+int o_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, float* s) {
+  if (!ax || !aw || !s || K <= 0) return O_EARG;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return O_EARG;
+  double a = (double)alpha;
+  for (int64_t j = 0; j < K; ++j) {
+    if (ax[j] == 0.0f || aw[j] == 0.0f) {
+      s[j] = 1.0f;
+      continue;
+    }
+    double v = pow((double)ax[j], a) / pow((double)aw[j], 1.0 - a);
+    s[j] = (float)v;
+  }
+  return O_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Folding the smoothing into the operands.  [SQ] the activations of channel j
+ * are divided by s_j and the weights of input channel j multiplied by s_j, so
+ * (X diag(s)^-1)(diag(s) W^T) = X W^T.
+ *   w_hat[n,j] = fl32(W[n,j] * s_j)
+ *   x_hat[t,j] = fl32(X[t,j] * fl32(1/s_j))
+ * With s == NULL both are the identity.
+ * ------------------------------------------------------------------------- */
+int o_fold_weight(const float* w, const float* s, int64_t N, int64_t K, float* wh) {
+  if (!w || !wh || N < 0 || K <= 0) return O_EARG;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < K; ++j) wh[n * K + j] = s ? w[n * K + j] * s[j] : w[n * K + j];
+  return O_OK;
+}
+
+int o_fold_act(const float* x, const float* s, int64_t T, int64_t K, float* xh) {
+  if (!x || !xh || T < 0 || K <= 0) return O_EARG;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < K; ++j) {
+      if (s) {
+        float r = 1.0f / s[j];
+        xh[t * K + j] = x[t * K + j] * r;
+      } else {
+        xh[t * K + j] = x[t * K + j];
+      }
+    }
+  return O_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Linear quantization, symmetric.  [INT8] 2.1: Q = round(R/S) + Z followed by
+ * saturation to the representable range; Z = 0 for symmetric quantization
+ * ([SSZ] iteration stage: symmetric keeps the offset at 0).
+ *   code = clamp(rne(fl32(R * fl32(1/S))), -qmax, qmax)
+ * ------------------------------------------------------------------------- */
+static int code_of(float r, float inv_s, int qmax) {
+  float t = r * inv_s;
+  float q = nearbyintf(t);
+  if (q > (float)qmax) q = (float)qmax;
+  if (q < (float)-qmax) q = (float)-qmax;
+  return (int)q;
+}
+
+int o_quant_row(const float* r, int64_t K, float S, int qmax, int8_t* q) {
+  if (!r || !q || K <= 0 || !(S > 0.0f) || qmax <= 0 || qmax > 127) return O_EARG;
+  float inv = 1.0f / S;
+  for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_of(r[k], inv, qmax);
+  return O_OK;
+}
+
+/* Quantization error of one channel: mean of (w_hat - S*q)^2 over its K
+ * elements, fp64, k ascending.  ([SSZ] compares "quantization error"; the
+ * mean is this oracle's reading.) */
+double o_mse_row(const float* wh, const int8_t* q, int64_t K, float S) {
+  double acc = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double d = (double)wh[k] - (double)S * (double)q[k];
+    acc += d * d;
+  }
+  return acc / (double)K;
+}
+
+/* Least-squares scale for fixed codes: argmin_S sum (w_hat - S q)^2 =
+ * sum(w_hat q) / sum(q^2).  Returns the fp64 quotient, or 0 when sum(q^2)=0.
+ * ([SSZ] each iteration fits the scale by least squares.) */
+double o_lsq_scale(const float* wh, const int8_t* q, int64_t K) {
+  double A = 0.0;
+  int64_t B = 0;
+  for (int64_t k = 0; k < K; ++k) {
+    A += (double)wh[k] * (double)q[k];
+    B += (int64_t)q[k] * (int64_t)q[k];
+  }
+  return B == 0 ? 0.0 : A / (double)B;
+}
+
+/* ---------------------------------------------------------------------------
+ * SSZ, symmetric per-channel, one row (= one output channel).
+ *
+ * [SSZ] flow: MinMax initial parameters; least-squares update; keep the new
+ * parameters only if the quantization error improves; repeat until converged
+ * or the iteration limit; symmetric keeps offset 0 and optimises the scale
+ * only.  Constants: at most 20 iterations, convergence threshold 1e-10,
+ * minimum scale 1e-5 (passed in).  Convergence: relative change
+ * (best - cur)/best < thr or absolute change |best - cur| < thr.
+ *
+ * Readings taken where the document is silent:
+ *   - MinMax init: S0 = max(fl32(max_k |w_hat_k| / qmax), fl32(min_scale)).
+ *   - each least-squares step refits S for the codes of the current S:
+ *     S' = max(fl32(A/B), fl32(min_scale)), A = sum w_hat q (fp64),
+ *     B = sum q^2 (exact); B == 0 leaves nothing to fit and ends the row.
+ *   - a candidate is kept only if strictly better (cur < best).
+ *   - either convergence test ends the row; d = best - cur is signed, so a
+ *     rejected candidate (d <= 0) also ends it (the next step would rebuild
+ *     the same candidate).  best == 0 counts as converged.
+ *   - each row stops on its own ("all channels converged" then ends the
+ *     whole search).
+ *   - iters = number of least-squares steps entered (0 when max_iter = 0).
+ * hist (may be NULL) receives best after the init (index 0) and after each
+ * step entered (index i); entries after the last step are left untouched.
+ * ------------------------------------------------------------------------- */
+static void ssz_one_row(const float* wh, int64_t K, int qmax, int max_iter, double thr, float min_scale,
+                        float* S_out, int8_t* q, int32_t* iters_out, double* mse_out, double* hist,
+                        int8_t* qc) {
+  float m = 0.0f;
+  for (int64_t k = 0; k < K; ++k) {
+    float a = fabsf(wh[k]);
+    if (a > m) m = a;
+  }
+  float S = m / (float)qmax;
+  if (S < min_scale) S = min_scale;
+  o_quant_row(wh, K, S, qmax, q);
+  double best = o_mse_row(wh, q, K, S);
+  if (hist) hist[0] = best;
+
+  double A = 0.0;
+  int64_t B = 0;
+  for (int64_t k = 0; k < K; ++k) {
+    A += (double)wh[k] * (double)q[k];
+    B += (int64_t)q[k] * (int64_t)q[k];
+  }
+
+  int it = 0;
+  for (int i = 1; i <= max_iter; ++i) {
+    it = i;
+    if (B == 0) break;
+    float Sc = (float)(A / (double)B);
+    if (Sc < min_scale) Sc = min_scale;
+    o_quant_row(wh, K, Sc, qmax, qc);
+    double cur = o_mse_row(wh, qc, K, Sc);
+    double d = best - cur;
+    int conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+    if (cur < best) {
+      S = Sc;
+      best = cur;
+      memcpy(q, qc, (size_t)K);
+      A = 0.0;
+      B = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        A += (double)wh[k] * (double)q[k];
+        B += (int64_t)q[k] * (int64_t)q[k];
+      }
+    }
+    if (hist) hist[i] = best;
+    if (conv) break;
+  }
+  *S_out = S;
+  if (iters_out) *iters_out = it;
+  if (mse_out) *mse_out = best;
+}
+
+/*
+ * Weight quantization parameters for a [N,K] weight: fold s (may be NULL),
+ * then MinMax + SSZ per row.  bits 8 -> qmax 127, bits 4 -> qmax 7 ([SSZ]
+ * limits: int8 and int4, per-channel, symmetric; the weight is 2-D).
+ * Outputs: S[N], q[N,K] codes (one code per byte), iters[N], mse[N] (any of
+ * iters/mse/hist may be NULL); hist is [N, max_iter+1].
+ */
+int o_ssz(const float* w, const float* s, int64_t N, int64_t K, int bits, int max_iter, double thr,
+          float min_scale, float* S, int8_t* q, int32_t* iters, double* mse, double* hist) {
+  if (!w || !S || !q || N < 0 || K <= 0) return O_EARG;
+  if (bits != 8 && bits != 4) return O_EARG;
+  if (max_iter < 0 || !(thr >= 0.0) || !(min_scale > 0.0f)) return O_EARG;
+  if (!all_finite(w, N * K)) return O_ENONFINITE;
+  const int qmax = bits == 8 ? 127 : 7;
+  int bad = 0;
+#pragma omp parallel
+  {
+    float* wh = (float*)malloc(sizeof(float) * (size_t)K);
+    int8_t* qc = (int8_t*)malloc((size_t)K);
+    if (!wh || !qc) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t n = 0; n < N; ++n) {
+        o_fold_weight(w + n * K, s, 1, K, wh);
+        ssz_one_row(wh, K, qmax, max_iter, thr, min_scale, S + n, q + n * K, iters ? iters + n : NULL,
+                    mse ? mse + n : NULL, hist ? hist + n * (int64_t)(max_iter + 1) : NULL, qc);
+      }
+    }
+    free(wh);
+    free(qc);
+  }
+  return bad ? O_EARG : O_OK;
+}
+
+/* Per-tensor (per-layer) MinMax for comparison with per-channel ([PTQ]
+ * granularity section): one S for the whole tensor,
+ * S = max(fl32(max|W| / qmax), fl32(min_scale)); codes for every row. */
+int o_minmax_per_tensor(const float* w, int64_t N, int64_t K, int bits, float min_scale, float* S_out,
+                        int8_t* q) {
+  if (!w || !S_out || !q || N <= 0 || K <= 0 || (bits != 8 && bits != 4)) return O_EARG;
+  const int qmax = bits == 8 ? 127 : 7;
+  float m = 0.0f;
+  for (int64_t i = 0; i < N * K; ++i) {
+    float a = fabsf(w[i]);
+    if (a > m) m = a;
+  }
+  float S = m / (float)qmax;
+  if (S < min_scale) S = min_scale;
+  for (int64_t n = 0; n < N; ++n) o_quant_row(w + n * K, K, S, qmax, q + n * K);
+  *S_out = S;
+  return O_OK;
+}
+
+/* int4 storage: byte i of a row holds element 2i in the low nibble and
+ * element 2i+1 in the high nibble, each a 4-bit two's-complement code.
+ * (The SSZ document supports int4 codes but gives no storage format; this is
+ * the library's.) */
+int o_pack_int4(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
+  if (!q || !packed || N < 0 || K <= 0 || (K & 1)) return O_EARG;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t i = 0; i < K / 2; ++i) {
+      uint8_t lo = (uint8_t)q[n * K + 2 * i] & 0xF, hi = (uint8_t)q[n * K + 2 * i + 1] & 0xF;
+      packed[n * (K / 2) + i] = (uint8_t)(lo | (hi << 4));
+    }
+  return O_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Per-token dynamic activation quantization, int8, symmetric.  One scale per
+ * token row computed from that row at run time; the smoothing fold X/s is
+ * applied first.
+ *   a_t = max_j |x_hat[t,j]|,  delta_t = a_t > 0 ? fl32(a_t / 127) : 1,
+ *   Xq[t,j] = clamp(rne(fl32(x_hat[t,j] * fl32(1/delta_t))), -127, 127).
+ * ([SQ] per-channel activation scales do not fit integer GEMM kernels, which
+ * is why the activation scale varies per token and the channel variation is
+ * moved into the weights; [INT8] 2.1 for the formula; section 6 closes on
+ * dynamic quantization.)
+ * ------------------------------------------------------------------------- */
+int o_quant_per_token(const float* x, const float* s, int64_t T, int64_t K, int8_t* xq, float* delta) {
+  if (!x || !xq || !delta || T < 0 || K <= 0) return O_EARG;
+  if (!all_finite(x, T * K)) return O_ENONFINITE;
+  int bad = 0;
+#pragma omp parallel
+  {
+    float* xh = (float*)malloc(sizeof(float) * (size_t)K);
+    if (!xh) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t t = 0; t < T; ++t) {
+        o_fold_act(x + t * K, s, 1, K, xh);
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+          float v = fabsf(xh[j]);
+          if (v > a) a = v;
+        }
+        float d = a > 0.0f ? a / 127.0f : 1.0f;
+        float inv = 1.0f / d;
+        for (int64_t j = 0; j < K; ++j) xq[t * K + j] = (int8_t)code_of(xh[j], inv, 127);
+        delta[t] = d;
+      }
+    }
+    free(xh);
+  }
+  return bad ? O_EARG : O_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Integer GEMM.  [INT8] 3.2: int8 x int8 products accumulated in integers;
+ * both operands are K-contiguous (the snippet loads both tiles with leading
+ * dimension K).  acc[t,n] = sum_k Xq[t,k] * Wq[n,k], in int64; returns
+ * O_EOVERFLOW if any sum leaves the int32 range ([INT8] 5.1 overflow).
+ * ------------------------------------------------------------------------- */
+int o_gemm_i8(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K, int64_t* acc) {
+  if (!xq || !wq || !acc || M < 0 || N < 0 || K <= 0) return O_EARG;
+  int ovf = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < M; ++t)
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t a = 0;
+      for (int64_t k = 0; k < K; ++k) a += (int64_t)xq[t * K + k] * (int64_t)wq[n * K + k];
+      acc[t * N + n] = a;
+      if (a > INT32_MAX || a < INT32_MIN) {
+#pragma omp atomic write
+        ovf = 1;
+      }
+    }
+  return ovf ? O_EOVERFLOW : O_OK;
+}
+
+/* Dequantization, the inverse of Q = round(R/S) with Z = 0 for both operands:
+ * y[t,n] = acc[t,n] * delta_t * S_n, fp64 (the reference output; the GPU
+ * writes fp32). */
+int o_dequant(const int64_t* acc, const float* delta, const float* S, int64_t M, int64_t N, double* y) {
+  if (!acc || !delta || !S || !y || M < 0 || N < 0) return O_EARG;
+  for (int64_t t = 0; t < M; ++t)
+    for (int64_t n = 0; n < N; ++n) y[t * N + n] = (double)acc[t * N + n] * (double)delta[t] * (double)S[n];
+  return O_OK;
+}

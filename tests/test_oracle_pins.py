@@ -1,0 +1,402 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with a copy of itself: each checks a value
+printed or implied by the pages (golden files), a closed form, an exact special
+case, a brute-force search, a textbook/library routine, or an invariant that
+a dropped term, a wrong sign, a wrong axis or a transposed operand breaks.
+CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import read_golden
+
+U = 2.0 ** -24  # unit roundoff of binary32
+
+
+def f32(x):
+    return np.float32(x)
+
+
+# ---------------------------------------------------------------- rounding (pin 1)
+
+def test_rounding_table_golden():
+    """Ties to even and saturation, from the golden table (quantizer at S = 1)."""
+    for r, qmax, want in read_golden("rounding_table.txt"):
+        got = oracle.quant_row(np.array([float(r)], dtype=np.float32), 1.0, int(qmax))[0]
+        assert got == int(want), (r, qmax, got, want)
+
+
+def test_rounding_power_of_two_scale():
+    """S a power of two makes R*(1/S) exact, so the code is the library rint of R/S."""
+    rng = np.random.default_rng(1)
+    for S in (0.5, 0.125, 2.0 ** -12, 4.0):
+        r = (rng.standard_normal(20000) * 60 * S).astype(np.float32)
+        ties = (np.arange(-130, 130) + 0.5).astype(np.float32) * np.float32(S)
+        r = np.concatenate([r, ties])
+        want = np.clip(np.rint(r.astype(np.float64) / S), -127, 127).astype(np.int8)
+        np.testing.assert_array_equal(oracle.quant_row(r, S, 127), want)
+
+
+def test_rounding_matches_rint_of_rounded_product():
+    """General S: the code is numpy's rint (ties-to-even) of the fp32 product with the fp32 reciprocal."""
+    rng = np.random.default_rng(2)
+    for _ in range(20):
+        S = np.float32(rng.uniform(1e-4, 1.0))
+        r = (rng.standard_normal(5000) * 50 * S).astype(np.float32)
+        inv = np.float32(1.0) / S
+        want = np.clip(np.rint(r * inv), -127, 127).astype(np.int8)
+        np.testing.assert_array_equal(oracle.quant_row(r, S, 127), want)
+
+
+# ---------------------------------------------------------------- smoothing (pins 2, 4)
+
+def test_smoothing_invariance_fp32_bound():
+    """(X diag(s)^-1)(diag(s) W^T) = X W^T; on the fp32-folded operands each product carries
+    at most three roundings, so |x_hat w_hat - x w| <= 3.01 u |x w| term by term."""
+    rng = np.random.default_rng(3)
+    T, K, N = 12, 48, 10
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, 5] *= 80
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    s = np.exp(rng.uniform(-4, 4, K)).astype(np.float32)
+    xh = oracle.fold_act(x, s).astype(np.float64)
+    wh = oracle.fold_weight(w, s).astype(np.float64)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    got = xh @ wh.T
+    bound = 3.01 * U * (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T)
+    assert np.all(np.abs(got - ref) <= bound)
+    # dividing both operands by s (a dropped inverse) breaks the identity by far
+    bad = (x.astype(np.float64) / s) @ (w.astype(np.float64) / s).T
+    assert np.max(np.abs(bad - ref)) > 1e3 * np.max(bound)
+
+
+def test_fold_none_is_identity():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 32)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.fold_act(x, None), x)
+    np.testing.assert_array_equal(oracle.fold_weight(x, None), x)
+
+
+def test_smoothing_closed_forms():
+    """alpha = 0 -> s = 1/a_w; alpha = 1 -> s = a_x; alpha = 1/2 -> s = sqrt(a_x/a_w)."""
+    rng = np.random.default_rng(5)
+    K = 257
+    ax = np.exp(rng.uniform(-3, 5, K)).astype(np.float32)
+    aw = np.exp(rng.uniform(-7, 0, K)).astype(np.float32)
+    s0 = oracle.smooth_factors(ax, aw, 0.0)
+    np.testing.assert_array_equal(s0, (1.0 / aw.astype(np.float64)).astype(np.float32))
+    s1 = oracle.smooth_factors(ax, aw, 1.0)
+    np.testing.assert_array_equal(s1, ax)
+    sh = oracle.smooth_factors(ax, aw, 0.5).astype(np.float64)
+    ref = np.sqrt(ax.astype(np.float64) / aw.astype(np.float64))
+    assert np.max(np.abs(sh - ref) / ref) <= 1.01 * U
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.25, 0.5, 0.8, 1.0])
+def test_smoothing_migrates_range(alpha):
+    """After folding, max|x_hat_j| = (a_x a_w)^(1-alpha) and max|w_hat_j| = (a_x a_w)^alpha."""
+    c = synth.cases("tiny")[0]
+    x = synth.widen(c.x_batch(0))
+    w = synth.widen(c.w())
+    ax = oracle.absmax_cols(x)
+    aw = oracle.absmax_cols(w)
+    s = oracle.smooth_factors(ax, aw, alpha)
+    mx = oracle.absmax_cols(oracle.fold_act(x, s)).astype(np.float64)
+    mw = oracle.absmax_cols(oracle.fold_weight(w, s)).astype(np.float64)
+    p = ax.astype(np.float64) * aw.astype(np.float64)
+    assert np.max(np.abs(mx / p ** (1 - alpha) - 1)) < 4 * U
+    assert np.max(np.abs(mw / p ** alpha - 1)) < 4 * U
+
+
+def test_smoothing_zero_channel_gets_one():
+    ax = np.array([0.0, 2.0, 3.0], dtype=np.float32)
+    aw = np.array([1.0, 0.0, 0.5], dtype=np.float32)
+    s = oracle.smooth_factors(ax, aw, 0.5)
+    assert s[0] == 1.0 and s[1] == 1.0 and s[2] == np.float32(math.sqrt(6.0))
+
+
+def test_absmax_running_over_batches():
+    """Calibration over batches is the column max of their concatenation; axis is the column."""
+    rng = np.random.default_rng(6)
+    bs = [rng.standard_normal((7, 33)).astype(np.float32) for _ in range(4)]
+    bs[2][3, 9] = -55.0
+    a = None
+    for b in bs:
+        a = oracle.absmax_cols(b, a)
+    np.testing.assert_array_equal(a, np.max(np.abs(np.concatenate(bs)), axis=0))
+    assert a[9] == 55.0
+
+
+# ---------------------------------------------------------------- granularity (pin 3)
+
+def test_per_channel_not_worse_than_per_tensor_two_channel_example():
+    """The tutorial's example: channels spanning [-1,1] and [-0.1,0.1]."""
+    rows = read_golden("two_channel_example.txt")
+    K = 64
+    rng = np.random.default_rng(7)
+    w = []
+    for _, lo, hi in rows:
+        lo, hi = float(lo), float(hi)
+        v = rng.uniform(lo, hi, K)
+        v[0], v[1] = lo, hi  # both ends present
+        w.append(v)
+    w = np.array(w, dtype=np.float32)
+    pc = oracle.ssz(w, None, 8, max_iter=0)  # per-channel MinMax
+    St, qt = oracle.minmax_per_tensor(w, 8)
+    mse_t = [oracle.mse_row(w[i], qt[i], St) for i in range(2)]
+    mse_c = pc["mse"]
+    assert St == np.float32(np.float32(1.0) / np.float32(127.0))
+    assert pc["S"][0] == St  # the wide channel sets the per-tensor scale
+    assert mse_c[0] == pytest.approx(mse_t[0], rel=0, abs=0)
+    assert mse_c[1] <= mse_t[1]
+    # step 10x smaller -> error power ~100x smaller on the narrow channel
+    assert 30 < mse_t[1] / mse_c[1] < 300
+
+
+# ---------------------------------------------------------------- SSZ (pins 5, 6, 7)
+
+def _ssz_rows(seed, N=64, K=256, heavy=True):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((N, K)) * 0.02 * np.exp(rng.uniform(np.log(0.05), 0, (N, 1)))
+    if heavy:
+        m = rng.random((N, K)) < 0.004
+        w[m] *= 20
+    return w.astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_ssz_monotone_and_not_worse_than_minmax(bits, smooth):
+    w = _ssz_rows(10 + bits)
+    s = np.exp(np.random.default_rng(9).uniform(-1, 1, w.shape[1])).astype(np.float32) if smooth else None
+    r = oracle.ssz(w, s, bits, hist=True)
+    mm = oracle.ssz(w, s, bits, max_iter=0)
+    h = r["hist"]
+    for n in range(w.shape[0]):
+        it = r["iters"][n]
+        seq = h[n, : it + 1]
+        assert np.all(np.diff(seq) <= 0), seq
+        assert r["mse"][n] == seq[-1]
+        assert r["mse"][n] <= mm["mse"][n]
+        assert h[n, 0] == mm["mse"][n]
+    # the reported error is the error of the reported scale and codes
+    wh = oracle.fold_weight(w, s)
+    for n in range(0, w.shape[0], 7):
+        assert oracle.mse_row(wh[n], r["q"][n], r["S"][n]) == r["mse"][n]
+        np.testing.assert_array_equal(oracle.quant_row(wh[n], r["S"][n], 127 if bits == 8 else 7), r["q"][n])
+
+
+def test_ssz_improves_somewhere_int4():
+    """SSZ exists to beat MinMax; on heavy-tailed int4 rows it must do so on many rows."""
+    w = _ssz_rows(21, N=128)
+    r = oracle.ssz(w, None, 4)
+    mm = oracle.ssz(w, None, 4, max_iter=0)
+    assert np.mean(r["mse"] < mm["mse"]) > 0.5
+    assert np.all(r["iters"] >= 1)
+
+
+def test_lsq_step_brute_force():
+    """For fixed codes, sum(w - S q)^2 is minimised at S = sum(w q) / sum(q^2): grid search."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        K = int(rng.integers(1, 9))
+        w = rng.standard_normal(K).astype(np.float32)
+        q = rng.integers(-127, 128, K).astype(np.int8)
+        if not np.any(q):
+            q[0] = 1
+        S_ls = oracle.lsq_scale(w, q)
+        grid = np.linspace(S_ls - 0.05, S_ls + 0.05, 20001)
+        err = ((w.astype(np.float64)[None, :] - grid[:, None] * q.astype(np.float64)[None, :]) ** 2).sum(1)
+        assert abs(grid[np.argmin(err)] - S_ls) <= 1.01 * (grid[1] - grid[0])
+    assert oracle.lsq_scale(np.ones(4, np.float32), np.zeros(4, np.int8)) == 0.0
+
+
+def test_mse_closed_form():
+    """w_hat = S q exactly -> 0; one element off by e -> e^2 / K."""
+    q = np.array([3, -7, 0, 127, -127, 1, 2, 5], dtype=np.int8)
+    S = 2.0 ** -9
+    w = (q.astype(np.float64) * S).astype(np.float32)
+    assert oracle.mse_row(w, q, S) == 0.0
+    w2 = w.copy()
+    w2[3] += np.float32(2.0 ** -12)
+    assert oracle.mse_row(w2, q, S) == (2.0 ** -12) ** 2 / 8
+
+
+@pytest.mark.parametrize("bits,qmax", [(8, 127), (4, 7)])
+def test_ssz_exact_grid_row(bits, qmax):
+    """Row = c * integers with max |k| = qmax, c = 2^-k: lossless, S = c, one step, error 0."""
+    rng = np.random.default_rng(12)
+    for e in (6, 10, 13):
+        c = 2.0 ** -e
+        k = rng.integers(-qmax, qmax + 1, (3, 96))
+        k[:, 17] = qmax
+        k[1, 40] = -qmax
+        w = (k * c).astype(np.float32)
+        r = oracle.ssz(w, None, bits)
+        assert np.all(r["S"] == np.float32(c))
+        np.testing.assert_array_equal(r["q"], k.astype(np.int8))
+        assert np.all(r["mse"] == 0.0)
+        assert np.all(r["iters"] == 1)
+
+
+def test_ssz_single_nonzero_element():
+    K = 64
+    for val in (0.37, -1.9, 3e-3):
+        w = np.zeros((1, K), dtype=np.float32)
+        w[0, 11] = val
+        r = oracle.ssz(w, None, 8)
+        S = np.float32(abs(np.float32(val))) / np.float32(127)
+        assert r["S"][0] == S
+        assert r["q"][0, 11] == (127 if val > 0 else -127)
+        assert np.count_nonzero(r["q"]) == 1
+        assert r["iters"][0] == 1
+        assert r["mse"][0] <= (abs(val) * 2 * U) ** 2 / K
+
+
+def test_ssz_zero_row_and_floor():
+    K = 32
+    fmin = np.float32(1e-5)
+    w = np.zeros((3, K), dtype=np.float32)
+    w[1] = np.linspace(-5e-4, 9e-4, K, dtype=np.float32)  # absmax/127 < 1e-5: floor binds the init
+    w[2] = 6e-6  # codes round 0.6 up to 1; the refit 6e-6 < 1e-5 must be floored back to 1e-5
+    r = oracle.ssz(w, None, 8)
+    assert r["S"][0] == fmin and not np.any(r["q"][0]) and r["iters"][0] == 1 and r["mse"][0] == 0.0
+    assert r["S"][1] >= fmin
+    assert r["S"][2] == fmin and np.all(r["q"][2] == 1) and r["iters"][2] == 1
+    mm = oracle.ssz(w, None, 8, max_iter=0)
+    assert np.all(mm["iters"] == 0) and mm["S"][1] == fmin and mm["S"][2] == fmin
+    assert np.max(np.abs(mm["q"][1])) == 90  # 9e-4 / 1e-5
+
+
+def test_ssz_converged_is_a_fixed_point():
+    """At exit (iters < 20) the next least-squares candidate improves by less than the thresholds."""
+    w = _ssz_rows(13, N=48)
+    thr = 1e-10
+    r = oracle.ssz(w, None, 8)
+    fmin = np.float32(1e-5)
+    for n in range(w.shape[0]):
+        if r["iters"][n] >= 20:
+            continue
+        S = r["S"][n]
+        q = r["q"][n]
+        Sn = max(np.float32(oracle.lsq_scale(w[n], q)), fmin)
+        cur = oracle.mse_row(w[n], oracle.quant_row(w[n], Sn, 127), Sn)
+        best = r["mse"][n]
+        d = best - cur
+        assert best == 0 or d / best < thr or abs(d) < thr
+
+
+def test_ssz_constants_golden():
+    rows = {k: float(v) for k, v in read_golden("ssz_constants.txt")}
+    import inspect
+    sig = inspect.signature(oracle.ssz).parameters
+    assert sig["max_iter"].default == rows["SCALE_SEARCH_ITER_NUM"]
+    assert sig["thr"].default == rows["SCALE_SEARCH_CONVERGE_THRESHOLD"]
+    assert sig["min_scale"].default == rows["SCALE_SEARCH_MIN_SCALE"]
+
+
+def test_pack_int4_layout():
+    q = np.array([[1, -1, 7, -7, 0, -8 + 1, 3, 4]], dtype=np.int8)
+    p = oracle.pack_int4(q)
+    assert p.tolist() == [[0xF1, 0x97, 0x90, 0x43]]  # -7 -> 0x9, 1 -> 0x1, -1 -> 0xF
+
+
+# ---------------------------------------------------------------- per token (pin 8)
+
+def test_per_token_invariants():
+    c = synth.cases("tiny")[0]
+    x = synth.widen(c.x_batch(0)).copy()
+    x[5] = 0.0
+    xq, d = oracle.quant_per_token(x, None)
+    assert np.all(np.abs(xq.astype(int)) <= 127)
+    for t in range(x.shape[0]):
+        if t == 5:
+            assert d[t] == 1.0 and not np.any(xq[t])
+            continue
+        a = np.max(np.abs(x[t]))
+        assert np.max(np.abs(xq[t].astype(int))) == 127
+        assert d[t] == np.float32(a) / np.float32(127)
+        # round to nearest: reconstruction error at most half a step (plus fp32 slack)
+        err = np.abs(x[t].astype(np.float64) - d[t] * xq[t].astype(np.float64))
+        assert np.all(err <= 0.5 * d[t] * (1 + 4e-6) + 4 * U * np.abs(x[t]))
+
+
+def test_per_token_scale_is_per_row():
+    """Scaling one token row leaves every other row's codes and scales untouched."""
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    xq, d = oracle.quant_per_token(x, None)
+    x2 = x.copy()
+    x2[2] *= 1000
+    xq2, d2 = oracle.quant_per_token(x2, None)
+    keep = [0, 1, 3, 4, 5]
+    np.testing.assert_array_equal(xq[keep], xq2[keep])
+    np.testing.assert_array_equal(d[keep], d2[keep])
+    np.testing.assert_array_equal(xq[2], xq2[2])  # power-of-ten scaling leaves codes (nearly) alone
+    assert d2[2] > 900 * d[2]
+
+
+# ---------------------------------------------------------------- GEMM (pin 9)
+
+def test_gemm_brute_force():
+    rng = np.random.default_rng(15)
+    for M, N, K in ((1, 1, 1), (3, 5, 7), (4, 9, 33), (2, 3, 64)):
+        a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+        b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        got = oracle.gemm_i8(a, b)
+        for t in range(M):
+            for n in range(N):
+                assert got[t, n] == sum(int(a[t, k]) * int(b[n, k]) for k in range(K))
+        np.testing.assert_array_equal(got, a.astype(np.int64) @ b.astype(np.int64).T)
+
+
+def test_gemm_int32_bound():
+    """K = floor((2^31 - 1) / 127^2) = 133144 is the largest K with no possible int32 overflow."""
+    K = (2 ** 31 - 1) // (127 * 127)
+    assert K == 133144
+    a = np.full((1, K), 127, dtype=np.int8)
+    assert oracle.gemm_i8(a, a)[0, 0] == 127 * 127 * K
+    a2 = np.full((1, K + 1), 127, dtype=np.int8)
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm_i8(a2, a2)
+
+
+# ---------------------------------------------------------------- whole path
+
+def test_lossless_path_reproduces_exact_product():
+    """X rows = d_t * integers and W rows = c_n * integers, both with max |k| = 127 and
+    power-of-two steps: quantization is lossless, so the dequantized output equals X W^T exactly.
+    A wrong scale axis, a transposed operand or a dropped scale breaks equality."""
+    rng = np.random.default_rng(16)
+    T, K, N = 9, 64, 13
+    kx = rng.integers(-127, 128, (T, K))
+    kx[:, 3] = 127
+    kw = rng.integers(-127, 128, (N, K))
+    kw[:, 10] = -127
+    dt = 2.0 ** rng.integers(-8, 3, T)
+    cn = 2.0 ** rng.integers(-14, -4, N)
+    x = (kx * dt[:, None]).astype(np.float32)
+    w = (kw * cn[:, None]).astype(np.float32)
+    out = oracle.run_linear([x], w, x, smooth=False)
+    np.testing.assert_array_equal(out["S"], cn.astype(np.float32))
+    np.testing.assert_array_equal(out["delta"], dt.astype(np.float32))
+    np.testing.assert_array_equal(out["y"], x.astype(np.float64) @ w.astype(np.float64).T)
+
+
+def test_smoothing_helps_on_outlier_activations():
+    """The SmoothQuant article's claim on the tiny outlier workload: smoothing lowers the W8A8 error."""
+    c = synth.cases("tiny")[0]
+    x = synth.widen(c.x_batch(0))
+    w = synth.widen(c.w())
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    e = {}
+    for sm in (False, True):
+        y = oracle.run_linear([x], w, x, alpha=0.5, smooth=sm)["y"]
+        e[sm] = np.max(np.abs(y - ref)) / np.max(np.abs(ref))
+    assert e[True] < e[False]
+    assert e[True] < 2e-2
