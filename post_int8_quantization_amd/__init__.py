@@ -1,0 +1,177 @@
+"""Python binding of libptq, the gfx950 W8A8 post-training-quantized linear layer.
+
+Argument marshalling only: every step runs in the HIP kernels of libptq.so,
+called through its C ABI (include/ptq.h) with ctypes.  PyTorch supplies
+device memory and the current stream.  There is no CPU fallback: importing
+this module fails if libptq.so is missing, and each call raises PtqError on a
+non-OK status.
+
+Entry points (same names as the C ABI):
+  sq_absmax_calib(x, amax=None, accumulate=False) -> amax[K] fp32
+  sq_smooth_factors(act_amax, w_amax, alpha) -> s[K] fp32
+  ssz_weight_qparams(w, s=None, bits=8, ...) -> (scale[N], wq, iters[N], mse[N])
+  quant_per_token_i8(x, s=None) -> (xq[T,K] int8, tok_scale[T] fp32)
+  w8a8_gemm_dequant(xq, wq, tok_scale, ch_scale, want_acc=False) -> y[M,N] fp32 (, acc int32)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libptq.so")
+
+PTQ_F32, PTQ_BF16 = 0, 1
+SSZ_MAX_ITER = 20
+SSZ_THRESHOLD = 1e-10
+SSZ_MIN_SCALE = 1e-5
+GEMM_MAX_K = 133144
+
+STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE", 4: "PTQ_ERR_UNSUPPORTED",
+          5: "PTQ_ERR_ARG", 6: "PTQ_ERR_ALIGN", 7: "PTQ_ERR_HIP"}
+
+EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
+           "ssz_weight_qparams", "quant_per_token_i8", "w8a8_gemm_dequant")
+
+
+class PtqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libptq.so not built at {LIB_PATH}; run `python post_int8_quantization_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, f32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    lib.ptq_abi_version.restype = ci
+    lib.ptq_abi_version.argtypes = []
+    lib.ptq_last_error.restype = ctypes.c_char_p
+    lib.ptq_last_error.argtypes = []
+    lib.ptq_status_string.restype = ctypes.c_char_p
+    lib.ptq_status_string.argtypes = [ci]
+    lib.sq_absmax_calib.argtypes = [vp, ci, i64, i64, vp, ci, vp]
+    lib.sq_smooth_factors.argtypes = [vp, vp, i64, f32, vp, vp]
+    lib.ssz_weight_qparams.argtypes = [vp, ci, i64, i64, vp, ci, ci, ci, f64, f32, vp, vp, vp, vp, vp]
+    lib.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
+    lib.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "quant_per_token_i8",
+               "w8a8_gemm_dequant"):
+        getattr(lib, fn).restype = ci
+    return lib
+
+
+lib = _load()
+
+
+def _check(st: int):
+    if st != 0:
+        raise PtqError(st, lib.ptq_last_error().decode(errors="replace"))
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def _dtype_code(t):
+    return PTQ_BF16 if t.dtype == torch.bfloat16 else PTQ_F32
+
+
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def sq_absmax_calib(x, amax=None, accumulate=False, stream=None):
+    _dev(x, "x", _FLOATS)
+    rows, cols = x.shape
+    if amax is None:
+        amax = torch.empty(cols, dtype=torch.float32, device=x.device)
+        accumulate = False
+    _dev(amax, "amax", (torch.float32,))
+    _check(lib.sq_absmax_calib(_ptr(x), _dtype_code(x), rows, cols, _ptr(amax), int(bool(accumulate)),
+                               _stream(stream)))
+    return amax
+
+
+def sq_smooth_factors(act_amax, w_amax, alpha, s=None, stream=None):
+    _dev(act_amax, "act_amax", (torch.float32,))
+    _dev(w_amax, "w_amax", (torch.float32,))
+    K = act_amax.numel()
+    if w_amax.numel() != K:
+        raise ValueError("act_amax and w_amax differ in length")
+    if s is None:
+        s = torch.empty(K, dtype=torch.float32, device=act_amax.device)
+    _check(lib.sq_smooth_factors(_ptr(act_amax), _ptr(w_amax), K, float(alpha), _ptr(s), _stream(stream)))
+    return s
+
+
+def ssz_weight_qparams(w, s=None, bits=8, symmetric=True, max_iter=SSZ_MAX_ITER, threshold=SSZ_THRESHOLD,
+                       min_scale=SSZ_MIN_SCALE, want_codes=True, want_stats=True, stream=None):
+    """Returns (scale[N] fp32, wq (int8 [N,K] or uint8 [N,K/2] for int4) or None, iters or None, mse or None)."""
+    _dev(w, "w", _FLOATS)
+    N, K = w.shape
+    dev = w.device
+    if s is not None:
+        _dev(s, "s", (torch.float32,))
+    scale = torch.empty(N, dtype=torch.float32, device=dev)
+    wq = None
+    if want_codes:
+        wq = torch.empty((N, K), dtype=torch.int8, device=dev) if bits == 8 else \
+            torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    iters = torch.empty(N, dtype=torch.int32, device=dev) if want_stats else None
+    mse = torch.empty(N, dtype=torch.float64, device=dev) if want_stats else None
+    _check(lib.ssz_weight_qparams(_ptr(w), _dtype_code(w), N, K, _ptr(s), int(bits), int(bool(symmetric)),
+                                  int(max_iter), float(threshold), float(min_scale), _ptr(scale), _ptr(wq),
+                                  _ptr(iters), _ptr(mse), _stream(stream)))
+    return scale, wq, iters, mse
+
+
+def quant_per_token_i8(x, s=None, xq=None, tok_scale=None, stream=None):
+    _dev(x, "x", _FLOATS)
+    T, K = x.shape
+    if s is not None:
+        _dev(s, "s", (torch.float32,))
+    if xq is None:
+        xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if tok_scale is None:
+        tok_scale = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check(lib.quant_per_token_i8(_ptr(x), _dtype_code(x), T, K, _ptr(s), _ptr(xq), _ptr(tok_scale),
+                                  _stream(stream)))
+    return xq, tok_scale
+
+
+def w8a8_gemm_dequant(xq, wq, tok_scale, ch_scale, want_acc=False, y=None, stream=None):
+    _dev(xq, "xq", (torch.int8,))
+    _dev(wq, "wq", (torch.int8,))
+    _dev(tok_scale, "tok_scale", (torch.float32,))
+    _dev(ch_scale, "ch_scale", (torch.float32,))
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K:
+        raise ValueError("xq and wq differ in K")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
+    _check(lib.w8a8_gemm_dequant(_ptr(xq), _ptr(wq), _ptr(tok_scale), _ptr(ch_scale), M, N, K, _ptr(y), _ptr(acc),
+                                 _stream(stream)))
+    return (y, acc) if want_acc else y

@@ -1,0 +1,30 @@
+// ptq_launch.hpp -- internal launchers behind the C ABI (C++ linkage, not exported).
+// Each launcher assumes its arguments were validated by capi.hip and enqueues
+// its kernels on `stream`; it returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptq {
+
+hipError_t launch_absmax_cols(const void* x, int dtype, int64_t rows, int64_t cols, float* amax, int accumulate,
+                              hipStream_t stream);
+
+hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, float* s,
+                                 hipStream_t stream);
+
+hipError_t launch_quant_per_token(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,
+                                  float* tok_scale, hipStream_t stream);
+
+hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits, int max_iter,
+                      double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,
+                      hipStream_t stream);
+
+hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
+                               int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, hipStream_t stream);
+
+// Largest K the row-resident kernels (per-token quantization, SSZ) accept.
+constexpr int64_t kMaxRowK = 131072;
+
+}  // namespace ptq

@@ -1,0 +1,240 @@
+// ssz.hip -- MinMax + SSZ per-output-channel symmetric weight quantization (gfx950).
+//
+// [SSZ] flow: MinMax initial scale, then least-squares refits of the scale for
+// the current codes, a refit kept only when it lowers the quantization error,
+// until the relative or absolute change falls under the threshold or the
+// iteration limit is reached; symmetric quantization fixes the offset at 0.
+// [SQ] the weight side of the smoothing fold, w_hat = fl32(w * s_j).
+//
+// One block of TPR threads owns one row (output channel).  The row is read
+// from HBM once and stays in registers (CPT chunks of 16 elements per
+// thread) for every pass; all passes are ALU work.  One pass over the row
+// for a scale S computes, per element, the code q = clamp(rne(w_hat * inv S))
+// and accumulates sum(w_hat q) and sum((w_hat - S q)^2) in fp64 and sum(q^2)
+// exactly (fp32 per lane, integer across lanes).  The sums are reduced with
+// xor butterflies (identical in every lane) and, for multi-wave rows, through
+// LDS in wave order, so every decision is uniform across the row.
+#include "ptq_dev.hpp"
+#include "ptq_launch.hpp"
+
+namespace ptq {
+
+namespace {
+
+struct PassSums {
+  double a;  // sum w_hat q
+  double e;  // sum (w_hat - S q)^2
+  int b;     // sum q^2
+};
+
+template <int TPR, int CPT>
+__device__ __forceinline__ PassSums row_pass(const float (&wh)[CPT][16], float S, float qmax, double (*red_d)[2],
+                                             int* red_i, int tid) {
+  const float inv = 1.0f / S;
+  const double Sd = (double)S;
+  double a = 0.0, e = 0.0;
+  float bq = 0.0f;  // at most 16*CPT terms of <= 127^2 each: exact in fp32
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float q = code_f(wh[m][k], inv, qmax);
+      const double qd = (double)q, wd = (double)wh[m][k];
+      a = __builtin_fma(wd, qd, a);
+      const double d = __builtin_fma(-Sd, qd, wd);  // S*q is exact in fp64
+      e = __builtin_fma(d, d, e);
+      bq = __builtin_fmaf(q, q, bq);
+    }
+  }
+  PassSums r;
+  r.a = wave_sum(a);
+  r.e = wave_sum(e);
+  r.b = wave_sum((int)bq);
+  constexpr int NW = TPR / kWave;
+  if constexpr (NW > 1) {
+    const int w = tid / kWave;
+    __syncthreads();  // previous readers of the LDS slots are done
+    if ((tid & (kWave - 1)) == 0) {
+      red_d[w][0] = r.a;
+      red_d[w][1] = r.e;
+      red_i[w] = r.b;
+    }
+    __syncthreads();
+    r.a = red_d[0][0];
+    r.e = red_d[0][1];
+    r.b = red_i[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      r.a += red_d[i][0];
+      r.e += red_d[i][1];
+      r.b += red_i[i];
+    }
+  }
+  return r;
+}
+
+template <int DT, bool HAS_S, int BITS, int TPR, int CPT>
+__global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t N, int64_t K,
+                                             const float* __restrict__ s, int max_iter, double thr, float min_scale,
+                                             float* __restrict__ scale, void* __restrict__ wq,
+                                             int32_t* __restrict__ iters, double* __restrict__ mse) {
+  constexpr int NW = TPR / kWave;
+  constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
+  __shared__ double red_d[NW][2];
+  __shared__ int red_i[NW];
+  __shared__ float red_f[NW];
+  const int tid = threadIdx.x;
+  const int64_t nchunk = K / 16;
+  const double Kd = (double)K;
+
+  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    // load + fold; out-of-row chunks are zeros (they add nothing to any sum)
+    float wh[CPT][16];
+    float m = 0.0f;
+#pragma unroll
+    for (int c8 = 0; c8 < CPT; ++c8) {
+      const int64_t c = tid + (int64_t)TPR * c8;
+      if (c < nchunk) {
+        float a8[8], b8[8];
+        load8<DT>(w, n * K + c * 16, a8);
+        load8<DT>(w, n * K + c * 16 + 8, b8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          wh[c8][e] = a8[e];
+          wh[c8][e + 8] = b8[e];
+        }
+        if constexpr (HAS_S) {
+          const float4* sp = reinterpret_cast<const float4*>(s + c * 16);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 sv = sp[q4];
+            wh[c8][4 * q4 + 0] = wh[c8][4 * q4 + 0] * sv.x;
+            wh[c8][4 * q4 + 1] = wh[c8][4 * q4 + 1] * sv.y;
+            wh[c8][4 * q4 + 2] = wh[c8][4 * q4 + 2] * sv.z;
+            wh[c8][4 * q4 + 3] = wh[c8][4 * q4 + 3] * sv.w;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(wh[c8][e]));
+    }
+    m = wave_max(m);
+    if constexpr (NW > 1) {
+      __syncthreads();
+      if ((tid & (kWave - 1)) == 0) red_f[tid / kWave] = m;
+      __syncthreads();
+      m = red_f[0];
+#pragma unroll
+      for (int i = 1; i < NW; ++i) m = fmaxf(m, red_f[i]);
+    }
+
+    // MinMax init
+    float S = m / QMAX;
+    S = S < min_scale ? min_scale : S;
+    PassSums cur = row_pass<TPR, CPT>(wh, S, QMAX, red_d, red_i, tid);
+    double best = cur.e / Kd;
+    double A = cur.a;
+    int B = cur.b;
+
+    // least-squares refits, greedy, per-row convergence
+    int it = 0;
+    for (int i = 1; i <= max_iter; ++i) {
+      it = i;
+      if (B == 0) break;
+      float Sc = (float)(A / (double)B);
+      Sc = Sc < min_scale ? min_scale : Sc;
+      const PassSums p = row_pass<TPR, CPT>(wh, Sc, QMAX, red_d, red_i, tid);
+      const double c = p.e / Kd;
+      const double d = best - c;
+      const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+      if (c < best) {
+        S = Sc;
+        best = c;
+        A = p.a;
+        B = p.b;
+      }
+      if (conv) break;
+    }
+
+    // codes of the kept scale
+    if (wq) {
+      const float inv = 1.0f / S;
+#pragma unroll
+      for (int c8 = 0; c8 < CPT; ++c8) {
+        const int64_t c = tid + (int64_t)TPR * c8;
+        if (c < nchunk) {
+          float q[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) q[e] = code_f(wh[c8][e], inv, QMAX);
+          if constexpr (BITS == 8) {
+            uint4 o;
+            o.x = pack4_i8(q[0], q[1], q[2], q[3]);
+            o.y = pack4_i8(q[4], q[5], q[6], q[7]);
+            o.z = pack4_i8(q[8], q[9], q[10], q[11]);
+            o.w = pack4_i8(q[12], q[13], q[14], q[15]);
+            *reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(wq) + n * K + c * 16) = o;
+          } else {
+            uint2 o;
+            o.x = pack8_i4(q);
+            o.y = pack8_i4(q + 8);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(wq) + n * (K / 2) + c * 8) = o;
+          }
+        }
+      }
+    }
+    if (tid == 0) {
+      scale[n] = S;
+      if (iters) iters[n] = it;
+      if (mse) mse[n] = best;
+    }
+  }
+}
+
+template <int DT, bool HAS_S, int BITS>
+hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max_iter, double thr, float min_scale,
+                    float* scale, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
+  const int64_t nchunk = K / 16;
+  // about 64 elements per thread; one wave per row up to K = 4096
+  int tpr = 64;
+  while (tpr < 1024 && (nchunk + tpr - 1) / tpr > 4) tpr *= 2;
+  const int64_t cpt = (nchunk + tpr - 1) / tpr;
+  const int64_t blocks = N;
+#define PTQ_S(TPR_, CPT_)                                                                                 \
+  if (tpr == TPR_ && cpt <= CPT_) {                                                                       \
+    k_ssz<DT, HAS_S, BITS, TPR_, CPT_><<<(unsigned)blocks, TPR_, 0, stream>>>(                            \
+        w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse);                                     \
+    return hipGetLastError();                                                                             \
+  }
+  PTQ_S(64, 1) PTQ_S(64, 2) PTQ_S(64, 4)
+  PTQ_S(128, 4) PTQ_S(256, 4) PTQ_S(512, 4) PTQ_S(1024, 4) PTQ_S(1024, 8)
+#undef PTQ_S
+  return hipErrorInvalidValue;
+}
+
+template <int DT, bool HAS_S>
+hipError_t dispatch_bits(const void* w, int64_t N, int64_t K, const float* s, int bits, int max_iter, double thr,
+                         float min_scale, float* scale, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
+  if (bits == 8) return dispatch<DT, HAS_S, 8>(w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse, stream);
+  return dispatch<DT, HAS_S, 4>(w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse, stream);
+}
+
+}  // namespace
+
+hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits, int max_iter,
+                      double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,
+                      hipStream_t stream) {
+  if (dtype == PTQ_BF16)
+    return s ? dispatch_bits<PTQ_BF16, true>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters,
+                                             mse, stream)
+             : dispatch_bits<PTQ_BF16, false>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters,
+                                              mse, stream);
+  return s ? dispatch_bits<PTQ_F32, true>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters, mse,
+                                          stream)
+           : dispatch_bits<PTQ_F32, false>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters, mse,
+                                           stream);
+}
+
+}  // namespace ptq

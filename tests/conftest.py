@@ -28,3 +28,28 @@ def read_golden(name):
 @pytest.fixture(scope="session")
 def golden():
     return read_golden
+
+
+_CONFIG = None
+
+
+def pytest_sessionstart(session):
+    global _CONFIG
+    _CONFIG = session.config
+
+
+def say(msg):
+    """Write a line to the real terminal right away (not captured), so the case a
+    GPU step belongs to is on record even if the process dies during the step."""
+    tr = _CONFIG.pluginmanager.getplugin("terminalreporter") if _CONFIG else None
+    if tr is not None:
+        tr.write_line(msg)
+        tr._tw.flush() if hasattr(tr, "_tw") else None
+    else:
+        sys.__stderr__.write(msg + "\n")
+        sys.__stderr__.flush()
+
+
+def pytest_runtest_logstart(nodeid, location):
+    if "gpu" in nodeid.split("::")[0]:
+        say(f"[gpu-test] start {nodeid}")

@@ -1,0 +1,175 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects every invalid argument on the host before any launch.
+
+Every call here fails validation, so no kernel is ever enqueued: pointers are
+either NULL or deliberately misaligned host-side integers that are never
+dereferenced because validation stops first.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, read_golden
+
+HEADER = os.path.join(ROOT, "include", "ptq.h")
+LIB = os.path.join(ROOT, "post_int8_quantization_amd", "libptq.so")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ARG, ALIGN, HIP = range(8)
+F32, BF16 = 0, 1
+P = 0x10000  # a 16-byte-aligned stand-in pointer, only ever paired with an argument that fails validation
+MIS = 0x10001  # misaligned stand-in pointer
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("ptq_build", os.path.join(ROOT, "post_int8_quantization_amd",
+                                                                                 "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    L = ctypes.CDLL(LIB)
+    vp, i64, ci, f32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    L.sq_absmax_calib.argtypes = [vp, ci, i64, i64, vp, ci, vp]
+    L.sq_smooth_factors.argtypes = [vp, vp, i64, f32, vp, vp]
+    L.ssz_weight_qparams.argtypes = [vp, ci, i64, i64, vp, ci, ci, ci, f64, f32, vp, vp, vp, vp, vp]
+    L.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
+    L.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    L.ptq_last_error.restype = ctypes.c_char_p
+    L.ptq_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return re.findall(r"PTQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def header_define(name):
+    m = re.search(r"#define\s+%s\s+(\S+)" % name, open(HEADER).read())
+    return m.group(1)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
+                          "sq_smooth_factors", "ssz_weight_qparams", "quant_per_token_i8", "w8a8_gemm_dequant"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ptq_abi_version() == int(header_define("PTQ_ABI_VERSION"))
+
+
+def test_header_constants_match_pages():
+    g = {k: float(v) for k, v in read_golden("ssz_constants.txt")}
+    assert int(header_define("PTQ_SSZ_MAX_ITER")) == g["SCALE_SEARCH_ITER_NUM"]
+    assert float(header_define("PTQ_SSZ_THRESHOLD")) == g["SCALE_SEARCH_CONVERGE_THRESHOLD"]
+    assert float(header_define("PTQ_SSZ_MIN_SCALE").rstrip("f")) == g["SCALE_SEARCH_MIN_SCALE"]
+    assert int(header_define("PTQ_GEMM_MAX_K")) == (2 ** 31 - 1) // 127 ** 2
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["PTQ_OK", "PTQ_ERR_NULL", "PTQ_ERR_SHAPE", "PTQ_ERR_DTYPE", "PTQ_ERR_UNSUPPORTED",
+                                 "PTQ_ERR_ARG", "PTQ_ERR_ALIGN", "PTQ_ERR_HIP"]):
+        assert lib.ptq_status_string(code).decode() == name
+
+
+def _expect(lib, status, want, needle=None):
+    assert status == want, (status, want, lib.ptq_last_error())
+    msg = lib.ptq_last_error().decode()
+    assert msg
+    if needle:
+        assert needle in msg, msg
+
+
+def test_calib_errors(lib):
+    c = lib.sq_absmax_calib
+    _expect(lib, c(None, BF16, 4, 16, P, 0, None), NULL)
+    _expect(lib, c(P, BF16, 4, 16, None, 0, None), NULL)
+    _expect(lib, c(P, 7, 4, 16, P, 0, None), DTYPE)
+    _expect(lib, c(P, BF16, 0, 16, P, 0, None), SHAPE)
+    _expect(lib, c(P, BF16, 4, 0, P, 0, None), SHAPE)
+    _expect(lib, c(P, BF16, 4, 24, P, 0, None), SHAPE, "multiple of 16")
+    _expect(lib, c(MIS, BF16, 4, 16, P, 0, None), ALIGN)
+    _expect(lib, c(P, F32, 4, 16, MIS, 1, None), ALIGN)
+
+
+def test_smooth_errors(lib):
+    c = lib.sq_smooth_factors
+    _expect(lib, c(None, P, 16, 0.5, P, None), NULL)
+    _expect(lib, c(P, P, 16, 0.5, None, None), NULL)
+    _expect(lib, c(P, P, 0, 0.5, P, None), SHAPE)
+    for a in (-0.01, 1.01, math.nan, math.inf):
+        _expect(lib, c(P, P, 16, a, MIS, None), ARG, "alpha")
+
+
+def test_ssz_errors(lib):
+    c = lib.ssz_weight_qparams
+
+    def call(w=P, dt=BF16, N=8, K=64, s=None, bits=8, sym=1, it=20, thr=1e-10, ms=1e-5, scale=P, wq=P):
+        return c(w, dt, N, K, s, bits, sym, it, thr, ms, scale, wq, None, None, None)
+
+    _expect(lib, call(w=None), NULL)
+    _expect(lib, call(scale=None), NULL)
+    _expect(lib, call(dt=2), DTYPE)
+    _expect(lib, call(N=0), SHAPE)
+    _expect(lib, call(K=40), SHAPE)
+    _expect(lib, call(K=131072 + 16), SHAPE)
+    _expect(lib, call(bits=2), UNSUP)
+    _expect(lib, call(bits=16), UNSUP)
+    _expect(lib, call(sym=0), UNSUP, "symmetric")
+    _expect(lib, call(it=-1), ARG)
+    _expect(lib, call(it=21), ARG)
+    _expect(lib, call(thr=-1.0), ARG)
+    _expect(lib, call(thr=math.nan), ARG)
+    _expect(lib, call(ms=0.0), ARG)
+    _expect(lib, call(ms=-1e-5), ARG)
+    _expect(lib, call(w=MIS), ALIGN)
+    _expect(lib, call(s=MIS), ALIGN)
+    _expect(lib, call(wq=MIS), ALIGN)
+
+
+def test_quant_errors(lib):
+    c = lib.quant_per_token_i8
+    _expect(lib, c(None, BF16, 4, 64, None, P, P, None), NULL)
+    _expect(lib, c(P, BF16, 4, 64, None, None, P, None), NULL)
+    _expect(lib, c(P, BF16, 4, 64, None, P, None, None), NULL)
+    _expect(lib, c(P, 5, 4, 64, None, P, P, None), DTYPE)
+    _expect(lib, c(P, BF16, 0, 64, None, P, P, None), SHAPE)
+    _expect(lib, c(P, BF16, 4, 72, None, P, P, None), SHAPE)
+    _expect(lib, c(MIS, BF16, 4, 64, None, P, P, None), ALIGN)
+    _expect(lib, c(P, BF16, 4, 64, None, MIS, P, None), ALIGN)
+    _expect(lib, c(P, F32, 4, 64, MIS, P, P, None), ALIGN)
+
+
+def test_gemm_errors(lib):
+    c = lib.w8a8_gemm_dequant
+    _expect(lib, c(None, P, P, P, 4, 4, 64, P, None, None), NULL)
+    _expect(lib, c(P, P, None, P, 4, 4, 64, P, None, None), NULL)
+    _expect(lib, c(P, P, P, P, 4, 4, 64, None, None, None), NULL)
+    _expect(lib, c(P, P, P, P, 0, 4, 64, P, None, None), SHAPE)
+    _expect(lib, c(P, P, P, P, 4, 0, 64, P, None, None), SHAPE)
+    _expect(lib, c(P, P, P, P, 4, 4, 40, P, None, None), SHAPE)
+    _expect(lib, c(P, P, P, P, 4, 4, 133152, P, None, None), SHAPE, "overflow")
+    _expect(lib, c(MIS, P, P, P, 4, 4, 64, P, None, None), ALIGN)
+    _expect(lib, c(P, P, P, P, 4, 4, 64, MIS, None, None), ALIGN)
+    _expect(lib, c(P, P, P, P, 4, 4, 64, P, MIS, None), ALIGN)
+
+
+def test_binding_rejects_host_tensors():
+    _ensure_built()
+    import torch
+    import post_int8_quantization_amd as pq
+    x = torch.zeros(4, 16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pq.sq_absmax_calib(x)
+    with pytest.raises(ValueError):
+        pq.quant_per_token_i8(x)
+    assert set(pq.EXPORTS) == set(header_functions())

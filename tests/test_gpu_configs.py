@@ -1,0 +1,122 @@
+"""GPU parity on the five workloads, whole path per linear layer:
+calibrate over the seeded batches -> smoothing factors -> MinMax + SSZ weight
+quantization -> per-token activation quantization -> int8 GEMM + dequant.
+
+Small workloads are compared in full.  At full size the GPU runs every row
+(the launch configuration the bench times) and the oracle recomputes sampled
+rows from the same seeded inputs: calibration is checked in full (it is
+cheap), the weight quantization on sampled output channels, the activation
+quantization on sampled tokens, and the GEMM on the sampled tokens x channels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import announce, assert_scales, assert_y, compare_ssz, dev, host, sample_rows, unpack_int4
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_int8_quantization_amd as m
+    return m
+
+
+def run_case(pq, case, alpha, bits=8, w_sample=None, x_sample=None):
+    """GPU whole path for one linear case; oracle on (sampled) rows; compare every stage."""
+    tag = f"{case.name} alpha={alpha} bits={bits}"
+    w_host = case.w()
+    w_f = synth.widen(w_host)
+    wdev = dev(w_host)
+
+    # calibration: running max over the calibration batches (GPU and oracle both see every batch)
+    ax_ref = None
+    ax = None
+    for b in range(case.calib_batches):
+        xb = case.x_batch(b)
+        ax_ref = oracle.absmax_cols(synth.widen(xb), ax_ref)
+        announce(f"{tag}: sq_absmax_calib batch {b}")
+        ax = pq.sq_absmax_calib(dev(xb), ax, accumulate=b > 0)
+        del xb
+    aw_ref = oracle.absmax_cols(w_f)
+    announce(f"{tag}: sq_absmax_calib weight")
+    aw = pq.sq_absmax_calib(wdev)
+    np.testing.assert_array_equal(host(ax), ax_ref, err_msg=tag + " a_x")
+    np.testing.assert_array_equal(host(aw), aw_ref, err_msg=tag + " a_w")
+
+    s_ref = oracle.smooth_factors(ax_ref, aw_ref, alpha)
+    announce(f"{tag}: sq_smooth_factors")
+    s = pq.sq_smooth_factors(ax, aw, alpha)
+    s_h = host(s)
+    assert_scales(s_h, s_ref, tag + " s")
+    assert np.array_equal(s_h, s_ref), f"{tag}: {np.sum(s_h != s_ref)} smoothing factors differ in the last bit"
+
+    # weight quantization (all rows on the GPU; oracle on the sample)
+    rows = np.arange(case.N) if w_sample is None else sample_rows(case.N, w_sample, 11)
+    ref_w = oracle.ssz(w_f[rows], s_ref, bits)
+    announce(f"{tag}: ssz_weight_qparams N={case.N} K={case.K}")
+    S, wq, it, mse = pq.ssz_weight_qparams(wdev, s, bits=bits)
+    codes = host(wq) if bits == 8 else unpack_int4(host(wq))
+    compare_ssz(host(S)[rows], codes[rows], host(it)[rows], host(mse)[rows], ref_w, tag + " ssz")
+    if bits != 8:
+        return
+
+    # activation quantization of the forward batch
+    x_eval = case.x_batch(case.eval_index())
+    toks = np.arange(case.T) if x_sample is None else sample_rows(case.T, x_sample, 13)
+    xq_ref, d_ref = oracle.quant_per_token(synth.widen(x_eval)[toks], s_ref)
+    announce(f"{tag}: quant_per_token_i8 T={case.T}")
+    xq, d = pq.quant_per_token_i8(dev(x_eval), s)
+    np.testing.assert_array_equal(host(d)[toks], d_ref, err_msg=tag + " tok_scale")
+    np.testing.assert_array_equal(host(xq)[toks], xq_ref, err_msg=tag + " xq")
+
+    # GEMM + dequant: full launch on the GPU, sampled block of outputs on the oracle
+    acc_ref = oracle.gemm_i8(xq_ref, ref_w["q"])
+    y_ref = oracle.dequant(acc_ref, d_ref, ref_w["S"])
+    announce(f"{tag}: w8a8_gemm_dequant M={case.T} N={case.N} K={case.K}")
+    y, acc = pq.w8a8_gemm_dequant(xq, wq, d, S, want_acc=True)
+    acc_h = host(acc)[np.ix_(toks, rows)]
+    np.testing.assert_array_equal(acc_h, acc_ref, err_msg=tag + " acc")
+    err = assert_y(host(y)[np.ix_(toks, rows)], y_ref, tag + " y")
+    # accuracy of the whole W8A8 layer against the unquantized product (reported; parity unpinned)
+    full = synth.widen(x_eval)[toks].astype(np.float64) @ w_f[rows].astype(np.float64).T
+    rel = np.max(np.abs(host(y)[np.ix_(toks, rows)] - full)) / np.max(np.abs(full))
+    announce(f"{tag}: y parity {err:.2e}; W8A8 vs fp64 product {rel:.3e}")
+
+
+def test_tiny(pq):
+    for case in synth.cases("tiny"):
+        run_case(pq, case, 0.5)
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_gpt345m(pq, idx):
+    run_case(pq, synth.cases("gpt345m")[idx], 0.5, w_sample=None, x_sample=None)
+
+
+def test_decode(pq):
+    run_case(pq, synth.cases("decode")[0], 0.5, w_sample=512)
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.8])
+@pytest.mark.parametrize("idx", [0, 1])
+def test_opt67b(pq, idx, alpha):
+    run_case(pq, synth.cases("opt67b")[idx], alpha, w_sample=256, x_sample=64)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("layer", [0, 31])
+def test_ssz_scale(pq, layer, bits):
+    for case in synth.cases("ssz_scale")[4 * layer: 4 * layer + 4]:
+        w_host = case.w()
+        rows = sample_rows(case.N, 384, 17 + layer)
+        ref = oracle.ssz(synth.widen(w_host)[rows], None, bits)
+        announce(f"{case.name}: ssz_weight_qparams int{bits} N={case.N} K={case.K}")
+        S, wq, it, mse = pq.ssz_weight_qparams(dev(w_host), None, bits=bits)
+        codes = host(wq) if bits == 8 else unpack_int4(host(wq))
+        compare_ssz(host(S)[rows], codes[rows], host(it)[rows], host(mse)[rows], ref, case.name)

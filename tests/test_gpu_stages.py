@@ -1,0 +1,195 @@
+"""GPU parity, stage by stage: each entry point of the C ABI against the oracle on
+seeded inputs, over shapes that span several tiles and a ragged tail, plus the
+degenerate cases of the method.  Integers are compared bit for bit; floats to
+the tolerances in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import (announce, assert_scales, assert_y, compare_ssz, dev, host, unpack_int4)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_int8_quantization_amd as m
+    return m
+
+
+def _x(name, T, K, dtype, factor=40.0, frac=0.01):
+    ch = synth.pick_channels(name, K, max(1, round(frac * K)))
+    return synth.activation(name, T, K, dtype, ch, factor)
+
+
+def _w(name, N, K, dtype, tail=0.0):
+    return synth.weight(name, N, K, dtype, 0.02, 0.05, 1.0, tail, 20.0)
+
+
+# ------------------------------------------------------------------ calibration
+
+@pytest.mark.parametrize("rows,cols,dtype,batches", [
+    (16, 64, synth.F32, 1), (1, 16, synth.BF16, 1), (300, 1040, synth.BF16, 3), (257, 4112, synth.F32, 2),
+    (4096, 4096, synth.BF16, 2), (2048, 16384, synth.BF16, 1), (28672, 8192, synth.BF16, 1)])
+def test_absmax_calib(pq, rows, cols, dtype, batches):
+    ref = None
+    amax = None
+    for b in range(batches):
+        x = _x(f"cal/{rows}x{cols}/b{b}", rows, cols, dtype)
+        ref = oracle.absmax_cols(synth.widen(x), ref)
+        announce(f"sq_absmax_calib rows={rows} cols={cols} dtype={dtype} batch={b}")
+        amax = pq.sq_absmax_calib(dev(x), amax, accumulate=b > 0)
+    np.testing.assert_array_equal(host(amax), ref)
+
+
+def test_absmax_calib_accumulate_keeps_larger(pq):
+    x = _x("cal/acc", 64, 256, synth.F32)
+    big = torch.full((256,), 1e6, device="cuda:0")
+    announce("sq_absmax_calib accumulate into large values")
+    out = pq.sq_absmax_calib(dev(x), big.clone(), accumulate=True)
+    assert torch.all(out == 1e6)
+
+
+# ------------------------------------------------------------------ smoothing factors
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 0.8, 1.0])
+def test_smooth_factors(pq, alpha):
+    K = 4096 + 16
+    rng = np.random.default_rng(3)
+    ax = np.exp(rng.uniform(-3, 5, K)).astype(np.float32)
+    aw = np.exp(rng.uniform(-7, 0, K)).astype(np.float32)
+    ax[5] = 0.0
+    aw[9] = 0.0
+    ref = oracle.smooth_factors(ax, aw, alpha)
+    announce(f"sq_smooth_factors K={K} alpha={alpha}")
+    s = host(pq.sq_smooth_factors(dev(ax), dev(aw), alpha))
+    assert s[5] == 1.0 and s[9] == 1.0
+    assert_scales(s, ref, "s")
+    assert np.sum(s != ref) <= 2  # fp64 pow may differ in the last bit before the single rounding
+
+
+# ------------------------------------------------------------------ per-token quantization
+
+@pytest.mark.parametrize("T,K,dtype,smooth", [
+    (16, 64, synth.F32, True), (1, 16, synth.BF16, False), (257, 1040, synth.BF16, True),
+    (300, 4096, synth.BF16, True), (300, 4096, synth.F32, False), (33, 16384, synth.BF16, True),
+    (5, 8192, synth.BF16, False), (64, 3072, synth.BF16, True), (9, 36864, synth.BF16, True),
+    (3, 65536 + 16, synth.BF16, True)])
+def test_quant_per_token(pq, T, K, dtype, smooth):
+    x = _x(f"q/{T}x{K}", T, K, dtype)
+    if T > 2:
+        x[2] = 0  # all-zero token
+    s = np.exp(np.random.default_rng(K).uniform(-2, 2, K)).astype(np.float32) if smooth else None
+    xq_ref, d_ref = oracle.quant_per_token(synth.widen(x), s)
+    announce(f"quant_per_token_i8 T={T} K={K} dtype={dtype} smooth={smooth}")
+    xq, d = pq.quant_per_token_i8(dev(x), None if s is None else dev(s))
+    np.testing.assert_array_equal(host(d), d_ref)
+    np.testing.assert_array_equal(host(xq), xq_ref)
+    if T > 2:
+        assert host(d)[2] == 1.0
+
+
+# ------------------------------------------------------------------ SSZ weight quantization
+
+def _edge_rows(K, qmax):
+    rows = np.zeros((4, K), dtype=np.float32)
+    k = (np.arange(K) % (2 * qmax + 1)) - qmax
+    rows[1] = k * 2.0 ** -9            # exact grid: lossless
+    rows[2, K // 3] = -0.37             # a single non-zero element
+    rows[3] = 6e-6                      # refit falls under the 1e-5 floor
+    return rows
+
+
+@pytest.mark.parametrize("N,K,dtype,bits,smooth,tail", [
+    (128, 64, synth.F32, 8, True, 0.0), (300, 1040, synth.BF16, 8, True, 0.001),
+    (300, 1040, synth.BF16, 4, False, 0.001), (96, 4096, synth.BF16, 8, False, 0.001),
+    (96, 4096, synth.BF16, 4, True, 0.0), (40, 16384, synth.BF16, 8, True, 0.001),
+    (40, 16384, synth.BF16, 4, False, 0.001), (23, 8192, synth.BF16, 8, True, 0.0),
+    (17, 2064, synth.F32, 4, True, 0.002), (6, 36864, synth.BF16, 8, False, 0.001)])
+def test_ssz(pq, N, K, dtype, bits, smooth, tail):
+    w = _w(f"ssz/{N}x{K}", N, K, dtype, tail)
+    wf = synth.widen(w).copy()
+    if dtype == synth.F32:
+        wf[:4] = _edge_rows(K, 127 if bits == 8 else 7)
+        w = wf
+    s = np.exp(np.random.default_rng(N + K).uniform(-1, 1, K)).astype(np.float32) if smooth else None
+    ref = oracle.ssz(wf, s, bits)
+    announce(f"ssz_weight_qparams N={N} K={K} dtype={dtype} bits={bits} smooth={smooth}")
+    S, wq, it, mse = pq.ssz_weight_qparams(dev(w), None if s is None else dev(s), bits=bits)
+    codes = host(wq) if bits == 8 else unpack_int4(host(wq))
+    compare_ssz(host(S), codes, host(it), host(mse), ref, f"ssz {N}x{K} int{bits}")
+
+
+@pytest.mark.parametrize("max_iter", [0, 1, 3])
+def test_ssz_max_iter(pq, max_iter):
+    w = _w("ssz/iter", 64, 1024, synth.BF16, 0.001)
+    ref = oracle.ssz(synth.widen(w), None, 4, max_iter=max_iter)
+    announce(f"ssz_weight_qparams max_iter={max_iter}")
+    S, wq, it, mse = pq.ssz_weight_qparams(dev(w), None, bits=4, max_iter=max_iter)
+    compare_ssz(host(S), unpack_int4(host(wq)), host(it), host(mse), ref, f"max_iter={max_iter}")
+
+
+def test_ssz_outputs_optional(pq):
+    w = _w("ssz/opt", 32, 512, synth.BF16)
+    ref = oracle.ssz(synth.widen(w), None, 8)
+    announce("ssz_weight_qparams scale only")
+    S, wq, it, mse = pq.ssz_weight_qparams(dev(w), None, bits=8, want_codes=False, want_stats=False)
+    assert wq is None and it is None
+    np.testing.assert_array_equal(host(S), ref["S"])
+
+
+# ------------------------------------------------------------------ GEMM + dequant
+
+@pytest.mark.parametrize("M,N,K", [
+    (16, 128, 64), (1, 1, 16), (7, 33, 48), (16, 1000, 8192), (33, 77, 160), (64, 300, 4096), (65, 130, 1040),
+    (300, 520, 1040), (257, 259, 4096), (512, 768, 2048), (256, 256, 16), (1024, 1024, 4096)])
+def test_gemm_dequant(pq, M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    ts = rng.uniform(0.01, 1.0, M).astype(np.float32)
+    cs = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    acc_ref = oracle.gemm_i8(a, b)
+    y_ref = oracle.dequant(acc_ref, ts, cs)
+    announce(f"w8a8_gemm_dequant M={M} N={N} K={K}")
+    y, acc = pq.w8a8_gemm_dequant(dev(a), dev(b), dev(ts), dev(cs), want_acc=True)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    assert_y(host(y), y_ref, f"y {M}x{N}x{K}")
+
+
+def test_gemm_max_k_extremes(pq):
+    """K = 133136 (largest multiple of 16 under the int32 bound) with all-extreme codes: exact int32."""
+    K = 133136
+    a = np.full((3, K), 127, dtype=np.int8)
+    a[1] = -127
+    b = np.full((20, K), 127, dtype=np.int8)
+    b[7] = -127
+    ref = oracle.gemm_i8(a, b)
+    assert ref.max() == 127 * 127 * K
+    ts = np.ones(3, np.float32)
+    cs = np.ones(20, np.float32)
+    announce("w8a8_gemm_dequant K=133136 extremes (skinny)")
+    y, acc = pq.w8a8_gemm_dequant(dev(a), dev(b), dev(ts), dev(cs), want_acc=True)
+    np.testing.assert_array_equal(host(acc), ref)
+    a2 = np.tile(a, (40, 1))[:100]
+    ref2 = oracle.gemm_i8(a2, b)
+    announce("w8a8_gemm_dequant K=133136 extremes (tiled)")
+    y2, acc2 = pq.w8a8_gemm_dequant(dev(a2), dev(b), dev(np.ones(100, np.float32)), dev(cs), want_acc=True)
+    np.testing.assert_array_equal(host(acc2), ref2)
+
+
+def test_gemm_deterministic(pq):
+    rng = np.random.default_rng(5)
+    a = dev(rng.integers(-127, 128, (700, 1024)).astype(np.int8))
+    b = dev(rng.integers(-127, 128, (900, 1024)).astype(np.int8))
+    ts = dev(rng.uniform(0.1, 1, 700).astype(np.float32))
+    cs = dev(rng.uniform(0.1, 1, 900).astype(np.float32))
+    announce("w8a8_gemm_dequant run twice")
+    y1 = pq.w8a8_gemm_dequant(a, b, ts, cs)
+    y2 = pq.w8a8_gemm_dequant(a, b, ts, cs)
+    assert torch.equal(y1, y2)
