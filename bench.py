@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 post-training-quantized linear path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input,
+on the hidden-4096 prefill workload (OPT-6.7B-sized MLP: fc1 W [16384,4096]
+with X [4096,4096], fc2 W [4096,16384] with X [4096,16384], bf16, 1% outlier
+channels x60).  For each of the two layers:
+
+  1. column absmax over the 8 calibration batches (running max)
+  2. column absmax of the weight (input channels)
+  3. smoothing factors s (alpha)
+  4. MinMax + SSZ int8 per-output-channel weight quantization with the fold
+  5. per-token int8 quantization of the forward batch with the fold
+  6. int8 GEMM with the fused dequantization
+
+Inputs are resident in HBM before the timed region.  Kernels run on torch's
+current stream; HIP events on that stream bracket every stage, giving
+per-kernel durations.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--alpha 0.5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_I8 = 5.0e15           # int8 dense MFMA ops/s
+PEAK_ALU = 256 * 64 * 2.4e9  # VALU lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+SSZ_OPS_PER_ELEM_PASS = 5  # scale-multiply, round, clamp, two multiply-adds (sum w q, sum q^2)
+METRIC = "W8A8 GEMM TOPS + quant/SSZ GB/s at hidden 4096; % of INT8/HBM peak"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--alpha", type=float, default=0.5)
+    p.add_argument("--calib-batches", type=int, default=8)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle GEMM time of the CPU baseline")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the current stream around named stages."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []  # (name, start_event, end_event)
+
+    def stage(self, name, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.marks.append((name, a, b))
+
+    def totals(self):
+        out = {}
+        for name, a, b in self.marks:
+            ms, n = out.get(name, (0.0, 0))
+            out[name] = (ms + a.elapsed_time(b), n + 1)
+        return out
+
+
+def load_counters(kernel_tag):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE), from the committed
+    summary under profiles/, if it was taken on the current kernel source (hash match); else None."""
+    src = os.path.join(ROOT, "post_int8_quantization_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(src, "*.hip")) + glob.glob(os.path.join(src, "*.hpp"))):
+        h.update(open(f, "rb").read())
+    digest = h.hexdigest()[:16]
+    for f in glob.glob(os.path.join(ROOT, "profiles", "*counters*.md")):
+        txt = open(f).read()
+        m = re.search(r"traffic-record:\s*(\{.*\})", txt)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("kernel") == kernel_tag and rec.get("source_sha") == digest:
+            return rec
+    return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the path "
+              "shards by token rows or weight rows with no collective on the hot path, and this build measures "
+              "the one-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import post_int8_quantization_amd as pq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cases = synth.cases("opt67b")
+    B = args.calib_batches
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    layers = []
+    for c in cases:
+        L = dict(case=c, calib=[up(c.x_batch(b)) for b in range(B)], x=up(c.x_batch(B)), w=up(c.w()))
+        L["ax"] = torch.empty(c.K, dtype=torch.float32, device=dev)
+        L["aw"] = torch.empty(c.K, dtype=torch.float32, device=dev)
+        L["s"] = torch.empty(c.K, dtype=torch.float32, device=dev)
+        L["S"] = torch.empty(c.N, dtype=torch.float32, device=dev)
+        L["wq"] = torch.empty((c.N, c.K), dtype=torch.int8, device=dev)
+        L["it"] = torch.empty(c.N, dtype=torch.int32, device=dev)
+        L["mse"] = torch.empty(c.N, dtype=torch.float64, device=dev)
+        L["xq"] = torch.empty((c.T, c.K), dtype=torch.int8, device=dev)
+        L["d"] = torch.empty(c.T, dtype=torch.float32, device=dev)
+        L["y"] = torch.empty((c.T, c.N), dtype=torch.float32, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(tm):
+        for L in layers:
+            def calib():
+                for b, xb in enumerate(L["calib"]):
+                    pq.sq_absmax_calib(xb, L["ax"], accumulate=b > 0, stream=stream)
+            tm.stage("calib_x", calib)
+            tm.stage("calib_w", lambda: pq.sq_absmax_calib(L["w"], L["aw"], stream=stream))
+            tm.stage("smooth", lambda: pq.sq_smooth_factors(L["ax"], L["aw"], args.alpha, s=L["s"], stream=stream))
+            tm.stage("ssz", lambda: pq.ssz_weight_qparams(L["w"], L["s"], bits=8, scale=L["S"], wq=L["wq"],
+                                                          iters=L["it"], mse=L["mse"], stream=stream))
+            tm.stage("quant", lambda: pq.quant_per_token_i8(L["x"], L["s"], xq=L["xq"], tok_scale=L["d"],
+                                                            stream=stream))
+            tm.stage("gemm", lambda: pq.w8a8_gemm_dequant(L["xq"], L["wq"], L["d"], L["S"], y=L["y"],
+                                                          stream=stream))
+
+    for _ in range(args.warmup):
+        step(Timer(torch))
+    torch.cuda.synchronize()
+
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tot = tm.totals()
+
+    # algorithmic work per step
+    it_mean = {}
+    elem_passes = 0
+    gemm_ops = calib_x_bytes = calib_w_bytes = ssz_bytes = quant_bytes = smooth_bytes = gemm_bytes = 0
+    for L in layers:
+        c = L["case"]
+        its = L["it"].cpu().numpy().astype(np.int64)
+        it_mean[c.name] = float(its.mean())
+        elem_passes += int(c.K * (its + 1).sum())
+        gemm_ops += 2 * c.T * c.N * c.K
+        calib_x_bytes += B * c.T * c.K * 2 + c.K * 4
+        calib_w_bytes += c.N * c.K * 2 + c.K * 4
+        smooth_bytes += 3 * c.K * 4
+        ssz_bytes += c.N * c.K * 2 + c.N * c.K + c.N * (4 + 4 + 8) + c.K * 4
+        quant_bytes += c.T * c.K * 2 + c.T * c.K + c.T * 4 + c.K * 4
+        gemm_bytes += c.T * c.K + c.N * c.K + 4 * c.T + 4 * c.N + 4 * c.T * c.N
+
+    K = args.steps
+
+    def sec(name):
+        return tot[name][0] / 1e3 / K  # seconds per step
+
+    gemm_s = sec("gemm")
+    gemm_tops = gemm_ops / gemm_s / 1e12
+    stages = {
+        "calib_x": {"ms": sec("calib_x") * 1e3, "GB/s": calib_x_bytes / sec("calib_x") / 1e9,
+                    "frac_hbm": calib_x_bytes / sec("calib_x") / PEAK_HBM, "launches_per_step": B * len(layers)},
+        "calib_w": {"ms": sec("calib_w") * 1e3, "GB/s": calib_w_bytes / sec("calib_w") / 1e9,
+                    "frac_hbm": calib_w_bytes / sec("calib_w") / PEAK_HBM},
+        "smooth": {"ms": sec("smooth") * 1e3},
+        "ssz": {"ms": sec("ssz") * 1e3, "GB/s": ssz_bytes / sec("ssz") / 1e9,
+                "frac_hbm": ssz_bytes / sec("ssz") / PEAK_HBM, "mean_iters": it_mean,
+                "element_passes": elem_passes,
+                "frac_alu": SSZ_OPS_PER_ELEM_PASS * elem_passes / sec("ssz") / PEAK_ALU},
+        "quant": {"ms": sec("quant") * 1e3, "GB/s": quant_bytes / sec("quant") / 1e9,
+                  "frac_hbm": quant_bytes / sec("quant") / PEAK_HBM},
+        "gemm": {"ms": gemm_s * 1e3, "TOPS": gemm_tops, "frac_i8": gemm_ops / gemm_s / PEAK_I8},
+    }
+    gpu_ms = sum(v[0] for v in tot.values()) / K
+
+    # dominant kernel: the stage with the largest share of the step
+    dom = max(("calib_x", "ssz", "quant", "gemm"), key=lambda n: tot[n][0])
+    if dom == "gemm":
+        launches = len(layers)
+        roof = {"kernel": "k_gemm_tile", "bound": "mfma", "achieved": gemm_ops / launches / (gemm_s / launches) / 1e12,
+                "peak": PEAK_I8 / 1e12, "unit": "TOP/s", "per_launch_ops": gemm_ops / launches}
+    elif dom == "ssz":
+        roof = {"kernel": "k_ssz", "bound": "alu",
+                "achieved": SSZ_OPS_PER_ELEM_PASS * elem_passes / sec("ssz") / 1e12,
+                "peak": PEAK_ALU / 1e12, "unit": "Tlane-op/s"}
+    elif dom == "calib_x":
+        roof = {"kernel": "k_absmax_cols", "bound": "hbm", "achieved": calib_x_bytes / sec("calib_x") / 1e9,
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"kernel": "k_quant_tok", "bound": "hbm", "achieved": quant_bytes / sec("quant") / 1e9,
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    rec = load_counters(roof["kernel"])
+    roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
+    roof["avg_launch_us"] = tot[dom][0] * 1e3 / tot[dom][1]
+
+    out = {
+        "metric": METRIC, "value": gemm_tops, "unit": "TOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "opt67b-prefill hidden 4096: fc1 X[4096,4096] W[16384,4096], fc2 X[4096,16384] "
+                               f"W[4096,16384], bf16, 1 percent outlier channels x60, {B} calibration batches, "
+                               f"alpha {args.alpha:g}, int8 SSZ",
+                   "tokens": 4096, "hidden": 4096, "calib_batches": B, "alpha": args.alpha, "bits": 8,
+                   "parallelism": "single GPU"},
+        "gpu_ms_per_step": gpu_ms, "step_tops": gemm_ops / (ms_per_step / 1e3) / 1e12,
+        "stages": stages, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers, args, synth)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layers, args, synth):
+    """The oracle (as it stands) on the host cores, on a bounded sample of the same workload: the whole
+    path per layer over every weight row and a slice of the token rows (calibration over that slice of
+    each calibration batch, SSZ over all rows, per-token quantization, GEMM and dequantization of the
+    slice).  The slice is sized so the oracle GEMM takes about --cpu-seconds in total.  Reported in the
+    metric's unit: int8 GEMM TOPS of the oracle."""
+    import oracle
+    probe_tok = 16
+    plans = []
+    for L in layers:
+        c = L["case"]
+        w = synth.widen(c.w())
+        xe = synth.widen(c.x_batch(args.calib_batches, T=probe_tok))
+        xq, _ = oracle.quant_per_token(xe)
+        wq = oracle.quant_per_token(w)[0]  # any int8 codes of the right shape serve to time the GEMM
+        g0 = time.perf_counter()
+        oracle.gemm_i8(xq, wq)
+        rate = 2 * probe_tok * c.N * c.K / (time.perf_counter() - g0)
+        plans.append((L, w, rate))
+    gemm_ops = 0
+    gemm_s = path_s = 0.0
+    detail = {}
+    for L, w, rate in plans:
+        c = L["case"]
+        tok = int(args.cpu_seconds / len(plans) * rate / (2 * c.N * c.K))
+        tok = max(16, min(c.T, (tok // 16) * 16))
+        xs = [synth.widen(c.x_batch(b, T=tok)) for b in range(args.calib_batches)]
+        xe = synth.widen(c.x_batch(args.calib_batches, T=tok))
+        t0 = time.perf_counter()
+        ax = None
+        for xb in xs:
+            ax = oracle.absmax_cols(xb, ax)
+        aw = oracle.absmax_cols(w)
+        s = oracle.smooth_factors(ax, aw, args.alpha)
+        t1 = time.perf_counter()
+        q = oracle.ssz(w, s, 8)
+        t2 = time.perf_counter()
+        xq, d = oracle.quant_per_token(xe, s)
+        t3 = time.perf_counter()
+        acc = oracle.gemm_i8(xq, q["q"])
+        t4 = time.perf_counter()
+        oracle.dequant(acc, d, q["S"])
+        t5 = time.perf_counter()
+        gemm_ops += 2 * tok * c.N * c.K
+        gemm_s += t4 - t3
+        path_s += t5 - t0
+        detail[c.name] = {"tokens": tok, "weight_rows": c.N, "calib_s": t1 - t0, "ssz_s": t2 - t1,
+                          "quant_s": t3 - t2, "gemm_s": t4 - t3, "dequant_s": t5 - t4}
+    return {"value": gemm_ops / gemm_s / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "per layer: all weight rows, a slice of tokens (see detail) of each of the %d calibration "
+                      "batches and of the forward batch; whole path timed, GEMM share sized to ~%gs"
+                      % (args.calib_batches, args.cpu_seconds),
+            "path_seconds": path_s, "detail": detail}
+
+
+if __name__ == "__main__":
+    main()

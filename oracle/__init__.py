@@ -70,10 +70,17 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = argt
             fn.restype = ci
+        lib.o_num_threads.argtypes = []
+        lib.o_num_threads.restype = ci
         lib.o_lsq_scale.restype = f64
         lib.o_mse_row.restype = f64
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's row-parallel loops use."""
+    return int(_load().o_num_threads())
 
 
 def _f32(a):

@@ -39,6 +39,7 @@
  * input.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,6 +48,9 @@
 #define O_EARG -1
 #define O_ENONFINITE -2
 #define O_EOVERFLOW -3
+
+/* Number of threads the OpenMP loops below use (reported by the CPU baseline). */
+int o_num_threads(void) { return omp_get_max_threads(); }
 
 static int all_finite(const float* a, int64_t n) {
   for (int64_t i = 0; i < n; ++i)

@@ -126,20 +126,26 @@ def sq_smooth_factors(act_amax, w_amax, alpha, s=None, stream=None):
 
 
 def ssz_weight_qparams(w, s=None, bits=8, symmetric=True, max_iter=SSZ_MAX_ITER, threshold=SSZ_THRESHOLD,
-                       min_scale=SSZ_MIN_SCALE, want_codes=True, want_stats=True, stream=None):
-    """Returns (scale[N] fp32, wq (int8 [N,K] or uint8 [N,K/2] for int4) or None, iters or None, mse or None)."""
+                       min_scale=SSZ_MIN_SCALE, want_codes=True, want_stats=True, scale=None, wq=None, iters=None,
+                       mse=None, stream=None):
+    """Returns (scale[N] fp32, wq (int8 [N,K] or uint8 [N,K/2] for int4) or None, iters or None, mse or None).
+    Output tensors may be passed in preallocated."""
     _dev(w, "w", _FLOATS)
     N, K = w.shape
     dev = w.device
     if s is not None:
         _dev(s, "s", (torch.float32,))
-    scale = torch.empty(N, dtype=torch.float32, device=dev)
-    wq = None
-    if want_codes:
+    if scale is None:
+        scale = torch.empty(N, dtype=torch.float32, device=dev)
+    if wq is None and want_codes:
         wq = torch.empty((N, K), dtype=torch.int8, device=dev) if bits == 8 else \
             torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    iters = torch.empty(N, dtype=torch.int32, device=dev) if want_stats else None
-    mse = torch.empty(N, dtype=torch.float64, device=dev) if want_stats else None
+    if want_stats:
+        iters = torch.empty(N, dtype=torch.int32, device=dev) if iters is None else iters
+        mse = torch.empty(N, dtype=torch.float64, device=dev) if mse is None else mse
+    for t, nm in ((scale, "scale"), (wq, "wq"), (iters, "iters"), (mse, "mse")):
+        if t is not None:
+            _dev(t, nm)
     _check(lib.ssz_weight_qparams(_ptr(w), _dtype_code(w), N, K, _ptr(s), int(bits), int(bool(symmetric)),
                                   int(max_iter), float(threshold), float(min_scale), _ptr(scale), _ptr(wq),
                                   _ptr(iters), _ptr(mse), _stream(stream)))
