@@ -6,24 +6,29 @@
 // dequantization runs in the epilogue of the same kernel ([INT8] 4.2 fusion).
 //
 // The only dense contraction of the path, so it runs on the CDNA4 matrix
-// cores: v_mfma_i32_16x16x64_i8 (A: 16 rows x 64 k, B: 64 k x 16 cols, each
-// lane supplying 16 bytes of one row, i.e. lane%16 selects the row/column and
-// lane/16 the 16-byte k-group; C: lane%16 = column, rows 4*(lane/16)+0..3).
-// Integer sums are exact, so the order of k inside a group never matters as
-// long as A and B use the same one, which they do (both are 16 contiguous k).
+// cores: v_mfma_i32_16x16x64_i8 (lane%16 selects the A row / B column, lane/16
+// the 16-byte k-group; C: lane%16 = column, rows 4*(lane/16)+0..3) or
+// v_mfma_i32_32x32x32_i8 (lane%32 selects the row/column, lane/32 the 16-byte
+// k-group of each 32-deep half; C: lane%32 = column, rows 8g + 4*(lane/32) +
+// 0..3 for g = 0..3).  Integer sums are exact, so the order of k inside a
+// group never matters as long as A and B use the same one, which they do
+// (both operands are 16 contiguous k of the same rows' K-contiguous storage).
 //
 // Two kernels:
-//  * k_gemm_tile  -- prefill: BM x BN block tiles, BK-deep K steps staged
-//                    through LDS (double buffer, one barrier per step), each
-//                    wave owning a TM x TN sub-tile of 16x16 fragments; LDS
-//                    rows are XOR-swizzled in 16-byte chunks so the MFMA
-//                    operand reads are bank-conflict free.
+//  * k_gemm_pipe   -- prefill.  BM x BN block tiles; each K step of BK bytes
+//                     stages a BM x BK A tile and a BN x BK B tile in an
+//                     ST-deep LDS ring with direct HBM->LDS 16-byte loads;
+//                     each wave owns a TM x TN sub-tile of MFMA fragments.
+//                     One barrier per K step.  The epilogue dequantizes from
+//                     registers with the tile's scales staged in LDS.
 //  * k_gemm_skinny -- decode (few tokens): HBM-bound weight streaming; each
-//                    block owns 16 output channels, its waves split K, the
-//                    weight chunks go straight from HBM to MFMA operand
-//                    registers and the int32 partials are summed in LDS.
+//                     block owns 16 output channels, its waves split K, the
+//                     weight chunks go straight from HBM to MFMA operand
+//                     registers and the int32 partials are summed in LDS.
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
+
+#include <type_traits>
 
 namespace ptq {
 
@@ -37,6 +42,14 @@ __device__ __forceinline__ v4i mfma16(const uint4& a, const uint4& b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
 }
 
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16i mfma32(const uint4& a, const uint4& b, v16i c) {
+  v4i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  v4i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0);
+}
+
 // 16-byte chunk position inside an LDS row of KC chunks (XOR swizzle by row)
 template <int KC>
 __device__ __forceinline__ int swz(int row, int kc) {
@@ -45,109 +58,228 @@ __device__ __forceinline__ int swz(int row, int kc) {
   else return kc;
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void k_gemm_tile(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+// ---------------------------------------------------------------------------
+// Prefill kernel pieces.
+//
+// Loads: global_load_lds_dwordx4 writes the 64 lanes' 16-byte chunks to 64
+// consecutive LDS slots (base in M0), so each lane picks the global chunk
+// that belongs in its slot under the XOR swizzle; the MFMA operand reads are
+// then bank-conflict free.  Chunks outside the matrix (M, N or K tails) load
+// from a 16-byte block of zeros.  The loads are issued with inline asm and
+// their completion is tracked only by explicit vmcnt waits that leave the
+// ST-2 younger stages in flight (the compiler, tracking such loads itself,
+// would drain the whole ring before every LDS read).  The asm has no output
+// registers -- the data goes to LDS through M0 -- so no register is ever
+// pending.  The barrier is an asm s_barrier with a memory clobber: the LDS
+// reads of a stage stay after it, and the loads into a buffer are issued
+// only after every wave has passed it, i.e. finished reading that buffer.
+//
+// Tile order: the hardware deals block i to XCD i % 8; tile_of gives each XCD
+// a contiguous range of tiles, walked in groups of GM tile rows, so the
+// blocks resident on one XCD share A and B panels in that XCD's L2.
+__device__ const uint4 g_zero16 = {0u, 0u, 0u, 0u};
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 layout: vmcnt bits [3:0] and [15:14],
+// expcnt [6:4] and lgkmcnt [11:8] left at their maxima)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+static_assert(vmcnt_imm(16) == 0x4F70 && vmcnt_imm(3) == 0x0F73, "waitcnt encoding");
+
+__device__ __forceinline__ void tile_of(int tm, int tn, int gm_group, int& tile_m, int& tile_n, int bid, int nb) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int lid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int width = gm_group * tn;
+  const int group = lid / width;
+  const int first_m = group * gm_group;
+  const int gsz = tm - first_m < gm_group ? tm - first_m : gm_group;
+  const int in = lid - group * width;
+  tile_m = first_m + in % gsz;
+  tile_n = in / gsz;
+}
+
+__device__ __forceinline__ void dma16_lds(const void* g, uint32_t lds_byte_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off\n\t"
+      :
+      : "v"(g), "s"(lds_byte_addr)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, bool PERSIST, int OCC>
+__global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           const float* __restrict__ ts, const float* __restrict__ cs,
                                                           int M, int N, int K, float* __restrict__ Y,
-                                                          int32_t* __restrict__ ACC, int tiles_n) {
-  constexpr int NT = WM * WN * 64;
+                                                          int32_t* __restrict__ ACC, int tiles_m, int tiles_n) {
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int KC = BK / 16;
-  constexpr int A_PT = BM * KC / NT, B_PT = BN * KC / NT;
-  static_assert(A_PT * NT == BM * KC && B_PT * NT == BN * KC, "tile loads must divide evenly");
-  __shared__ uint4 sA[2][BM * KC];
-  __shared__ uint4 sB[2][BN * KC];
+  constexpr int FM = TM / MF, FN = TN / MF;
+  constexpr int KC = BK / 16;  // 16-byte chunks per row of a K step
+  static_assert(KC == 4 || KC == 8, "BK 64 or 128");
+  constexpr int A_CH = BM * KC, B_CH = BN * KC, S_CH = A_CH + B_CH;
+  constexpr int A_PW = A_CH / (NW * 64), B_PW = B_CH / (NW * 64);
+  static_assert(A_PW * NW * 64 == A_CH && B_PW * NW * 64 == B_CH, "tile loads must divide evenly");
+  static_assert(ST >= 2 && ST <= 8, "2..8 stages");
+  using acc_t = typename std::conditional<MF == 32, v16i, v4i>::type;
+  constexpr int NR = MF == 32 ? 16 : 4;
+  constexpr int PER = A_PW + B_PW;  // loads per stage per thread
+  static_assert((ST - 2) * PER <= 63, "vmcnt range");
+  __shared__ uint4 sm[ST * S_CH];
+  __shared__ __attribute__((aligned(16))) float s_ts[BM];  // the tile's token scales
+  __shared__ float s_cs[BN];                               // and channel scales
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lk = lane >> 4;
-  const int tile = blockIdx.x;
-  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  const uint32_t sm_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
+  const int ntiles = tiles_m * tiles_n;
+  // persistent: block b takes virtual ids b, b + grid, ...; the grid is a multiple of 8 so every
+  // virtual id stays on the block's XCD and tile_of keeps each round's tiles grouped per XCD
+  for (int vt = blockIdx.x; vt < ntiles; vt += (PERSIST ? gridDim.x : ntiles)) {
+  int tile_m, tile_n;
+  tile_of(tiles_m, tiles_n, GM, tile_m, tile_n, vt, PERSIST ? ntiles : gridDim.x);
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  __syncthreads();  // the previous tile's epilogue and last K steps are done with LDS
+  for (int t = tid; t < BM; t += NW * 64) s_ts[t] = m0 + t < M ? ts[m0 + t] : 0.0f;
+  for (int t = tid; t < BN; t += NW * 64) s_cs[t] = n0 + t < N ? cs[n0 + t] : 0.0f;
+  __syncthreads();
 
-  uint4 ra[A_PT], rb[B_PT];
-  auto gload = [&](int k0) {
+  // per-lane source rows/chunks of the loads (the LDS slot is fixed by lane order and the swizzle)
+  const int8_t* a_src[A_PW];
+  bool a_ok[A_PW];
+  int a_k[A_PW];
 #pragma unroll
-    for (int i = 0; i < A_PT; ++i) {
-      const int c = tid + i * NT, row = c / KC, kc = c % KC;
-      const int gm = m0 + row, gk = k0 + kc * 16;
-      ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const uint4*>(A + (int64_t)gm * K + gk) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < A_PW; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane;
+    const int row = slot / KC;
+    a_k[i] = swz<KC>(row, slot % KC) * 16;
+    a_ok[i] = m0 + row < M;
+    a_src[i] = A + (int64_t)(a_ok[i] ? m0 + row : 0) * K;
+  }
+  const int8_t* b_src[B_PW];
+  bool b_ok[B_PW];
+  int b_k[B_PW];
+#pragma unroll
+  for (int i = 0; i < B_PW; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane;
+    const int row = slot / KC;
+    b_k[i] = swz<KC>(row, slot % KC) * 16;
+    b_ok[i] = n0 + row < N;
+    b_src[i] = B + (int64_t)(b_ok[i] ? n0 + row : 0) * K;
+  }
+
+  auto issue = [&](int buf, int k0) {
+    const uint32_t base = sm_base + (uint32_t)(buf * S_CH) * 16u;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int gk = k0 + a_k[i];
+      const void* src = (a_ok[i] && gk < K) ? (const void*)(a_src[i] + gk) : (const void*)&g_zero16;
+      dma16_lds(src, base + (uint32_t)((i * NW + wave) * 64) * 16u);
     }
 #pragma unroll
-    for (int i = 0; i < B_PT; ++i) {
-      const int c = tid + i * NT, row = c / KC, kc = c % KC;
-      const int gn = n0 + row, gk = k0 + kc * 16;
-      rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + gk) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < B_PW; ++i) {
+      const int gk = k0 + b_k[i];
+      const void* src = (b_ok[i] && gk < K) ? (const void*)(b_src[i] + gk) : (const void*)&g_zero16;
+      dma16_lds(src, base + (uint32_t)(A_CH + (i * NW + wave) * 64) * 16u);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PT; ++i) {
-      const int c = tid + i * NT, row = c / KC, kc = c % KC;
-      sA[buf][row * KC + swz<KC>(row, kc)] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PT; ++i) {
-      const int c = tid + i * NT, row = c / KC, kc = c % KC;
-      sB[buf][row * KC + swz<KC>(row, kc)] = rb[i];
-    }
-  };
 
-  v4i acc[FM][FN];
+  acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int ks = 0; ks < BK / 64; ++ks) {
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0;
+
+  auto compute = [&](int buf) {
+    const uint4* sa = sm + buf * S_CH;
+    const uint4* sb = sa + A_CH;
+    constexpr int KS = (MF == 32 ? 2 : 1) * (BK / 64);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int rl = MF == 32 ? (lane & 31) : lr;
+      const int ch = MF == 32 ? ks * 2 + (lane >> 5) : ks * 4 + lk;
       uint4 a[FM], b[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int row = wm * TM + i * 16 + lr;
-        a[i] = sA[cur][row * KC + swz<KC>(row, ks * 4 + lk)];
+        const int row = wm * TM + i * MF + rl;
+        a[i] = sa[row * KC + swz<KC>(row, ch)];
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int row = wn * TN + j * 16 + lr;
-        b[j] = sB[cur][row * KC + swz<KC>(row, ks * 4 + lk)];
+        const int row = wn * TN + j * MF + rl;
+        b[j] = sb[row * KC + swz<KC>(row, ch)];
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (MF == 32) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+          else acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        }
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) issue(s, s * BK);
+
+  int buf = 0;
+  for (int k = 0; k < nk; ++k) {
+    // this thread's loads of step k have landed once at most `younger` later stages are pending
+    const int younger = (nk - 1 - k) < (ST - 2) ? (nk - 1 - k) : (ST - 2);
+    switch (younger) {
+      case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PER)); break;
+      default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER)); break;
+    }
+    block_barrier();  // step k is in LDS for every wave; every wave is done with step k-1's buffer
+    if (k + ST - 1 < nk) issue(buf == 0 ? ST - 1 : buf - 1, (k + ST - 1) * BK);
+    compute(buf);
+    buf = buf + 1 == ST ? 0 : buf + 1;
   }
 
-  // epilogue: dequantize and store
+  // epilogue: dequantize and store.  Each lane holds, per fragment, one column and groups of 4
+  // consecutive rows (16x16: rows 4*(lane/16)+0..3; 32x32: rows 8*g + 4*(lane/32) + 0..3, g = 0..3),
+  // so the token scales of a group are one 16-byte LDS read.
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+  constexpr int NG = NR / 4;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * TN + j * 16 + lr;
-    const float csn = n < N ? cs[n] : 0.0f;
+    const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
+    const int n = n0 + cl;
+    const float csn = s_cs[cl];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * TM + i * 16 + lk * 4 + r;
-        if (m < M && n < N) {
-          const int a = acc[i][j][r];
-          const float sc = ts[m] * csn;
-          Y[(int64_t)m * N + n] = (float)a * sc;
-          if (ACC) ACC[(int64_t)m * N + n] = a;
+      for (int g = 0; g < NG; ++g) {
+        const int rl0 = wm * TM + i * MF + (MF == 32 ? 8 * g + 4 * (lane >> 5) : lk * 4);
+        const float4 t4 = *reinterpret_cast<const float4*>(&s_ts[rl0]);
+        const float tsv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + rl0 + q;
+          const int a = acc[i][j][g * 4 + q];
+          if (full || (m < M && n < N)) {
+            Y[(int64_t)m * N + n] = (float)a * (tsv[q] * csn);
+            if (ACC) ACC[(int64_t)m * N + n] = a;
+          }
         }
       }
     }
   }
+  }  // tile loop
 }
 
 // Decode: M <= 16*MT tokens, 16 output channels per block, KS waves splitting K.
@@ -212,12 +344,12 @@ __global__ __launch_bounds__(KS * 64) void k_gemm_skinny(const int8_t* __restric
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
-hipError_t launch_tile(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
-                       float* y, int32_t* acc, hipStream_t stream) {
+template <int BM, int BN, int BK, int WM, int WN, int ST, int MF>
+hipError_t launch_tiled(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
+                        float* y, int32_t* acc, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  k_gemm_tile<BM, BN, BK, WM, WN><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(xq, wq, ts, cs, M, N, K, y, acc,
-                                                                                   tn);
+  k_gemm_pipe<BM, BN, BK, WM, WN, ST, 4, MF, false, 1><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
+      xq, wq, ts, cs, M, N, K, y, acc, tm, tn);
   return hipGetLastError();
 }
 
@@ -237,7 +369,13 @@ hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* 
   if (M <= 16) return launch_skinny<1>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
   if (M <= 32) return launch_skinny<2>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
   if (M <= 64) return launch_skinny<4>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  return launch_tile<256, 256, 64, 2, 4>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  // the largest tile that still gives about one tile per CU (256 CUs)
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 200)
+    return launch_tiled<256, 256, 128, 2, 4, 2, 16>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  if (M >= N)
+    return launch_tiled<256, 128, 128, 4, 2, 2, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  return launch_tiled<128, 256, 128, 2, 4, 2, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
 }
 
 }  // namespace ptq
