@@ -8,12 +8,17 @@
 //
 // One block of TPR threads owns one row (output channel).  The row is read
 // from HBM once and stays in registers (CPT chunks of 16 elements per
-// thread) for every pass; all passes are ALU work.  One pass over the row
-// for a scale S computes, per element, the code q = clamp(rne(w_hat * inv S))
-// and accumulates sum(w_hat q) and sum((w_hat - S q)^2) in fp64 and sum(q^2)
-// exactly (fp32 per lane, integer across lanes).  The sums are reduced with
-// xor butterflies (identical in every lane) and, for multi-wave rows, through
-// LDS in wave order, so every decision is uniform across the row.
+// thread, in fp32 and, when it fits, also widened to fp64) for every pass;
+// all passes are ALU work.  One pass over the row for a scale S computes, per
+// element, the code q = clamp(rne(w_hat * inv S)) and accumulates A =
+// sum(w_hat q) in fp64 and B = sum(q^2) exactly (fp32 per lane, integer
+// across lanes) -- the two sums the least-squares step needs.  The error of
+// the pass follows from the same sums and the row's sum of squares W2
+// (computed once): K * mse(S) = W2 - 2 S A + S^2 B, the expansion of
+// sum (w_hat - S q)^2, evaluated in fp64 and clamped at 0.  The sums are
+// reduced with xor butterflies (identical in every lane) and, for multi-wave
+// rows, through LDS in wave order, so every decision is uniform across the
+// row.
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
 
@@ -23,54 +28,53 @@ namespace {
 
 struct PassSums {
   double a;  // sum w_hat q
-  double e;  // sum (w_hat - S q)^2
   int b;     // sum q^2
 };
 
-template <int TPR, int CPT>
-__device__ __forceinline__ PassSums row_pass(const float (&wh)[CPT][16], float S, float qmax, double (*red_d)[2],
-                                             int* red_i, int tid) {
+template <int TPR, int CPT, bool WIDE>
+__device__ __forceinline__ PassSums row_pass(const float (&wh)[CPT][16], const double (&wd)[WIDE ? CPT : 1][16],
+                                             float S, float qmax, double* red_d, int* red_i, int tid) {
   const float inv = 1.0f / S;
-  const double Sd = (double)S;
-  double a = 0.0, e = 0.0;
+  double a = 0.0;
   float bq = 0.0f;  // at most 16*CPT terms of <= 127^2 each: exact in fp32
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float q = code_f(wh[m][k], inv, qmax);
-      const double qd = (double)q, wd = (double)wh[m][k];
-      a = __builtin_fma(wd, qd, a);
-      const double d = __builtin_fma(-Sd, qd, wd);  // S*q is exact in fp64
-      e = __builtin_fma(d, d, e);
+      const double w = WIDE ? wd[WIDE ? m : 0][k] : (double)wh[m][k];
+      a = __builtin_fma(w, (double)q, a);
       bq = __builtin_fmaf(q, q, bq);
     }
   }
   PassSums r;
   r.a = wave_sum(a);
-  r.e = wave_sum(e);
   r.b = wave_sum((int)bq);
   constexpr int NW = TPR / kWave;
   if constexpr (NW > 1) {
     const int w = tid / kWave;
     __syncthreads();  // previous readers of the LDS slots are done
     if ((tid & (kWave - 1)) == 0) {
-      red_d[w][0] = r.a;
-      red_d[w][1] = r.e;
+      red_d[w] = r.a;
       red_i[w] = r.b;
     }
     __syncthreads();
-    r.a = red_d[0][0];
-    r.e = red_d[0][1];
+    r.a = red_d[0];
     r.b = red_i[0];
 #pragma unroll
     for (int i = 1; i < NW; ++i) {
-      r.a += red_d[i][0];
-      r.e += red_d[i][1];
+      r.a += red_d[i];
       r.b += red_i[i];
     }
   }
   return r;
+}
+
+// K * mse(S) from the pass sums: W2 - 2 S A + S^2 B, never below 0
+__device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) {
+  const double Sd = (double)S;
+  const double e = (w2 - 2.0 * Sd * p.a) + Sd * Sd * (double)p.b;
+  return e > 0.0 ? e : 0.0;
 }
 
 template <int DT, bool HAS_S, int BITS, int TPR, int CPT>
@@ -79,8 +83,9 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
                                              float* __restrict__ scale, void* __restrict__ wq,
                                              int32_t* __restrict__ iters, double* __restrict__ mse) {
   constexpr int NW = TPR / kWave;
+  constexpr bool WIDE = CPT <= 4 && TPR <= 256;  // fp64 copy of the row fits the register budget
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
-  __shared__ double red_d[NW][2];
+  __shared__ double red_d[NW];
   __shared__ int red_i[NW];
   __shared__ float red_f[NW];
   const int tid = threadIdx.x;
@@ -90,7 +95,9 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
     // load + fold; out-of-row chunks are zeros (they add nothing to any sum)
     float wh[CPT][16];
+    double wd[WIDE ? CPT : 1][16];
     float m = 0.0f;
+    double w2 = 0.0;
 #pragma unroll
     for (int c8 = 0; c8 < CPT; ++c8) {
       const int64_t c = tid + (int64_t)TPR * c8;
@@ -119,23 +126,36 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
         for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(wh[c8][e]));
+      for (int e = 0; e < 16; ++e) {
+        m = fmaxf(m, fabsf(wh[c8][e]));
+        const double x = (double)wh[c8][e];
+        if constexpr (WIDE) wd[c8][e] = x;
+        w2 = __builtin_fma(x, x, w2);
+      }
     }
     m = wave_max(m);
+    w2 = wave_sum(w2);
     if constexpr (NW > 1) {
       __syncthreads();
-      if ((tid & (kWave - 1)) == 0) red_f[tid / kWave] = m;
+      if ((tid & (kWave - 1)) == 0) {
+        red_f[tid / kWave] = m;
+        red_d[tid / kWave] = w2;
+      }
       __syncthreads();
       m = red_f[0];
+      w2 = red_d[0];
 #pragma unroll
-      for (int i = 1; i < NW; ++i) m = fmaxf(m, red_f[i]);
+      for (int i = 1; i < NW; ++i) {
+        m = fmaxf(m, red_f[i]);
+        w2 += red_d[i];
+      }
     }
 
     // MinMax init
     float S = m / QMAX;
     S = S < min_scale ? min_scale : S;
-    PassSums cur = row_pass<TPR, CPT>(wh, S, QMAX, red_d, red_i, tid);
-    double best = cur.e / Kd;
+    PassSums cur = row_pass<TPR, CPT, WIDE>(wh, wd, S, QMAX, red_d, red_i, tid);
+    double best = sq_err(w2, S, cur) / Kd;
     double A = cur.a;
     int B = cur.b;
 
@@ -146,8 +166,8 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
       if (B == 0) break;
       float Sc = (float)(A / (double)B);
       Sc = Sc < min_scale ? min_scale : Sc;
-      const PassSums p = row_pass<TPR, CPT>(wh, Sc, QMAX, red_d, red_i, tid);
-      const double c = p.e / Kd;
+      const PassSums p = row_pass<TPR, CPT, WIDE>(wh, wd, Sc, QMAX, red_d, red_i, tid);
+      const double c = sq_err(w2, Sc, p) / Kd;
       const double d = best - c;
       const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
       if (c < best) {
@@ -159,16 +179,23 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
       if (conv) break;
     }
 
-    // codes of the kept scale
-    if (wq) {
+    // codes of the kept scale, and its error summed directly (the reported mse; the expansion
+    // above loses relative accuracy when the error is tiny next to W2)
+    double e_dir = 0.0;
+    if (wq || mse) {
       const float inv = 1.0f / S;
+      const double Sd = (double)S;
 #pragma unroll
       for (int c8 = 0; c8 < CPT; ++c8) {
         const int64_t c = tid + (int64_t)TPR * c8;
-        if (c < nchunk) {
-          float q[16];
+        float q[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) q[e] = code_f(wh[c8][e], inv, QMAX);
+        for (int e = 0; e < 16; ++e) {
+          q[e] = code_f(wh[c8][e], inv, QMAX);
+          const double dd = __builtin_fma(-Sd, (double)q[e], (double)wh[c8][e]);  // S*q is exact in fp64
+          e_dir = __builtin_fma(dd, dd, e_dir);
+        }
+        if (wq && c < nchunk) {
           if constexpr (BITS == 8) {
             uint4 o;
             o.x = pack4_i8(q[0], q[1], q[2], q[3]);
@@ -184,11 +211,22 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
           }
         }
       }
+      if (mse) {
+        e_dir = wave_sum(e_dir);
+        if constexpr (NW > 1) {
+          __syncthreads();
+          if ((tid & (kWave - 1)) == 0) red_d[tid / kWave] = e_dir;
+          __syncthreads();
+          e_dir = red_d[0];
+#pragma unroll
+          for (int i = 1; i < NW; ++i) e_dir += red_d[i];
+        }
+      }
     }
     if (tid == 0) {
       scale[n] = S;
       if (iters) iters[n] = it;
-      if (mse) mse[n] = best;
+      if (mse) mse[n] = e_dir / Kd;
     }
   }
 }
