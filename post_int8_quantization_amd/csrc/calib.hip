@@ -2,11 +2,12 @@
 //
 // Column absmax ([SQ] max|X_j|, max|W_j| along the input channel j; [INT8] 2.1
 // range calibration).  HBM-bound: every element is read once with 16-byte
-// loads ([INT8] 3.1).  A block covers 16 vector-columns (256 bytes of a row)
-// and a chunk of rows; its 16 row-lanes keep running maxima in registers, fold
-// them through LDS, and publish one atomic max per column.  Maxima of
-// non-negative floats order like their bit patterns, so an unsigned atomic max
-// gives the exact result in any order.
+// loads ([INT8] 3.1).  A block of 16 waves owns a strip of 64 16-byte vector
+// columns (1 KB of every row) and a run of rows; each wave streams its own
+// contiguous rows with 16 loads in flight per lane, keeping running maxima in
+// registers.  The 16 waves merge through LDS and the block publishes one
+// atomic max per column.  Maxima of non-negative floats order like their bit
+// patterns, so an unsigned atomic max gives the exact result in any order.
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
 
@@ -16,10 +17,10 @@ namespace ptq {
 
 namespace {
 
-constexpr int kCalibThreads = 256;
-constexpr int kVecCols = 16;   // vector-columns per block (lanes % 16)
-constexpr int kRowLanes = 16;  // row-lanes per block
-constexpr int kUnroll = 4;     // rows in flight per thread
+constexpr int kWaves = 16;               // waves per block
+constexpr int kThreads = kWaves * kWave;  // 1024
+constexpr int kVecs = kWave;              // 16-byte vector columns per block strip
+constexpr int kInFlight = 16;             // loads in flight per lane
 
 template <int DT>
 struct Vec {
@@ -27,54 +28,57 @@ struct Vec {
 };
 
 template <int DT>
-__global__ __launch_bounds__(kCalibThreads) void k_absmax_cols(const uint4* __restrict__ x, int64_t rows,
-                                                                int64_t vecs_per_row, int64_t rows_per_chunk,
-                                                                unsigned* __restrict__ amax_bits) {
+__device__ __forceinline__ void fold_max(float (&m)[Vec<DT>::kElems], const uint4& d) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  if constexpr (DT == PTQ_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = fmaxf(m[2 * i], fabsf(bf16_lo(w[i])));
+      m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf16_hi(w[i])));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], fabsf(__uint_as_float(w[i])));
+  }
+}
+
+// grid: x = column strips, y = row runs of rows_per_block rows (split evenly over the 16 waves)
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_absmax_cols(const uint4* __restrict__ x, int64_t rows,
+                                                         int64_t vecs_per_row, int64_t rows_per_block,
+                                                         unsigned* __restrict__ amax_bits) {
   constexpr int E = Vec<DT>::kElems;
-  __shared__ float red[kRowLanes][kVecCols * E + 1];
+  __shared__ float red[kWaves][kVecs * E];
   const int tid = threadIdx.x;
-  const int vc = tid % kVecCols, rl = tid / kVecCols;
-  const int64_t v = (int64_t)blockIdx.x * kVecCols + vc;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
-  const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t v = (int64_t)blockIdx.x * kVecs + lane;
+  const int64_t per_wave = (rows_per_block + kWaves - 1) / kWaves;
+  const int64_t b0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t b1 = b0 + rows_per_block < rows ? b0 + rows_per_block : rows;
+  const int64_t r0 = b0 + wave * per_wave;
+  const int64_t r1 = r0 + per_wave < b1 ? r0 + per_wave : b1;
 
   float m[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) m[e] = 0.0f;
-
   if (v < vecs_per_row) {
-    for (int64_t r = r0 + rl; r < r1; r += kRowLanes * kUnroll) {
-      uint4 d[kUnroll];
+    const uint4* p = x + v;
+    for (int64_t r = r0; r < r1; r += kInFlight) {
+      uint4 d[kInFlight];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t rr = r + (int64_t)u * kRowLanes;
-        d[u] = rr < r1 ? x[rr * vecs_per_row + v] : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < kInFlight; ++u) d[u] = r + u < r1 ? p[(r + u) * vecs_per_row] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t w[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
-        if constexpr (DT == PTQ_BF16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            m[2 * i] = fmaxf(m[2 * i], fabsf(bf16_lo(w[i])));
-            m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf16_hi(w[i])));
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], fabsf(__uint_as_float(w[i])));
-        }
-      }
+      for (int u = 0; u < kInFlight; ++u) fold_max<DT>(m, d[u]);
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[rl][vc * E + e] = m[e];
+  for (int e = 0; e < E; ++e) red[wave][lane * E + e] = m[e];
   __syncthreads();
-  if (tid < kVecCols * E) {
-    const int c = tid;  // column within the block's 16*E columns
+  for (int c = tid; c < kVecs * E; c += kThreads) {
     float mm = red[0][c];
 #pragma unroll
-    for (int i = 1; i < kRowLanes; ++i) mm = fmaxf(mm, red[i][c]);
-    const int64_t vcol = (int64_t)blockIdx.x * kVecCols + c / E;
+    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, red[w][c]);
+    const int64_t vcol = (int64_t)blockIdx.x * kVecs + c / E;
     if (vcol < vecs_per_row) atomicMax(amax_bits + vcol * E + (c % E), __float_as_uint(mm));
   }
 }
@@ -107,20 +111,21 @@ hipError_t launch_absmax_cols(const void* x, int dtype, int64_t rows, int64_t co
   }
   const int E = dtype == PTQ_BF16 ? 8 : 4;
   const int64_t vecs = cols / E;
-  const int64_t gx = (vecs + kVecCols - 1) / kVecCols;
-  // aim at ~2048 blocks; at least 64 rows per block so the per-column atomics stay few
-  const int64_t step = kRowLanes * kUnroll;
-  int64_t chunk = (rows * gx + 2047) / 2048;
-  chunk = ((chunk + step - 1) / step) * step;
-  if (chunk < step) chunk = step;
-  const int64_t gy = (rows + chunk - 1) / chunk;
+  const int64_t gx = (vecs + kVecs - 1) / kVecs;
+  // about one block per CU (256 CUs) and at least one row per wave
+  int64_t gy = (256 + gx - 1) / gx;
+  const int64_t max_gy = (rows + kWaves - 1) / kWaves;
+  if (gy > max_gy) gy = max_gy;
+  if (gy > 65535) gy = 65535;
+  const int64_t rows_per_block = (rows + gy - 1) / gy;
+  gy = (rows + rows_per_block - 1) / rows_per_block;
   dim3 grid((unsigned)gx, (unsigned)gy);
   if (dtype == PTQ_BF16)
-    k_absmax_cols<PTQ_BF16><<<grid, kCalibThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
-                                                                 chunk, reinterpret_cast<unsigned*>(amax));
+    k_absmax_cols<PTQ_BF16><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
+                                                            rows_per_block, reinterpret_cast<unsigned*>(amax));
   else
-    k_absmax_cols<PTQ_F32><<<grid, kCalibThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs, chunk,
-                                                                reinterpret_cast<unsigned*>(amax));
+    k_absmax_cols<PTQ_F32><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
+                                                           rows_per_block, reinterpret_cast<unsigned*>(amax));
   return hipGetLastError();
 }
 

@@ -17,6 +17,9 @@ hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, fl
 hipError_t launch_quant_per_token(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,
                                   float* tok_scale, hipStream_t stream);
 
+hipError_t launch_quant_per_token_rpb(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,
+                                      float* tok_scale, int64_t rows_per_block, hipStream_t stream);
+
 hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits, int max_iter,
                       double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,
                       hipStream_t stream);
