@@ -50,7 +50,21 @@ def parse():
     p.add_argument("--calib-batches", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle GEMM time of the CPU baseline")
+    p.add_argument("--copy-ref", action="store_true",
+                   help="only run a plain 1 GiB device copy three times (reference for scaling the "
+                        "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def copy_reference():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": n, "repeats": 3}), flush=True)
 
 
 class Timer:
@@ -98,6 +112,9 @@ def load_counters(kernel_tag):
 
 def main():
     args = parse()
+    if args.copy_ref:
+        copy_reference()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the path "
