@@ -2,11 +2,12 @@
 //
 // Column absmax ([SQ] max|X_j|, max|W_j| along the input channel j; [INT8] 2.1
 // range calibration).  HBM-bound: every element is read once with 16-byte
-// loads ([INT8] 3.1).  A block of 16 waves owns a strip of 64 16-byte vector
-// columns (1 KB of every row) and a run of rows; each wave streams its own
-// contiguous rows with 16 loads in flight per lane, keeping running maxima in
-// registers.  The 16 waves merge through LDS and the block publishes one
-// atomic max per column.  Maxima of non-negative floats order like their bit
+// loads ([INT8] 3.1, streaming hint).  A block of 4 waves owns a strip of 64
+// 16-byte vector columns (1 KB of every row) and a run of rows; each wave
+// streams its own contiguous rows with 16 loads in flight per lane, keeping
+// running maxima in registers; about 4 blocks per CU keep ~256 KB in flight
+// per CU.  The waves merge through LDS and the block publishes one atomic max
+// per column.  Maxima of non-negative floats order like their bit
 // patterns, so an unsigned atomic max gives the exact result in any order.
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
@@ -17,8 +18,8 @@ namespace ptq {
 
 namespace {
 
-constexpr int kWaves = 16;               // waves per block
-constexpr int kThreads = kWaves * kWave;  // 1024
+constexpr int kWaves = 4;                // waves per block
+constexpr int kThreads = kWaves * kWave;  // 256
 constexpr int kVecs = kWave;              // 16-byte vector columns per block strip
 constexpr int kInFlight = 16;             // loads in flight per lane
 
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_absmax_cols(const uint4* __restric
     for (int64_t r = r0; r < r1; r += kInFlight) {
       uint4 d[kInFlight];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) d[u] = r + u < r1 ? p[(r + u) * vecs_per_row] : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < kInFlight; ++u) d[u] = r + u < r1 ? load_once(p + (r + u) * vecs_per_row) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) fold_max<DT>(m, d[u]);
     }
@@ -112,8 +113,8 @@ hipError_t launch_absmax_cols(const void* x, int dtype, int64_t rows, int64_t co
   const int E = dtype == PTQ_BF16 ? 8 : 4;
   const int64_t vecs = cols / E;
   const int64_t gx = (vecs + kVecs - 1) / kVecs;
-  // about one block per CU (256 CUs) and at least one row per wave
-  int64_t gy = (256 + gx - 1) / gx;
+  // about 4 blocks per CU (256 CUs) and at least one row per wave
+  int64_t gy = (1024 + gx - 1) / gx;
   const int64_t max_gy = (rows + kWaves - 1) / kWaves;
   if (gy > max_gy) gy = max_gy;
   if (gy > 65535) gy = 65535;

@@ -109,7 +109,7 @@ __device__ __forceinline__ void dma16_lds(const void* g, uint32_t lds_byte_addr)
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, bool PERSIST, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, bool PERSIST, int OCC, bool NTS = true>
 __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           const float* __restrict__ ts, const float* __restrict__ cs,
                                                           int M, int N, int K, float* __restrict__ Y,
@@ -272,7 +272,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
           const int m = m0 + rl0 + q;
           const int a = acc[i][j][g * 4 + q];
           if (full || (m < M && n < N)) {
-            Y[(int64_t)m * N + n] = (float)a * (tsv[q] * csn);
+            const float yv = (float)a * (tsv[q] * csn);
+            if constexpr (NTS) __builtin_nontemporal_store(yv, &Y[(int64_t)m * N + n]);  // written once, not re-read
+            else Y[(int64_t)m * N + n] = yv;
             if (ACC) ACC[(int64_t)m * N + n] = a;
           }
         }

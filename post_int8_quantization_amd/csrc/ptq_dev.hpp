@@ -14,6 +14,14 @@ namespace ptq {
 
 constexpr int kWave = 64;
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data read exactly once (streaming; nontemporal hint)
+__device__ __forceinline__ uint4 load_once(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bf16 pair in one dword -> two fp32 (exact widening)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
@@ -22,16 +30,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 template <int DT>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
   if constexpr (DT == PTQ_BF16) {
-    const uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    const uint4 d = load_once(reinterpret_cast<const uint16_t*>(base) + elem);
     v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
     v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
     v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
     v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const float* p = reinterpret_cast<const float*>(base) + elem;
+    const uint4 a = load_once(p), b = load_once(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
   }
 }
 

@@ -34,7 +34,7 @@ __device__ __forceinline__ void load_raw(const void* x, int64_t t, int64_t K, in
   for (int m = 0; m < CPT; ++m) {
     const int64_t c = tid + (int64_t)TPR * m;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) raw[m][q] = c < nchunk ? row[c * NV + q] : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < NV; ++q) raw[m][q] = c < nchunk ? load_once(row + c * NV + q) : make_uint4(0, 0, 0, 0);
   }
 }
 
