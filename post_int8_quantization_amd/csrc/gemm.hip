@@ -375,9 +375,10 @@ hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* 
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 200)
     return launch_tiled<256, 256, 128, 2, 4, 2, 16>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  // smaller tiles: three 48 KB stages in flight instead of two 64 KB ones
   if (M >= N)
-    return launch_tiled<256, 128, 128, 4, 2, 2, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  return launch_tiled<128, 256, 128, 2, 4, 2, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+    return launch_tiled<256, 128, 128, 4, 2, 3, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  return launch_tiled<128, 256, 128, 2, 4, 3, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
 }
 
 }  // namespace ptq
