@@ -1,8 +1,9 @@
 // ptq_dev.hpp -- device helpers shared by the gfx950 kernels of libptq.
 //
-// Wavefronts are 64 lanes.  Cross-lane reductions use xor butterflies: every
-// lane ends with the same bits (fp addition is commutative, so partner lanes
-// add the same two partials), which keeps per-row decisions uniform.
+// Wavefronts are 64 lanes.  Cross-lane reductions are butterflies in which
+// every lane ends with the same bits (fp addition and max are commutative, so
+// the two lanes of a pair combine the same two partials), which keeps per-row
+// decisions uniform.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,21 +44,80 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)
   }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Lane exchanges for the butterflies.  Steps 1, 2, 4 and 8 stay inside a row of
+// 16 lanes and use DPP moves (quad permutes, then the half-row and row
+// mirrors, which pair each group of 4 or 8 lanes with the other half of the
+// group after the earlier steps have made the group uniform); steps 16 and 32
+// use the gfx950 row swaps (v_permlane16_swap / v_permlane32_swap), which
+// hand every lane the same lane of the paired row or half.  All are VALU
+// moves: no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
+
+// Applies OP(v, partner) for each butterfly step; partner values are the same
+// lanes' values of the other half of every group, so both lanes of a pair
+// combine the same two operands.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<kDppXor1>(v));
+  v = op(v, dpp_u32<kDppXor2>(v));
+  v = op(v, dpp_u32<kDppHalfMirror>(v));
+  v = op(v, dpp_u32<kDppMirror>(v));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(r[0], r[1]);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = op(r[0], r[1]);
+  }
   return v;
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(
+      wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); }));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return (int)wave_reduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return (uint32_t)((int)a + (int)b); });
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double join_f64(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = join_f64(lo[0], hi[0]) + join_f64(lo[1], hi[1]);
+  }
+  {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = join_f64(lo[0], hi[0]) + join_f64(lo[1], hi[1]);
+  }
   return v;
 }
 
