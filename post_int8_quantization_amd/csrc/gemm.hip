@@ -21,10 +21,13 @@
 //                     each wave owns a TM x TN sub-tile of MFMA fragments.
 //                     One barrier per K step.  The epilogue dequantizes from
 //                     registers with the tile's scales staged in LDS.
-//  * k_gemm_skinny -- decode (few tokens): HBM-bound weight streaming; each
-//                     block owns 16 output channels, its waves split K, the
-//                     weight chunks go straight from HBM to MFMA operand
-//                     registers and the int32 partials are summed in LDS.
+//  * k_gemm_dec    -- decode (M <= 64 tokens): HBM-bound weight streaming.
+//                     A block owns 16*NT output channels and its waves split
+//                     K into 128-byte slabs.  Each wave loads a slab with
+//                     row-contiguous 16-byte loads (8 rows x 128 B per
+//                     instruction: whole cache lines), transposes it into the
+//                     MFMA operand layout through a wave-private LDS area,
+//                     and the int32 partials of the waves are summed in LDS.
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
 
@@ -284,62 +287,149 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
   }  // tile loop
 }
 
-// Decode: M <= 16*MT tokens, 16 output channels per block, KS waves splitting K.
-template <int MT, int KS, int U>
-__global__ __launch_bounds__(KS * 64) void k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
-                                                        const float* __restrict__ ts, const float* __restrict__ cs,
-                                                        int M, int N, int K, float* __restrict__ Y,
-                                                        int32_t* __restrict__ ACC) {
-  __shared__ v4i part[KS][MT][64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int n = n0 + lr;
-  const bool nvalid = n < N;
-  const int8_t* brow = B + (int64_t)(nvalid ? n : 0) * K;
+// ---------------------------------------------------------------------------
+// Decode kernel pieces.
+//
+// Loading the MFMA operand layout directly (lane%16 = row, lane/16 = 16-byte
+// k-group) makes every load instruction touch 16 rows x 64 B, half of each
+// 128-byte line; loading 8 rows x 128 B instead and transposing through LDS
+// streams whole lines.  A slab is 16 rows x 128 bytes of K; chunk c of row r
+// sits at slab_slot(r, c), XOR-swizzled so that the eight lanes of one LDS
+// read cycle (eight rows, same chunk) hit different banks.  The LDS area of a
+// wave is private to it: LDS operations of one wave complete in order, so
+// only the compiler needs fencing (wave_sync_lds) between the transposing
+// stores and loads, and between a slab's loads and the next slab's stores.
 
-  v4i acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-  const int kstep = 64 * KS;
-  for (int k0 = wave * 64; k0 < K; k0 += kstep * U) {
-    uint4 b[U], a[U][MT];
+__device__ __forceinline__ int slab_slot(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+template <int MT, int NT>
+struct Slab {
+  uint4 b[NT][2];  // [16-row group][rows 0-7 | 8-15 of the group]
+  uint4 a[MT][2];
+};
+
+// Slab j (bytes 128j .. 128j+127 of K) of the block's weight rows and of the token rows, in the
+// load layout: lane -> row lrow (+8 for the second half), chunk lch.  Chunks past K or rows past M/N
+// load zeros.
+template <int MT, int NT>
+__device__ __forceinline__ void load_slab(Slab<MT, NT>& r, const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                          int M, int N, int K, int n0, int j, int lrow, int lch) {
+  const int gk = j * 128 + lch * 16;
+  const bool kv = gk < K;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int gk = k0 + u * kstep + lk * 16;
-      const bool kv = gk < K;
-      b[u] = (nvalid && kv) ? *reinterpret_cast<const uint4*>(brow + gk) : make_uint4(0, 0, 0, 0);
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int m = t * 16 + lr;
-        a[u][t] = (m < M && kv) ? *reinterpret_cast<const uint4*>(A + (int64_t)m * K + gk) : make_uint4(0, 0, 0, 0);
-      }
+    for (int u = 0; u < NT; ++u) {
+      const int n = n0 + u * 16 + lrow + 8 * h;
+      r.b[u][h] = (kv && n < N) ? load_once(B + (int64_t)n * K + gk) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma16(a[u][t], b[u], acc[t]);
-  }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) part[wave][t][lane] = acc[t];
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
     for (int t = 0; t < MT; ++t) {
-      v4i s = part[0][t][lane];
+      const int m = t * 16 + lrow + 8 * h;
+      r.a[t][h] = (kv && m < M) ? *reinterpret_cast<const uint4*>(A + (int64_t)m * K + gk) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Transpose one slab through the wave's LDS area and run its 2*MT*NT MFMAs (k-groups 0-3, then 4-7).
+template <int MT, int NT>
+__device__ __forceinline__ void mma_slab(const Slab<MT, NT>& r, uint4* ws, v4i (&acc)[MT][NT], int lrow, int lch,
+                                         int mrow, int mg) {
+  constexpr int CH = 128;  // 16-byte chunks per slab
 #pragma unroll
-      for (int w = 1; w < KS; ++w) s += part[w][t][lane];
-      if (nvalid) {
-        const float csn = cs[n];
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = t * 16 + lk * 4 + r;
-          if (m < M) {
-            Y[(int64_t)m * N + n] = (float)s[r] * (ts[m] * csn);
-            if (ACC) ACC[(int64_t)m * N + n] = s[r];
-          }
+    for (int u = 0; u < NT; ++u) ws[u * CH + slab_slot(lrow + 8 * h, lch)] = r.b[u][h];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ws[(NT + t) * CH + slab_slot(lrow + 8 * h, lch)] = r.a[t][h];
+  }
+  wave_sync_lds();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint4 tb[NT], ta[MT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) tb[u] = ws[u * CH + slab_slot(mrow, 4 * i + mg)];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ta[t] = ws[(NT + t) * CH + slab_slot(mrow, 4 * i + mg)];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int u = 0; u < NT; ++u) acc[t][u] = mfma16(ta[t], tb[u], acc[t][u]);
+  }
+  wave_sync_lds();
+}
+
+// M <= 16*MT tokens; a block of KS waves owns 16*NT output channels; wave w takes slabs w, w+KS, ...
+// PF: the next slab's loads are issued before the current slab's transpose and MFMAs.
+template <int MT, int NT, int KS, bool PF>
+__global__ __launch_bounds__(KS * 64) void k_gemm_dec(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                     const float* __restrict__ ts, const float* __restrict__ cs,
+                                                     int M, int N, int K, float* __restrict__ Y,
+                                                     int32_t* __restrict__ ACC) {
+  constexpr int WAVE_CH = (NT + MT) * 128;
+  static_assert(MT * NT * 64 <= WAVE_CH, "the partials fit in the slab area");
+  __shared__ uint4 sm[KS * WAVE_CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16 * NT;
+  uint4* ws = sm + wave * WAVE_CH;
+  const int lrow = lane >> 3, lch = lane & 7;  // load layout
+  const int mrow = lane & 15, mg = lane >> 4;  // MFMA layout
+
+  v4i acc[MT][NT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) acc[t][u] = v4i{0, 0, 0, 0};
+
+  const int nslab = (K + 127) / 128;
+  if constexpr (PF) {
+    Slab<MT, NT> r0, r1;
+    int j = wave;
+    if (j < nslab) load_slab(r0, A, B, M, N, K, n0, j, lrow, lch);
+    while (j < nslab) {
+      if (j + KS < nslab) load_slab(r1, A, B, M, N, K, n0, j + KS, lrow, lch);
+      mma_slab(r0, ws, acc, lrow, lch, mrow, mg);
+      j += KS;
+      if (j >= nslab) break;
+      if (j + KS < nslab) load_slab(r0, A, B, M, N, K, n0, j + KS, lrow, lch);
+      mma_slab(r1, ws, acc, lrow, lch, mrow, mg);
+      j += KS;
+    }
+  } else {
+    for (int j = wave; j < nslab; j += KS) {
+      Slab<MT, NT> r0;
+      load_slab(r0, A, B, M, N, K, n0, j, lrow, lch);
+      mma_slab(r0, ws, acc, lrow, lch, mrow, mg);
+    }
+  }
+
+  // sum of the waves' partials through the (now idle) slab area; wave w finishes tiles w, w+KS, ...
+  __syncthreads();
+  v4i* part = reinterpret_cast<v4i*>(sm);
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) part[((wave * MT + t) * NT + u) * 64 + lane] = acc[t][u];
+  __syncthreads();
+  for (int tu = wave; tu < MT * NT; tu += KS) {
+    const int t = tu / NT, u = tu % NT;
+    v4i s = part[(t * NT + u) * 64 + lane];
+    for (int w = 1; w < KS; ++w) s += part[((w * MT + t) * NT + u) * 64 + lane];
+    const int n = n0 + u * 16 + mrow;
+    if (n < N) {
+      const float csn = cs[n];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = t * 16 + mg * 4 + r;
+        if (m < M) {
+          Y[(int64_t)m * N + n] = (float)s[r] * (ts[m] * csn);
+          if (ACC) ACC[(int64_t)m * N + n] = s[r];
         }
       }
     }
@@ -355,11 +445,11 @@ hipError_t launch_tiled(const int8_t* xq, const int8_t* wq, const float* ts, con
   return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_skinny(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
-                         float* y, int32_t* acc, hipStream_t stream) {
-  const int blocks = (N + 15) / 16;
-  k_gemm_skinny<MT, 4, 4><<<(unsigned)blocks, 4 * 64, 0, stream>>>(xq, wq, ts, cs, M, N, K, y, acc);
+template <int MT, int NT, int KS, bool PF>
+hipError_t launch_dec(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
+                      float* y, int32_t* acc, hipStream_t stream) {
+  const int blocks = (N + 16 * NT - 1) / (16 * NT);
+  k_gemm_dec<MT, NT, KS, PF><<<(unsigned)blocks, KS * 64, 0, stream>>>(xq, wq, ts, cs, M, N, K, y, acc);
   return hipGetLastError();
 }
 
@@ -368,9 +458,13 @@ hipError_t launch_skinny(const int8_t* xq, const int8_t* wq, const float* ts, co
 hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
                                int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (M <= 16) return launch_skinny<1>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  if (M <= 32) return launch_skinny<2>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  if (M <= 64) return launch_skinny<4>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  if (M <= 16) return launch_dec<1, 1, 8, false>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  if (M <= 32) return launch_dec<2, 1, 8, false>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  if (M <= 64) {
+    // 64 channels per block re-read the token rows 4x less often, once that still fills the CUs
+    if ((N + 63) / 64 >= 256) return launch_dec<4, 4, 4, false>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+    return launch_dec<4, 2, 8, true>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  }
   // the largest tile that still gives about one tile per CU (256 CUs)
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 200)

@@ -146,7 +146,8 @@ def test_ssz_outputs_optional(pq):
 # ------------------------------------------------------------------ GEMM + dequant
 
 @pytest.mark.parametrize("M,N,K", [
-    (16, 128, 64), (1, 1, 16), (7, 33, 48), (16, 1000, 8192), (33, 77, 160), (64, 300, 4096), (65, 130, 1040),
+    (16, 128, 64), (1, 1, 16), (7, 33, 48), (16, 1000, 8192), (5, 1000, 8208), (20, 700, 272), (31, 4000, 4112),
+    (33, 77, 160), (64, 300, 4096), (64, 16448, 1040), (65, 130, 1040),
     (300, 520, 1040), (257, 259, 4096), (512, 768, 2048), (256, 256, 16), (1024, 1024, 4096)])
 def test_gemm_dequant(pq, M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
@@ -173,12 +174,12 @@ def test_gemm_max_k_extremes(pq):
     assert ref.max() == 127 * 127 * K
     ts = np.ones(3, np.float32)
     cs = np.ones(20, np.float32)
-    announce("w8a8_gemm_dequant K=133136 extremes (skinny)")
+    announce("w8a8_gemm_dequant K=133136 extremes (decode kernel)")
     y, acc = pq.w8a8_gemm_dequant(dev(a), dev(b), dev(ts), dev(cs), want_acc=True)
     np.testing.assert_array_equal(host(acc), ref)
     a2 = np.tile(a, (40, 1))[:100]
     ref2 = oracle.gemm_i8(a2, b)
-    announce("w8a8_gemm_dequant K=133136 extremes (tiled)")
+    announce("w8a8_gemm_dequant K=133136 extremes (prefill kernel)")
     y2, acc2 = pq.w8a8_gemm_dequant(dev(a2), dev(b), dev(np.ones(100, np.float32)), dev(cs), want_acc=True)
     np.testing.assert_array_equal(host(acc2), ref2)
 
