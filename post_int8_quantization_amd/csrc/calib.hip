@@ -4,9 +4,9 @@
 // range calibration).  HBM-bound: every element is read once with 16-byte
 // loads ([INT8] 3.1, streaming hint).  A block of 4 waves owns a strip of 64
 // 16-byte vector columns (1 KB of every row) and a run of rows; each wave
-// streams its own contiguous rows with 16 loads in flight per lane, keeping
-// running maxima in registers; about 4 blocks per CU keep ~256 KB in flight
-// per CU.  The waves merge through LDS and the block publishes one atomic max
+// streams its own contiguous rows with 8 to 16 loads in flight per lane,
+// keeping running maxima in registers; about 4 blocks per CU keep up to
+// ~256 KB in flight per CU.  The waves merge through LDS and the block publishes one atomic max
 // per column.  Maxima of non-negative floats order like their bit
 // patterns, so an unsigned atomic max gives the exact result in any order.
 #include "ptq_dev.hpp"
@@ -21,7 +21,7 @@ namespace {
 constexpr int kWaves = 4;                // waves per block
 constexpr int kThreads = kWaves * kWave;  // 256
 constexpr int kVecs = kWave;              // 16-byte vector columns per block strip
-constexpr int kInFlight = 16;             // loads in flight per lane
+constexpr int kBatch = 8;                 // row loads per batch; two batches in flight per lane
 
 template <int DT>
 struct Vec {
@@ -43,7 +43,11 @@ __device__ __forceinline__ void fold_max(float (&m)[Vec<DT>::kElems], const uint
   }
 }
 
-// grid: x = column strips, y = row runs of rows_per_block rows (split evenly over the 16 waves)
+// grid: x = column strips, y = row runs of rows_per_block rows (split evenly over the waves).
+// Each wave keeps two batches of kBatch row loads in flight: the next batch is issued before the
+// current one is folded.  Rows are read through per-row range-checked descriptors, so rows past
+// the wave's run and lanes past the row's end read zeros (neutral for a max of magnitudes) with no
+// branch around any load.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_absmax_cols(const uint4* __restrict__ x, int64_t rows,
                                                          int64_t vecs_per_row, int64_t rows_per_block,
@@ -51,26 +55,40 @@ __global__ __launch_bounds__(kThreads) void k_absmax_cols(const uint4* __restric
   constexpr int E = Vec<DT>::kElems;
   __shared__ float red[kWaves][kVecs * E];
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: row descriptors in SGPRs
   const int64_t v = (int64_t)blockIdx.x * kVecs + lane;
   const int64_t per_wave = (rows_per_block + kWaves - 1) / kWaves;
   const int64_t b0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t b1 = b0 + rows_per_block < rows ? b0 + rows_per_block : rows;
   const int64_t r0 = b0 + wave * per_wave;
   const int64_t r1 = r0 + per_wave < b1 ? r0 + per_wave : b1;
+  const uint32_t row_bytes = (uint32_t)(vecs_per_row * 16);
+  const uint32_t off = (uint32_t)(v * 16);
 
   float m[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) m[e] = 0.0f;
-  if (v < vecs_per_row) {
-    const uint4* p = x + v;
-    for (int64_t r = r0; r < r1; r += kInFlight) {
-      uint4 d[kInFlight];
+  auto load_batch = [&](uint4 (&d)[kBatch], int64_t r) {
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) d[u] = r + u < r1 ? load_once(p + (r + u) * vecs_per_row) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < kInFlight; ++u) fold_max<DT>(m, d[u]);
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t rr = r + u;
+      const bool live = rr < r1;
+      d[u] = buf_load16_once(buf_rsrc(x + (live ? rr : 0) * vecs_per_row, live ? row_bytes : 0u), off);
     }
+  };
+  uint4 da[kBatch], db[kBatch];
+  load_batch(da, r0);
+  // the scheduling barriers keep each batch's loads issued before the previous batch is folded
+  for (int64_t r = r0; r < r1; r += 2 * kBatch) {
+    load_batch(db, r + kBatch);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) fold_max<DT>(m, da[u]);
+    load_batch(da, r + 2 * kBatch);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) fold_max<DT>(m, db[u]);
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) red[wave][lane * E + e] = m[e];

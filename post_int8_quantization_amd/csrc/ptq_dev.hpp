@@ -23,6 +23,37 @@ __device__ __forceinline__ uint4 load_once(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer accesses with hardware range checking (gfx9 raw buffer, stride 0):
+// a load at a byte offset past num_records returns zeros and a store there is
+// dropped, so tails and absent rows need no branches -- every lane issues the
+// same loads and stores, which also lets the compiler count them exactly when
+// it places its waits.  Descriptor word 3 is the gfx9 default.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16-byte load of read-once data (nontemporal)
+__device__ __forceinline__ uint4 buf_load16_once(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  const u32x2_t d = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+
 // bf16 pair in one dword -> two fp32 (exact widening)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }

@@ -2,12 +2,22 @@
 //
 // One block of TPR threads owns one token row at a time and walks rows with a
 // grid stride, loading the next row while it quantizes the current one.  Each
-// thread holds CPT chunks of 16 consecutive elements in registers, so a row is
-// read from HBM once (16-byte loads, [INT8] 3.1) and written once as int8 (one
-// 16-byte store per chunk).  The smoothing fold x_hat = fl32(x * fl32(1/s_j))
-// ([SQ] X diag(s)^-1) uses per-column reciprocals that each thread computes
-// once (IEEE division) for its own columns and keeps in registers across the
-// rows it visits; the grid size trades that reuse against rows in flight.
+// thread holds CPT groups of 16 elements of the row in registers, so a row is
+// read from HBM once and written once as int8.  A group is split into pieces
+// of E elements (one 16-byte load: E = 8 for bf16, 4 for fp32); piece p of
+// group m of thread tid starts at column
+//     m*TPR*16 + p*TPR*E + tid*E,
+// so the 64 lanes of a wave read 1 KB of consecutive bytes per load
+// instruction (whole cache lines) and write E*64 consecutive code bytes per
+// store ([INT8] 3.1: 16-byte vectorised accesses).  The smoothing fold
+// x_hat = fl32(x * fl32(1/s_j)) ([SQ] X diag(s)^-1) uses per-column
+// reciprocals that each thread computes once (IEEE division) for its own
+// columns and keeps in registers across the rows it visits; the grid size
+// trades that reuse against rows in flight.
+//
+// All row accesses are range-checked buffer loads and stores on a per-row
+// descriptor (zero bytes for a row past T), so no lane or row takes a branch
+// around a memory access and the loads of the rows in flight stay in flight.
 //
 // Per row: a = max|x_hat| (wave butterfly + LDS across waves),
 // delta = a > 0 ? fl32(a/127) : 1, inv = fl32(1/delta),
@@ -20,26 +30,33 @@ namespace ptq {
 namespace {
 
 template <int DT>
-struct Raw {
-  static constexpr int kVecs = DT == PTQ_BF16 ? 2 : 4;  // 16-byte vectors per 16-element chunk
+struct Piece {
+  static constexpr int E = DT == PTQ_BF16 ? 8 : 4;  // elements per 16-byte load
+  static constexpr int P = 16 / E;                  // pieces per 16-element group
 };
 
+template <int DT, int TPR>
+__device__ __forceinline__ int64_t piece_col(int m, int p, int tid) {
+  return (int64_t)m * TPR * 16 + (int64_t)p * TPR * Piece<DT>::E + (int64_t)tid * Piece<DT>::E;
+}
+
+// Row t of x (zero-length past T: the loads then return zeros).
 template <int DT, int TPR, int CPT>
-__device__ __forceinline__ void load_raw(const void* x, int64_t t, int64_t K, int tid, int64_t nchunk,
-                                         uint4 (&raw)[CPT][Raw<DT>::kVecs]) {
-  constexpr int NV = Raw<DT>::kVecs;
-  const uint4* row = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) +
-                                                    t * K * (DT == PTQ_BF16 ? 2 : 4));
+__device__ __forceinline__ void load_raw(const void* x, int64_t t, int64_t T, int64_t K, int tid,
+                                         uint4 (&raw)[CPT][Piece<DT>::P]) {
+  constexpr int P = Piece<DT>::P;
+  constexpr int BYTES = DT == PTQ_BF16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs =
+      buf_rsrc(reinterpret_cast<const char*>(x) + (t < T ? t : 0) * K * BYTES, t < T ? (uint32_t)(K * BYTES) : 0u);
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    const int64_t c = tid + (int64_t)TPR * m;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) raw[m][q] = c < nchunk ? load_once(row + c * NV + q) : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < P; ++p) raw[m][p] = buf_load16_once(rs, (uint32_t)(piece_col<DT, TPR>(m, p, tid) * BYTES));
   }
 }
 
 template <int DT>
-__device__ __forceinline__ void unpack16(const uint4 (&raw)[Raw<DT>::kVecs], float (&v)[16]) {
+__device__ __forceinline__ void unpack16(const uint4 (&raw)[Piece<DT>::P], float (&v)[16]) {
   if constexpr (DT == PTQ_BF16) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -63,10 +80,11 @@ __device__ __forceinline__ void unpack16(const uint4 (&raw)[Raw<DT>::kVecs], flo
 
 // One row: fold, absmax (wave butterfly + LDS across waves), codes, store.
 template <int DT, bool HAS_S, int TPR, int CPT>
-__device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Raw<DT>::kVecs], const float (&r)[CPT][16],
-                                          int64_t t, int64_t K, int tid, int64_t nchunk, int8_t* __restrict__ xq,
+__device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P], const float (&r)[CPT][16], int64_t t,
+                                          int64_t T, int64_t K, int tid, int8_t* __restrict__ xq,
                                           float* __restrict__ tok_scale, float (*red)[TPR / kWave], int parity) {
   constexpr int NW = TPR / kWave;
+  constexpr int E = Piece<DT>::E, P = Piece<DT>::P;
   float v[CPT][16];
   float amax = 0.0f;
 #pragma unroll
@@ -88,78 +106,112 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Raw<DT>::kVecs
   }
   const float delta = amax > 0.0f ? amax / 127.0f : 1.0f;
   const float inv = 1.0f / delta;
+  const bool live = t < T;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + (live ? t : 0) * K, live ? (uint32_t)K : 0u);
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    const int64_t c = tid + (int64_t)TPR * m;
-    if (c < nchunk) {
-      float q[16];
+    float q[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = code_f(v[m][e], inv, 127.0f);
-      uint4 o;
-      o.x = pack4_i8(q[0], q[1], q[2], q[3]);
-      o.y = pack4_i8(q[4], q[5], q[6], q[7]);
-      o.z = pack4_i8(q[8], q[9], q[10], q[11]);
-      o.w = pack4_i8(q[12], q[13], q[14], q[15]);
-      *reinterpret_cast<uint4*>(xq + t * K + c * 16) = o;
+    for (int e = 0; e < 16; ++e) q[e] = code_f(v[m][e], inv, 127.0f);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t c = (uint32_t)piece_col<DT, TPR>(m, p, tid);
+      if constexpr (E == 8) {
+        uint2 o;
+        o.x = pack4_i8(q[p * 8 + 0], q[p * 8 + 1], q[p * 8 + 2], q[p * 8 + 3]);
+        o.y = pack4_i8(q[p * 8 + 4], q[p * 8 + 5], q[p * 8 + 6], q[p * 8 + 7]);
+        buf_store8(rq, c, o);
+      } else {
+        buf_store4(rq, c, pack4_i8(q[p * 4 + 0], q[p * 4 + 1], q[p * 4 + 2], q[p * 4 + 3]));
+      }
     }
   }
-  if (tid == 0) tok_scale[t] = delta;
+  // lane 0 writes delta: the other lanes' offsets fall past the 4-byte range
+  const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tok_scale + (live ? t : 0), live ? 4u : 0u);
+  buf_store4(rt, tid == 0 ? 0u : 4u, __float_as_uint(delta));
 }
 
-// Grid-stride over rows; the next row's raw data is loaded while the current one is processed.
-template <int DT, bool HAS_S, int TPR, int CPT>
+// Grid-stride over rows with D rows in flight: slot d of the register ring is
+// refilled with the row D strides ahead as soon as its row is quantized.  A
+// block walks whole rounds of D rows; the rows of a round past T are no-ops
+// (zero-length descriptors).
+template <int DT, bool HAS_S, int TPR, int CPT, int D>
 __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, int64_t T, int64_t K,
                                                    const float* __restrict__ s, int8_t* __restrict__ xq,
                                                    float* __restrict__ tok_scale) {
-  constexpr int NV = Raw<DT>::kVecs;
+  constexpr int E = Piece<DT>::E, P = Piece<DT>::P;
   __shared__ float red[2][TPR / kWave];
   const int tid = threadIdx.x;
-  const int64_t nchunk = K / 16;
+  const int64_t G = gridDim.x;
 
-  int64_t t = blockIdx.x;
-  if (t >= T) return;
-  uint4 ra[CPT][NV], rb[CPT][NV];
-  load_raw<DT, TPR, CPT>(x, t, K, tid, nchunk, ra);  // in flight while the reciprocals are computed
+  // the smoothing factors of this thread's columns are loaded first, so that waiting for them (loads
+  // complete in issue order) leaves the first D rows in flight while the reciprocals are computed
+  uint4 sv[HAS_S ? CPT : 1][4];
+  if constexpr (HAS_S) {
+    const __amdgpu_buffer_rsrc_t rsc = buf_rsrc(s, (uint32_t)(K * 4));
+#pragma unroll
+    for (int m = 0; m < CPT; ++m)
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h)
+          sv[m][p * (E / 4) + h] = buf_load16(rsc, (uint32_t)((piece_col<DT, TPR>(m, p, tid) + 4 * h) * 4));
+  }
+  uint4 ring[D][CPT][P];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_raw<DT, TPR, CPT>(x, blockIdx.x + d * G, T, K, tid, ring[d]);
 
   float r[CPT][16];
+  if constexpr (HAS_S) {
 #pragma unroll
-  for (int m = 0; m < CPT; ++m) {
-    const int64_t c = tid + (int64_t)TPR * m;
+    for (int m = 0; m < CPT; ++m) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) r[m][e] = (HAS_S && c < nchunk) ? 1.0f / s[c * 16 + e] : 1.0f;
+      for (int p = 0; p < P; ++p) {
+        const bool in = piece_col<DT, TPR>(m, p, tid) < K;
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+          const uint4 w = sv[m][p * (E / 4) + h];
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[m][p * E + 4 * h + i] = in ? 1.0f / __uint_as_float(u[i]) : 1.0f;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r[m][e] = 1.0f;
   }
   int parity = 0;
-  for (;;) {
-    int64_t tn = t + gridDim.x;
-    if (tn < T) load_raw<DT, TPR, CPT>(x, tn, K, tid, nchunk, rb);
-    quant_row<DT, HAS_S, TPR, CPT>(ra, r, t, K, tid, nchunk, xq, tok_scale, red, parity);
-    parity ^= 1;
-    if (tn >= T) break;
-    t = tn;
-    tn = t + gridDim.x;
-    if (tn < T) load_raw<DT, TPR, CPT>(x, tn, K, tid, nchunk, ra);
-    quant_row<DT, HAS_S, TPR, CPT>(rb, r, t, K, tid, nchunk, xq, tok_scale, red, parity);
-    parity ^= 1;
-    if (tn >= T) break;
-    t = tn;
+  for (int64_t base = blockIdx.x; base < T; base += D * G) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t t = base + d * G;
+      quant_row<DT, HAS_S, TPR, CPT>(ring[d], r, t, T, K, tid, xq, tok_scale, red, parity);
+      parity ^= 1;
+      load_raw<DT, TPR, CPT>(x, t + D * G, T, K, tid, ring[d]);
+    }
   }
 }
 
 template <int DT, bool HAS_S, int TPR, int CPT>
 void launch_one(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, int64_t blocks,
                 hipStream_t stream) {
-  k_quant_tok<DT, HAS_S, TPR, CPT><<<(unsigned)blocks, TPR, 0, stream>>>(x, T, K, s, xq, ts);
+  constexpr int D = CPT >= 4 ? 1 : 4 / CPT;  // rows in flight per block: about 4 groups of 16 elements per thread
+  k_quant_tok<DT, HAS_S, TPR, CPT, D><<<(unsigned)blocks, TPR, 0, stream>>>(x, T, K, s, xq, ts);
 }
 
 template <int DT, bool HAS_S>
 hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, int64_t rows_per_block,
                     hipStream_t stream) {
-  const int64_t nchunk = K / 16;
-  int tpr = nchunk >= 256 ? 256 : 64;
-  int64_t cpt = (nchunk + tpr - 1) / tpr;
-  while (cpt > 4 && tpr < 1024) {
+  const int64_t ngroup = K / 16;
+  // the narrowest block with at most 2 groups of 16 elements per thread (up to 8 at 1024 threads)
+  int tpr = 64;
+  int64_t cpt = (ngroup + tpr - 1) / tpr;
+  while (cpt > 2 && tpr < 1024) {
     tpr *= 2;
-    cpt = (nchunk + tpr - 1) / tpr;
+    cpt = (ngroup + tpr - 1) / tpr;
   }
   // rows per block: the per-column reciprocals are computed once per block and reused for its rows
   int64_t blocks = (T + rows_per_block - 1) / rows_per_block;
@@ -169,9 +221,8 @@ hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t*
     launch_one<DT, HAS_S, TPR_, CPT_>(x, T, K, s, xq, ts, blocks, stream);          \
     return hipGetLastError();                                                       \
   }
-  PTQ_Q(64, 1) PTQ_Q(64, 2) PTQ_Q(64, 4)
-  PTQ_Q(256, 1) PTQ_Q(256, 2) PTQ_Q(256, 4)
-  PTQ_Q(512, 4) PTQ_Q(1024, 4) PTQ_Q(1024, 8)
+  PTQ_Q(64, 1) PTQ_Q(64, 2) PTQ_Q(128, 2) PTQ_Q(256, 2) PTQ_Q(512, 2)
+  PTQ_Q(1024, 2) PTQ_Q(1024, 4) PTQ_Q(1024, 8)
 #undef PTQ_Q
   return hipErrorInvalidValue;
 }
@@ -183,7 +234,7 @@ hipError_t launch_quant_per_token_rpb(const void* x, int dtype, int64_t T, int64
                                       float* tok_scale, int64_t rows_per_block, hipStream_t stream) {
   if (rows_per_block <= 0) {
     // enough blocks to keep rows in flight on every CU, enough rows per block to reuse the reciprocals
-    rows_per_block = T / (K >= 4096 ? 512 : 1024);
+    rows_per_block = T / (K >= 8192 ? 512 : 1024);
     rows_per_block = rows_per_block < 1 ? 1 : (rows_per_block > 16 ? 16 : rows_per_block);
   }
   if (dtype == PTQ_BF16)
