@@ -18,7 +18,14 @@ Inputs are resident in HBM before the timed region.  Kernels run on torch's
 current stream; HIP events on that stream bracket every stage, giving
 per-kernel durations.  Prints one JSON line.
 
+--workload decode measures the decode configuration instead (16 tokens,
+X [16,8192] against W [28672,8192]): the weight is calibrated and quantized
+once, untimed; a step is the per-token quantization of the token batch and
+the int8 GEMM with dequantization.  The int8 weight is rotated over three
+copies so that it is read from HBM, not from the 256 MB last-level cache.
+
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--alpha 0.5] [--no-cpu-baseline]
+                  [--workload opt67b|decode]
 """
 from __future__ import annotations
 
@@ -50,6 +57,7 @@ def parse():
     p.add_argument("--calib-batches", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle GEMM time of the CPU baseline")
+    p.add_argument("--workload", choices=("opt67b", "decode"), default="opt67b")
     p.add_argument("--copy-ref", action="store_true",
                    help="only run a plain 1 GiB device copy three times (reference for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -91,22 +99,28 @@ class Timer:
         return out
 
 
-def load_counters(kernel_tag):
-    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE), from the committed
-    summary under profiles/, if it was taken on the current kernel source (hash match); else None."""
+KERNEL_SOURCES = {"k_ssz": "ssz.hip", "k_gemm_pipe": "gemm.hip", "k_gemm_dec": "gemm.hip",
+                  "k_absmax_cols": "calib.hip", "k_quant_tok": "quant.hip"}
+
+
+def kernel_source_sha(kernel_tag):
+    """Hash of the source a kernel is built from: its .hip file and the shared device header."""
     src = os.path.join(ROOT, "post_int8_quantization_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(src, "*.hip")) + glob.glob(os.path.join(src, "*.hpp"))):
-        h.update(open(f, "rb").read())
-    digest = h.hexdigest()[:16]
-    for f in glob.glob(os.path.join(ROOT, "profiles", "*counters*.md")):
-        txt = open(f).read()
-        m = re.search(r"traffic-record:\s*(\{.*\})", txt)
-        if not m:
-            continue
-        rec = json.loads(m.group(1))
-        if rec.get("kernel") == kernel_tag and rec.get("source_sha") == digest:
-            return rec
+    for f in (KERNEL_SOURCES[kernel_tag], "ptq_dev.hpp"):
+        h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_counters(kernel_tag):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE), from the committed
+    summaries under profiles/, if they were taken on the kernel's current source (hash match); else None."""
+    digest = kernel_source_sha(kernel_tag)
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*counters*.md"))):
+        for m in re.finditer(r"traffic-record:\s*(\{.*\})", open(f).read()):
+            rec = json.loads(m.group(1))
+            if rec.get("kernel") == kernel_tag and rec.get("source_sha") == digest:
+                return rec
     return None
 
 
@@ -121,6 +135,10 @@ def main():
               "shards by token rows or weight rows with no collective on the hot path, and this build measures "
               "the one-GPU share.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "decode":
+        decode(args)
+        return
 
     import numpy as np
     import torch
@@ -228,7 +246,7 @@ def main():
     dom = max(("calib_x", "ssz", "quant", "gemm"), key=lambda n: tot[n][0])
     if dom == "gemm":
         launches = len(layers)
-        roof = {"kernel": "k_gemm_tile", "bound": "mfma", "achieved": gemm_ops / launches / (gemm_s / launches) / 1e12,
+        roof = {"kernel": "k_gemm_pipe", "bound": "mfma", "achieved": gemm_ops / launches / (gemm_s / launches) / 1e12,
                 "peak": PEAK_I8 / 1e12, "unit": "TOP/s", "per_launch_ops": gemm_ops / launches}
     elif dom == "ssz":
         roof = {"kernel": "k_ssz", "bound": "alu",
@@ -259,6 +277,112 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args, synth)
+    print(json.dumps(out), flush=True)
+
+
+def decode(args):
+    import numpy as np
+    import torch
+
+    import post_int8_quantization_amd as pq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    (c,) = synth.cases("decode")
+    B = args.calib_batches
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    stream = torch.cuda.current_stream()
+    w = up(c.w())
+    ax = torch.empty(c.K, dtype=torch.float32, device=dev)
+    for b in range(B):
+        pq.sq_absmax_calib(up(c.x_batch(b)), ax, accumulate=b > 0, stream=stream)
+    aw = torch.empty(c.K, dtype=torch.float32, device=dev)
+    pq.sq_absmax_calib(w, aw, stream=stream)
+    s = pq.sq_smooth_factors(ax, aw, args.alpha, stream=stream)
+    S, wq0, _, _ = pq.ssz_weight_qparams(w, s, bits=8, stream=stream)
+    del w
+    wqs = [wq0] + [wq0.clone() for _ in range(2)]
+    x = up(c.x_batch(B))
+    xq = torch.empty((c.T, c.K), dtype=torch.int8, device=dev)
+    d = torch.empty(c.T, dtype=torch.float32, device=dev)
+    y = torch.empty((c.T, c.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(tm, i):
+        tm.stage("quant", lambda: pq.quant_per_token_i8(x, s, xq=xq, tok_scale=d, stream=stream))
+        tm.stage("gemm", lambda: pq.w8a8_gemm_dequant(xq, wqs[i % len(wqs)], d, S, y=y, stream=stream))
+
+    for i in range(args.warmup):
+        step(Timer(torch), i)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(tm, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot = tm.totals()
+    K = args.steps
+
+    def sec(name):
+        return tot[name][0] / 1e3 / K
+
+    gemm_ops = 2 * c.T * c.N * c.K
+    gemm_bytes = c.T * c.K + c.N * c.K + 4 * c.T + 4 * c.N + 4 * c.T * c.N
+    quant_bytes = c.T * c.K * 2 + c.T * c.K + c.T * 4 + c.K * 4
+    gemm_s = sec("gemm")
+    stages = {
+        "quant": {"ms": sec("quant") * 1e3, "GB/s": quant_bytes / sec("quant") / 1e9,
+                  "frac_hbm": quant_bytes / sec("quant") / PEAK_HBM},
+        "gemm": {"ms": gemm_s * 1e3, "TOPS": gemm_ops / gemm_s / 1e12, "GB/s": gemm_bytes / gemm_s / 1e9,
+                 "frac_hbm": gemm_bytes / gemm_s / PEAK_HBM},
+    }
+    roof = {"kernel": "k_gemm_dec", "bound": "hbm", "achieved": gemm_bytes / gemm_s / 1e9, "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s", "per_launch_bytes": gemm_bytes}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    rec = load_counters("k_gemm_dec")
+    roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
+    roof["avg_launch_us"] = tot["gemm"][0] * 1e3 / tot["gemm"][1]
+    out = {
+        "metric": METRIC, "value": gemm_ops / gemm_s / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"decode: X[{c.T},{c.K}] bf16 (0.5 percent outlier channels x60) against "
+                               f"W[{c.N},{c.K}] int8 quantized once untimed; step = per-token quantization + "
+                               "int8 GEMM with dequantization; weight rotated over 3 copies",
+                   "tokens": c.T, "hidden": c.K, "out": c.N, "alpha": args.alpha, "bits": 8,
+                   "parallelism": "single GPU"},
+        "gpu_ms_per_step": sum(v[0] for v in tot.values()) / K, "stages": stages, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        wh = synth.widen(c.w())
+        p0 = time.perf_counter()
+        axh = None
+        for b in range(B):
+            axh = oracle.absmax_cols(synth.widen(c.x_batch(b)), axh)
+        sh = oracle.smooth_factors(axh, oracle.absmax_cols(wh), args.alpha)
+        qh = oracle.ssz(wh, sh, 8)
+        p1 = time.perf_counter()
+        xe = synth.widen(c.x_batch(B))
+        t0 = time.perf_counter()
+        xqh, dh = oracle.quant_per_token(xe, sh)
+        t1 = time.perf_counter()
+        acc = oracle.gemm_i8(xqh, qh["q"])
+        oracle.dequant(acc, dh, qh["S"])
+        t2 = time.perf_counter()
+        out["cpu_baseline"] = {"value": gemm_ops / (t2 - t1) / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": "one whole step (16 tokens x all 28672 weight rows): "
+                               "per-token quantization, then GEMM + dequantization (the value times the latter); "
+                               "the weight's calibration and SSZ run first, untimed like on the GPU",
+                               "quant_seconds": t1 - t0, "gemm_dequant_seconds": t2 - t1,
+                               "untimed_prep_seconds": p1 - p0}
     print(json.dumps(out), flush=True)
 
 
