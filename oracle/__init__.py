@@ -61,6 +61,10 @@ def _load():
             "o_mse_row": [vp, vp, i64, f32],
             "o_ssz": [vp, vp, i64, i64, ci, ci, f64, f32, vp, vp, vp, vp, vp],
             "o_minmax_per_tensor": [vp, i64, i64, ci, f32, vp, vp],
+            "o_quant_row_asym": [vp, i64, f32, ci, vp],
+            "o_mse_row_asym": [vp, vp, i64, f32, ci],
+            "o_lsq_affine": [vp, vp, i64, vp, vp],
+            "o_ssz_asym": [vp, vp, i64, i64, ci, f64, f32, vp, vp, vp, vp, vp, vp],
             "o_pack_int4": [vp, i64, i64, vp],
             "o_quant_per_token": [vp, vp, i64, i64, vp, vp],
             "o_gemm_i8": [vp, vp, i64, i64, i64, vp],
@@ -74,6 +78,7 @@ def _load():
         lib.o_num_threads.restype = ci
         lib.o_lsq_scale.restype = f64
         lib.o_mse_row.restype = f64
+        lib.o_mse_row_asym.restype = f64
         _lib = lib
     return _lib
 
@@ -162,6 +167,50 @@ def ssz(w, s=None, bits=8, max_iter=20, thr=1e-10, min_scale=1e-5, hist=False):
     _check(_load().o_ssz(w.ctypes.data, _p(s), N, K, int(bits), int(max_iter), float(thr), float(min_scale),
                          S.ctypes.data, q.ctypes.data, it.ctypes.data, mse.ctypes.data, _p(h)), "ssz")
     out = dict(S=S, q=q, iters=it, mse=mse)
+    if hist:
+        out["hist"] = h
+    return out
+
+
+def quant_row_asym(r, S, Z):
+    """Asymmetric int8 codes clamp(rne(r / S) + Z, -128, 127) of one row."""
+    r = _f32(r).ravel()
+    q = np.empty(r.size, dtype=np.int8)
+    _check(_load().o_quant_row_asym(r.ctypes.data, r.size, float(S), int(Z), q.ctypes.data), "quant_row_asym")
+    return q
+
+
+def mse_row_asym(wh, q, S, Z):
+    wh = _f32(wh).ravel()
+    q = np.ascontiguousarray(q, dtype=np.int8).ravel()
+    return float(_load().o_mse_row_asym(wh.ctypes.data, q.ctypes.data, wh.size, float(S), int(Z)))
+
+
+def lsq_affine(wh, q):
+    """(a, b) of the least-squares line wh ~ a q + b, or None when all codes are equal."""
+    wh = _f32(wh).ravel()
+    q = np.ascontiguousarray(q, dtype=np.int8).ravel()
+    a = ctypes.c_double()
+    b = ctypes.c_double()
+    ok = _load().o_lsq_affine(wh.ctypes.data, q.ctypes.data, wh.size, ctypes.addressof(a), ctypes.addressof(b))
+    return (a.value, b.value) if ok else None
+
+
+def ssz_asym(w, s=None, max_iter=20, thr=1e-10, min_scale=1e-5, hist=False):
+    """MinMax + asymmetric int8 SSZ per row.  Returns dict(S, Z, q, iters, mse[, hist])."""
+    w = _f32(w)
+    N, K = w.shape
+    s = None if s is None else _f32(s)
+    S = np.empty(N, dtype=np.float32)
+    Z = np.empty(N, dtype=np.int32)
+    q = np.empty((N, K), dtype=np.int8)
+    it = np.empty(N, dtype=np.int32)
+    mse = np.empty(N, dtype=np.float64)
+    h = np.full((N, max_iter + 1), np.nan, dtype=np.float64) if hist else None
+    _check(_load().o_ssz_asym(w.ctypes.data, _p(s), N, K, int(max_iter), float(thr), float(min_scale),
+                              S.ctypes.data, Z.ctypes.data, q.ctypes.data, it.ctypes.data, mse.ctypes.data, _p(h)),
+           "ssz_asym")
+    out = dict(S=S, Z=Z, q=q, iters=it, mse=mse)
     if hist:
         out["hist"] = h
     return out

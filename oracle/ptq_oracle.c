@@ -286,6 +286,171 @@ int o_ssz(const float* w, const float* s, int64_t N, int64_t K, int bits, int ma
   return bad ? O_EARG : O_OK;
 }
 
+/* ---------------------------------------------------------------------------
+ * Asymmetric linear quantization, int8.  [INT8] 2.1: Q = round(R/S) + Z with
+ * saturation; the SSZ document's asymmetric mode lets the offset move
+ * ([SSZ] iteration stage; "symmetric: false" in the option table) and
+ * supports it for int8 only ([SSZ] limits: no int4 asymmetric).
+ *   code = clamp(rne(fl32(R * fl32(1/S))) + Z, -128, 127),  Z an integer,
+ *   dequantized value S * (code - Z).
+ * Readings: the full two's-complement range [-128, 127] (256 levels); Z is
+ * an integer in that range.
+ * ------------------------------------------------------------------------- */
+#define O_QMIN_ASYM (-128)
+#define O_QMAX_ASYM 127
+
+static int code_asym(float r, float inv_s, int z) {
+  float t = r * inv_s;
+  int q = (int)nearbyintf(t);
+  /* saturate before adding Z so that a huge |t| cannot overflow the int */
+  if (q > 1000) q = 1000;
+  if (q < -1000) q = -1000;
+  q += z;
+  if (q > O_QMAX_ASYM) q = O_QMAX_ASYM;
+  if (q < O_QMIN_ASYM) q = O_QMIN_ASYM;
+  return q;
+}
+
+int o_quant_row_asym(const float* r, int64_t K, float S, int Z, int8_t* q) {
+  if (!r || !q || K <= 0 || !(S > 0.0f) || Z < O_QMIN_ASYM || Z > O_QMAX_ASYM) return O_EARG;
+  float inv = 1.0f / S;
+  for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_asym(r[k], inv, Z);
+  return O_OK;
+}
+
+/* mean of (w_hat - S*(q - Z))^2, fp64, k ascending */
+double o_mse_row_asym(const float* wh, const int8_t* q, int64_t K, float S, int Z) {
+  double acc = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double d = (double)wh[k] - (double)S * (double)((int)q[k] - Z);
+    acc += d * d;
+  }
+  return acc / (double)K;
+}
+
+/* Least squares over scale and offset for fixed codes: the line w ~ a*q + b
+ * that minimises sum (w_hat - a q - b)^2, from its 2x2 normal equations
+ *   [sum q^2  sum q] [a]   [sum w q]
+ *   [sum q    K    ] [b] = [sum w  ]
+ * solved as a = (K sum wq - sum w sum q) / det, b = (sum w - a sum q) / K,
+ * det = K sum q^2 - (sum q)^2 (exact integers; fp64 for the w sums).
+ * ([SSZ] asymmetric mode fits scale and offset together by least squares.)
+ * Returns 1 and a, b when det > 0; 0 when all codes are equal (nothing to fit). */
+int o_lsq_affine(const float* wh, const int8_t* q, int64_t K, double* a, double* b) {
+  double sw = 0.0, swq = 0.0;
+  int64_t sq = 0, sqq = 0;
+  for (int64_t k = 0; k < K; ++k) {
+    sw += (double)wh[k];
+    swq += (double)wh[k] * (double)q[k];
+    sq += q[k];
+    sqq += (int64_t)q[k] * q[k];
+  }
+  int64_t det = K * sqq - sq * sq;
+  if (det <= 0) return 0;
+  double aa = ((double)K * swq - sw * (double)sq) / (double)det;
+  *a = aa;
+  *b = (sw - aa * (double)sq) / (double)K;
+  return 1;
+}
+
+/* ---------------------------------------------------------------------------
+ * SSZ, asymmetric per-channel int8, one row.  Same flow, constants, greedy
+ * rule and convergence tests as the symmetric search above; the parameters
+ * are the pair (S, Z) ([SSZ] asymmetric: scale and offset optimised
+ * together).
+ *
+ * Readings taken where the document is silent:
+ *   - MinMax init from the channel's min lo and max hi:
+ *       S0 = max(fl32(fl32(hi - lo) / 255), fl32(min_scale)),
+ *       Z0 = clamp(-128 - rne(fl32(lo * fl32(1/S0))), -128, 127),
+ *     which maps lo to -128 and hi to (about) 127.
+ *   - each least-squares step fits the line w ~ a q + b to the codes q of
+ *     the current (S, Z) (o_lsq_affine) and converts it to parameters:
+ *       S' = max(fl32(a), fl32(min_scale)),
+ *       Z' = clamp(rne(-b / a), -128, 127)   (fp64 quotient, ties to even),
+ *     since S (q - Z) = S q - S Z.  All codes equal (det = 0) leaves nothing
+ *     to fit and ends the row.
+ *   - the candidate's error is computed with its own codes; kept only if
+ *     strictly better; iters, convergence and hist as in the symmetric case.
+ * ------------------------------------------------------------------------- */
+static void ssz_asym_one_row(const float* wh, int64_t K, int max_iter, double thr, float min_scale, float* S_out,
+                             int32_t* Z_out, int8_t* q, int32_t* iters_out, double* mse_out, double* hist,
+                             int8_t* qc) {
+  float lo = wh[0], hi = wh[0];
+  for (int64_t k = 1; k < K; ++k) {
+    if (wh[k] < lo) lo = wh[k];
+    if (wh[k] > hi) hi = wh[k];
+  }
+  float range = hi - lo;
+  float S = range / 255.0f;
+  if (S < min_scale) S = min_scale;
+  float inv0 = 1.0f / S;
+  int Z = O_QMIN_ASYM - (int)nearbyintf(lo * inv0);
+  if (Z < O_QMIN_ASYM) Z = O_QMIN_ASYM;
+  if (Z > O_QMAX_ASYM) Z = O_QMAX_ASYM;
+  o_quant_row_asym(wh, K, S, Z, q);
+  double best = o_mse_row_asym(wh, q, K, S, Z);
+  if (hist) hist[0] = best;
+
+  int it = 0;
+  for (int i = 1; i <= max_iter; ++i) {
+    it = i;
+    double a, b;
+    if (!o_lsq_affine(wh, q, K, &a, &b)) break;
+    float Sc = (float)a;
+    if (Sc < min_scale) Sc = min_scale;
+    double zr = nearbyint(-b / a);
+    int Zc = zr < (double)O_QMIN_ASYM ? O_QMIN_ASYM : (zr > (double)O_QMAX_ASYM ? O_QMAX_ASYM : (int)zr);
+    o_quant_row_asym(wh, K, Sc, Zc, qc);
+    double cur = o_mse_row_asym(wh, qc, K, Sc, Zc);
+    double d = best - cur;
+    int conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+    if (cur < best) {
+      S = Sc;
+      Z = Zc;
+      best = cur;
+      memcpy(q, qc, (size_t)K);
+    }
+    if (hist) hist[i] = best;
+    if (conv) break;
+  }
+  *S_out = S;
+  *Z_out = Z;
+  if (iters_out) *iters_out = it;
+  if (mse_out) *mse_out = best;
+}
+
+/* Asymmetric int8 weight quantization parameters for a [N,K] weight: fold s
+ * (may be NULL), then MinMax + asymmetric SSZ per row.  Outputs S[N], Z[N],
+ * q[N,K] codes in [-128,127], iters[N], mse[N], hist[N, max_iter+1] (the
+ * last three may be NULL). */
+int o_ssz_asym(const float* w, const float* s, int64_t N, int64_t K, int max_iter, double thr, float min_scale,
+               float* S, int32_t* Z, int8_t* q, int32_t* iters, double* mse, double* hist) {
+  if (!w || !S || !Z || !q || N < 0 || K <= 0) return O_EARG;
+  if (max_iter < 0 || !(thr >= 0.0) || !(min_scale > 0.0f)) return O_EARG;
+  if (!all_finite(w, N * K)) return O_ENONFINITE;
+  int bad = 0;
+#pragma omp parallel
+  {
+    float* wh = (float*)malloc(sizeof(float) * (size_t)K);
+    int8_t* qc = (int8_t*)malloc((size_t)K);
+    if (!wh || !qc) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t n = 0; n < N; ++n) {
+        o_fold_weight(w + n * K, s, 1, K, wh);
+        ssz_asym_one_row(wh, K, max_iter, thr, min_scale, S + n, Z + n, q + n * K, iters ? iters + n : NULL,
+                         mse ? mse + n : NULL, hist ? hist + n * (int64_t)(max_iter + 1) : NULL, qc);
+      }
+    }
+    free(wh);
+    free(qc);
+  }
+  return bad ? O_EARG : O_OK;
+}
+
 /* Per-tensor (per-layer) MinMax for comparison with per-channel ([PTQ]
  * granularity section): one S for the whole tensor,
  * S = max(fl32(max|W| / qmax), fl32(min_scale)); codes for every row. */

@@ -291,6 +291,113 @@ def test_ssz_converged_is_a_fixed_point():
         assert best == 0 or d / best < thr or abs(d) < thr
 
 
+# ------------------------------------------------------- asymmetric int8 SSZ (NEXT-1)
+
+def test_asym_code_table():
+    """Q = clamp(rne(R/S) + Z, -128, 127) at S = 1: ties to even, then the offset, then saturation."""
+    cases = [(0.5, 0, 0), (1.5, 0, 2), (2.5, 3, 5), (-2.5, 3, 1), (126.5, 0, 126), (127.5, 0, 127),
+             (-128.5, 0, -128), (-127.5, 0, -128), (100.0, 40, 127), (-100.0, -40, -128), (-3.0, -128, -128),
+             (0.0, -128, -128), (255.0, -128, 127), (254.5, -128, 126)]
+    for r, z, want in cases:
+        got = oracle.quant_row_asym(np.array([r], dtype=np.float32), 1.0, z)[0]
+        assert got == want, (r, z, got, want)
+
+
+def test_asym_lsq_brute_force():
+    """For fixed codes, sum(w - a q - b)^2 is minimised at the normal-equation solution: grid search."""
+    rng = np.random.default_rng(31)
+    for _ in range(60):
+        K = int(rng.integers(2, 9))
+        w = rng.standard_normal(K).astype(np.float32)
+        q = rng.integers(-128, 128, K).astype(np.int8)
+        if np.all(q == q[0]):
+            q[0] = q[0] ^ 1
+        a, b = oracle.lsq_affine(w, q)
+        wd, qd = w.astype(np.float64), q.astype(np.float64)
+        ga = np.linspace(a - 2e-3, a + 2e-3, 401)
+        gb = np.linspace(b - 0.05, b + 0.05, 401)
+        err = ((wd[None, None, :] - ga[:, None, None] * qd[None, None, :] - gb[None, :, None]) ** 2).sum(-1)
+        i, j = np.unravel_index(np.argmin(err), err.shape)
+        assert abs(ga[i] - a) <= 1.01 * (ga[1] - ga[0]) and abs(gb[j] - b) <= 1.01 * (gb[1] - gb[0])
+    assert oracle.lsq_affine(np.ones(5, np.float32), np.full(5, 7, np.int8)) is None
+
+
+def test_asym_exact_grid_row():
+    """w = c (k - z) with k spanning [-128, 127], c = 2^-e: MinMax recovers S = c and Z = z exactly,
+    the codes are k, the error is 0 and the first step converges."""
+    rng = np.random.default_rng(32)
+    for e, z in ((6, 37), (11, -90), (9, 0), (13, 127)):
+        c = 2.0 ** -e
+        k = rng.integers(-128, 128, (3, 80))
+        k[:, 5] = -128
+        k[:, 60] = 127
+        w = ((k - z) * c).astype(np.float32)
+        r = oracle.ssz_asym(w)
+        assert np.all(r["S"] == np.float32(c)) and np.all(r["Z"] == z), (r["S"], r["Z"])
+        np.testing.assert_array_equal(r["q"], k.astype(np.int8))
+        assert np.all(r["mse"] == 0.0) and np.all(r["iters"] == 1)
+
+
+def test_asym_degenerate_rows():
+    """All-zero row: floor scale, Z = -128, codes -128 (dequantized 0), error 0, one step.
+    Constant non-zero row: floor scale, Z saturates, all codes equal, nothing to fit (one step)."""
+    K = 24
+    w = np.zeros((2, K), dtype=np.float32)
+    w[1] = 0.5
+    r = oracle.ssz_asym(w)
+    fmin = np.float32(1e-5)
+    assert r["S"][0] == fmin and r["Z"][0] == -128 and np.all(r["q"][0] == -128) and r["mse"][0] == 0.0
+    assert r["S"][1] == fmin and r["Z"][1] == -128 and np.all(r["q"][1] == 127)
+    assert r["mse"][1] == pytest.approx((0.5 - float(fmin) * 255) ** 2, rel=1e-14)
+    assert np.all(r["iters"] == 1)
+
+
+def test_asym_offset_halves_the_step_on_one_sided_rows():
+    """Rows uniform on [0, 1]: the symmetric grid wastes its negative half, so its MinMax step is about
+    twice the asymmetric one and its error about four times larger.  A lost or mis-signed offset fails."""
+    rng = np.random.default_rng(33)
+    w = rng.uniform(0.0, 1.0, (16, 2048)).astype(np.float32)
+    w[:, 0], w[:, 1] = 0.0, 1.0
+    sym = oracle.ssz(w, None, 8, max_iter=0)
+    asym = oracle.ssz_asym(w, max_iter=0)
+    assert np.all(asym["Z"] == -128)
+    np.testing.assert_allclose(sym["S"] / asym["S"], 255 / 127, rtol=1e-6)
+    ratio = sym["mse"] / asym["mse"]
+    assert np.all((ratio > 3.3) & (ratio < 4.8)), ratio
+    # and shifted to [-1, 0] the offset flips to the top of the range
+    asym_n = oracle.ssz_asym(-w, max_iter=0)
+    assert np.all(asym_n["Z"] == 127)
+
+
+def test_asym_monotone_consistent_and_fixed_point():
+    w = _ssz_rows(34, N=64)
+    w[::3] += np.float32(0.01)  # some rows off-centre
+    r = oracle.ssz_asym(w, hist=True)
+    mm = oracle.ssz_asym(w, max_iter=0)
+    thr = 1e-10
+    fmin = np.float32(1e-5)
+    for n in range(w.shape[0]):
+        it = r["iters"][n]
+        seq = r["hist"][n, : it + 1]
+        assert np.all(np.diff(seq) <= 0) and r["mse"][n] == seq[-1] and r["mse"][n] <= mm["mse"][n]
+        assert -128 <= r["Z"][n] <= 127
+        np.testing.assert_array_equal(oracle.quant_row_asym(w[n], r["S"][n], r["Z"][n]), r["q"][n])
+        assert oracle.mse_row_asym(w[n], r["q"][n], r["S"][n], r["Z"][n]) == r["mse"][n]
+        if 1 <= it < 20 and r["mse"][n] > 0:
+            if seq[-1] == seq[-2]:
+                # the last candidate was rejected: it is rebuilt from the kept codes and is again no better
+                a, b = oracle.lsq_affine(w[n], r["q"][n])
+                Sn = max(np.float32(a), fmin)
+                Zn = int(min(127, max(-128, np.rint(-b / a))))
+                cur = oracle.mse_row_asym(w[n], oracle.quant_row_asym(w[n], Sn, Zn), Sn, Zn)
+                assert cur >= r["mse"][n]
+            else:
+                # the last candidate was kept with a change under the relative or absolute threshold
+                d = seq[-2] - seq[-1]
+                assert d / seq[-2] < thr or abs(d) < thr
+    assert np.mean(r["mse"] < mm["mse"]) > 0.3
+
+
 def test_ssz_constants_golden():
     rows = {k: float(v) for k, v in read_golden("ssz_constants.txt")}
     import inspect
