@@ -18,6 +18,12 @@ Inputs are resident in HBM before the timed region.  Kernels run on torch's
 current stream; HIP events on that stream bracket every stage, giving
 per-kernel durations.  Prints one JSON line.
 
+--workload ssz_scale measures the weight quantization alone at model scale:
+MinMax + SSZ over the 128 matrices of 32 hidden-4096 layers (QKV [12288,4096],
+out [4096,4096], fc1 [16384,4096], fc2 [4096,16384], bf16, heavy-tailed rows),
+back to back on one stream, once as symmetric int8, once as symmetric int4
+and once as asymmetric int8; a step is the three passes over all matrices.
+
 --workload decode measures the decode configuration instead (16 tokens,
 X [16,8192] against W [28672,8192]): the weight is calibrated and quantized
 once, untimed; a step is the per-token quantization of the token batch and
@@ -57,7 +63,8 @@ def parse():
     p.add_argument("--calib-batches", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle GEMM time of the CPU baseline")
-    p.add_argument("--workload", choices=("opt67b", "decode"), default="opt67b")
+    p.add_argument("--workload", choices=("opt67b", "decode", "ssz_scale"), default="opt67b")
+    p.add_argument("--layers", type=int, default=32, help="ssz_scale workload: number of 4-matrix layers")
     p.add_argument("--copy-ref", action="store_true",
                    help="only run a plain 1 GiB device copy three times (reference for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -138,6 +145,9 @@ def main():
 
     if args.workload == "decode":
         decode(args)
+        return
+    if args.workload == "ssz_scale":
+        ssz_scale(args)
         return
 
     import numpy as np
@@ -383,6 +393,108 @@ def decode(args):
                                "the weight's calibration and SSZ run first, untimed like on the GPU",
                                "quant_seconds": t1 - t0, "gemm_dequant_seconds": t2 - t1,
                                "untimed_prep_seconds": p1 - p0}
+    print(json.dumps(out), flush=True)
+
+
+def ssz_scale(args):
+    import numpy as np
+    import torch
+
+    import post_int8_quantization_amd as pq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cases = synth.cases("ssz_scale")[: 4 * args.layers]
+    stream = torch.cuda.current_stream()
+    mats = []
+    for c in cases:
+        a = c.w()
+        mats.append((c, torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)))
+        del a
+    # outputs per matrix shape (overwritten layer after layer), per-row statistics per matrix
+    outs = {}
+    for c, _ in mats:
+        if (c.N, c.K) not in outs:
+            outs[(c.N, c.K)] = dict(
+                S=torch.empty(c.N, dtype=torch.float32, device=dev), Z=torch.empty(c.N, dtype=torch.int32, device=dev),
+                q8=torch.empty((c.N, c.K), dtype=torch.int8, device=dev),
+                q4=torch.empty((c.N, c.K // 2), dtype=torch.uint8, device=dev),
+                mse=torch.empty(c.N, dtype=torch.float64, device=dev))
+    iters = {m: [torch.empty(c.N, dtype=torch.int32, device=dev) for c, _ in mats] for m in ("int8", "int4", "asym8")}
+    torch.cuda.synchronize()
+
+    def step(tm):
+        for mode in ("int8", "int4", "asym8"):
+            def run(mode=mode):
+                for i, (c, w) in enumerate(mats):
+                    o = outs[(c.N, c.K)]
+                    if mode == "asym8":
+                        pq.ssz_weight_qparams_asym(w, None, scale=o["S"], zero_point=o["Z"], wq=o["q8"],
+                                                   iters=iters[mode][i], mse=o["mse"], stream=stream)
+                    else:
+                        bits = 8 if mode == "int8" else 4
+                        pq.ssz_weight_qparams(w, None, bits=bits, scale=o["S"], wq=o["q8"] if bits == 8 else o["q4"],
+                                              iters=iters[mode][i], mse=o["mse"], stream=stream)
+            tm.stage(mode, run)
+
+    for _ in range(args.warmup):
+        step(Timer(torch))
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot = tm.totals()
+    K = args.steps
+    elems = sum(c.N * c.K for c, _ in mats)
+    rows = sum(c.N for c, _ in mats)
+    stages = {}
+    for mode in ("int8", "int4", "asym8"):
+        sec = tot[mode][0] / 1e3 / K
+        out_b = elems if mode != "int4" else elems // 2
+        nbytes = 2 * elems + out_b + rows * (4 + 4 + 8 + (4 if mode == "asym8" else 0))
+        its = np.concatenate([t.cpu().numpy() for t in iters[mode]]).astype(np.int64)
+        passes = sum(int(c.K * (iters[mode][i].cpu().numpy().astype(np.int64) + 1).sum()) for i, (c, _) in
+                     enumerate(mats))
+        ops = (SSZ_OPS_PER_ELEM_PASS + (2 if mode == "asym8" else 0)) * passes
+        stages[mode] = {"ms": sec * 1e3, "GB/s": nbytes / sec / 1e9, "frac_hbm": nbytes / sec / PEAK_HBM,
+                        "mean_iters": float(its.mean()), "element_passes": passes,
+                        "frac_alu": ops / sec / PEAK_ALU, "launches": len(mats)}
+    v = stages["int8"]
+    roof = {"kernel": "k_ssz", "bound": "alu",
+            "achieved": SSZ_OPS_PER_ELEM_PASS * v["element_passes"] / (v["ms"] / 1e3) / 1e12,
+            "peak": PEAK_ALU / 1e12, "unit": "Tlane-op/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    rec = load_counters("k_ssz")
+    roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
+    roof["avg_launch_us"] = v["ms"] * 1e3 / len(mats)
+    out = {
+        "metric": METRIC, "value": v["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32+f64", "data": "synthetic",
+        "config": {"workload": f"ssz_scale: MinMax + SSZ over {len(mats)} matrices ({args.layers} hidden-4096 layers "
+                               "x QKV/out/fc1/fc2), bf16 N(0,0.02) x logU[0.05,1] with 0.1 percent entries x20, no "
+                               "smoothing; value = symmetric int8 pass; int4 and asymmetric int8 in stages",
+                   "elements": elems, "rows": rows, "parallelism": "single GPU"},
+        "gpu_ms_per_step": sum(x[0] for x in tot.values()) / K, "stages": stages, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = [c for c, _ in mats[:16]]
+        secs = 0.0
+        nb = 0
+        for c in sample:
+            wh = synth.widen(c.w())
+            t0 = time.perf_counter()
+            oracle.ssz(wh, None, 8)
+            secs += time.perf_counter() - t0
+            nb += c.N * c.K * 3 + c.N * 16
+        out["cpu_baseline"] = {"value": nb / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": f"symmetric int8 SSZ of the first {len(sample)} matrices "
+                               "(4 layers), every row", "seconds": secs}
     print(json.dumps(out), flush=True)
 
 

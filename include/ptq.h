@@ -7,6 +7,7 @@
  *   sq_absmax_calib      column absmax calibration of activations / weights
  *   sq_smooth_factors    SmoothQuant smoothing factors s_j
  *   ssz_weight_qparams   MinMax + SSZ per-output-channel weight quantization
+ *   ssz_weight_qparams_asym   the same with a per-channel offset (int8)
  *   quant_per_token_i8   per-token int8 activation quantization (with X/s)
  *   w8a8_gemm_dequant    int8 x int8 -> int32 GEMM, fused dequantization
  *
@@ -148,7 +149,8 @@ PTQ_API ptq_status sq_smooth_factors(const float* act_amax, const float* w_amax,
  *
  *   w          [N, K] of `dtype`, 16-B aligned;  N >= 1;  K multiple of 16, <= 131072
  *   s          [K] fp32 smoothing factors, or NULL for no smoothing
- *   bits       8 or 4;  symmetric must be 1 (asymmetric is not supported)
+ *   bits       8 or 4;  symmetric must be 1 (asymmetric int8: ssz_weight_qparams_asym;
+ *              symmetric = 0 here returns PTQ_ERR_UNSUPPORTED)
  *   max_iter   0..20 (PTQ_SSZ_MAX_ITER; 0 = MinMax only)
  *   threshold  >= 0 (PTQ_SSZ_THRESHOLD);  min_scale > 0 (PTQ_SSZ_MIN_SCALE)
  *   scale      [N] fp32 output: S per output channel
@@ -161,6 +163,39 @@ PTQ_API ptq_status sq_smooth_factors(const float* act_amax, const float* w_amax,
 PTQ_API ptq_status ssz_weight_qparams(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits,
                               int symmetric, int max_iter, double threshold, float min_scale, float* scale,
                               void* wq, int32_t* iters, double* mse, void* stream);
+
+/*
+ * Per-output-channel ASYMMETRIC int8 weight quantization: MinMax initial
+ * scale and offset refined by the SSZ least-squares search over both.
+ * [SSZ] asymmetric mode (scale and offset optimised together; int8 only, as
+ * the method's limits exclude int4 asymmetric), flow, convergence and
+ * constants as for ssz_weight_qparams; [INT8] 2.1 Q = round(R/S) + Z with
+ * saturation.
+ *
+ * For each row n, with w_hat as above:
+ *   quant(S, Z)[k] = clamp(rne(fl32(w_hat[k] * fl32(1/S))) + Z, -128, 127)
+ *   mse(S, Z)      = mean_k (w_hat[k] - S (q[k] - Z))^2 in fp64
+ *   init: lo = min_k w_hat[k], hi = max_k w_hat[k];
+ *         S = max(fl32(fl32(hi - lo) / 255), min_scale);
+ *         Z = clamp(-128 - rne(fl32(lo * fl32(1/S))), -128, 127)
+ *   step: for the codes q of the current (S, Z), the least-squares line
+ *         w_hat ~ a q + b (2x2 normal equations; det = K sum q^2 - (sum q)^2,
+ *         det == 0 stops the row);  S' = max(fl32(a), min_scale),
+ *         Z' = clamp(rne(-b / a), -128, 127) (fp64 quotient);  kept only if
+ *         mse(S', Z') < best;  convergence, iteration limit and per-row stop
+ *         exactly as in ssz_weight_qparams.
+ * Dequantized weight: S (q - Z).
+ *
+ *   w, s, N, K, max_iter, threshold, min_scale   as for ssz_weight_qparams
+ *   scale       [N] fp32 output
+ *   zero_point  [N] int32 output, in [-128, 127]
+ *   wq          [N, K] int8 output codes in [-128, 127], 16-B aligned, or NULL
+ *   iters, mse  [N] int32 / fp64 outputs, or NULL
+ */
+PTQ_API ptq_status ssz_weight_qparams_asym(const void* w, int dtype, int64_t N, int64_t K, const float* s,
+                                           int max_iter, double threshold, float min_scale, float* scale,
+                                           int32_t* zero_point, int8_t* wq, int32_t* iters, double* mse,
+                                           void* stream);
 
 /*
  * Per-token dynamic int8 activation quantization with the smoothing fold.

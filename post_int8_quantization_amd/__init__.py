@@ -33,7 +33,7 @@ STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE"
           5: "PTQ_ERR_ARG", 6: "PTQ_ERR_ALIGN", 7: "PTQ_ERR_HIP"}
 
 EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
-           "ssz_weight_qparams", "quant_per_token_i8", "w8a8_gemm_dequant")
+           "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant")
 
 
 class PtqError(RuntimeError):
@@ -56,10 +56,11 @@ def _load():
     lib.sq_absmax_calib.argtypes = [vp, ci, i64, i64, vp, ci, vp]
     lib.sq_smooth_factors.argtypes = [vp, vp, i64, f32, vp, vp]
     lib.ssz_weight_qparams.argtypes = [vp, ci, i64, i64, vp, ci, ci, ci, f64, f32, vp, vp, vp, vp, vp]
+    lib.ssz_weight_qparams_asym.argtypes = [vp, ci, i64, i64, vp, ci, f64, f32, vp, vp, vp, vp, vp, vp]
     lib.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
     lib.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
-    for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "quant_per_token_i8",
-               "w8a8_gemm_dequant"):
+    for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
+               "quant_per_token_i8", "w8a8_gemm_dequant"):
         getattr(lib, fn).restype = ci
     return lib
 
@@ -150,6 +151,34 @@ def ssz_weight_qparams(w, s=None, bits=8, symmetric=True, max_iter=SSZ_MAX_ITER,
                                   int(max_iter), float(threshold), float(min_scale), _ptr(scale), _ptr(wq),
                                   _ptr(iters), _ptr(mse), _stream(stream)))
     return scale, wq, iters, mse
+
+
+def ssz_weight_qparams_asym(w, s=None, max_iter=SSZ_MAX_ITER, threshold=SSZ_THRESHOLD, min_scale=SSZ_MIN_SCALE,
+                            want_codes=True, want_stats=True, scale=None, zero_point=None, wq=None, iters=None,
+                            mse=None, stream=None):
+    """Asymmetric int8.  Returns (scale[N] fp32, zero_point[N] int32, wq int8 [N,K] or None, iters or None,
+    mse or None).  Output tensors may be passed in preallocated."""
+    _dev(w, "w", _FLOATS)
+    N, K = w.shape
+    dev = w.device
+    if s is not None:
+        _dev(s, "s", (torch.float32,))
+    if scale is None:
+        scale = torch.empty(N, dtype=torch.float32, device=dev)
+    if zero_point is None:
+        zero_point = torch.empty(N, dtype=torch.int32, device=dev)
+    if wq is None and want_codes:
+        wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    if want_stats:
+        iters = torch.empty(N, dtype=torch.int32, device=dev) if iters is None else iters
+        mse = torch.empty(N, dtype=torch.float64, device=dev) if mse is None else mse
+    for t, nm in ((scale, "scale"), (zero_point, "zero_point"), (wq, "wq"), (iters, "iters"), (mse, "mse")):
+        if t is not None:
+            _dev(t, nm)
+    _check(lib.ssz_weight_qparams_asym(_ptr(w), _dtype_code(w), N, K, _ptr(s), int(max_iter), float(threshold),
+                                       float(min_scale), _ptr(scale), _ptr(zero_point), _ptr(wq), _ptr(iters),
+                                       _ptr(mse), _stream(stream)))
+    return scale, zero_point, wq, iters, mse
 
 
 def quant_per_token_i8(x, s=None, xq=None, tok_scale=None, stream=None):

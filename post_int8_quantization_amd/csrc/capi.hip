@@ -93,7 +93,9 @@ ptq_status ssz_weight_qparams(const void* w, int dtype, int64_t N, int64_t K, co
   if (N > 0x7fffffff) return fail(PTQ_ERR_SHAPE, "%s: N=%lld too large", fn, (long long)N);
   if (bits != 8 && bits != 4) return fail(PTQ_ERR_UNSUPPORTED, "%s: bits=%d (only 8 and 4 are supported)", fn, bits);
   if (symmetric != 1)
-    return fail(PTQ_ERR_UNSUPPORTED, "%s: only symmetric per-channel quantization is supported", fn);
+    return fail(PTQ_ERR_UNSUPPORTED,
+                "%s: symmetric=0 is served by ssz_weight_qparams_asym (int8 only; the SSZ method has no int4 "
+                "asymmetric mode)", fn);
   if (max_iter < 0 || max_iter > PTQ_SSZ_MAX_ITER)
     return fail(PTQ_ERR_ARG, "%s: max_iter=%d must lie in [0, %d]", fn, max_iter, PTQ_SSZ_MAX_ITER);
   if (!(threshold >= 0.0) || isinf(threshold)) return fail(PTQ_ERR_ARG, "%s: threshold=%g invalid", fn, threshold);
@@ -103,6 +105,29 @@ ptq_status ssz_weight_qparams(const void* w, int dtype, int64_t N, int64_t K, co
     return fail(PTQ_ERR_ALIGN, "%s: w, s and wq must be 16-byte aligned", fn);
   return from_hip(ptq::launch_ssz(w, dtype, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters, mse,
                                   (hipStream_t)stream),
+                  fn);
+}
+
+ptq_status ssz_weight_qparams_asym(const void* w, int dtype, int64_t N, int64_t K, const float* s, int max_iter,
+                                   double threshold, float min_scale, float* scale, int32_t* zero_point, int8_t* wq,
+                                   int32_t* iters, double* mse, void* stream) {
+  const char* fn = "ssz_weight_qparams_asym";
+  if (!w || !scale || !zero_point) return fail(PTQ_ERR_NULL, "%s: w, scale and zero_point are required", fn);
+  if (!known_dtype(dtype)) return fail(PTQ_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+  if (N <= 0 || K <= 0) return fail(PTQ_ERR_SHAPE, "%s: N=%lld K=%lld must be >= 1", fn, (long long)N, (long long)K);
+  if (K % PTQ_K_MULTIPLE) return fail(PTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+  if (K > ptq::kMaxRowK) return fail(PTQ_ERR_SHAPE, "%s: K=%lld exceeds %lld", fn, (long long)K,
+                                     (long long)ptq::kMaxRowK);
+  if (N > 0x7fffffff) return fail(PTQ_ERR_SHAPE, "%s: N=%lld too large", fn, (long long)N);
+  if (max_iter < 0 || max_iter > PTQ_SSZ_MAX_ITER)
+    return fail(PTQ_ERR_ARG, "%s: max_iter=%d must lie in [0, %d]", fn, max_iter, PTQ_SSZ_MAX_ITER);
+  if (!(threshold >= 0.0) || isinf(threshold)) return fail(PTQ_ERR_ARG, "%s: threshold=%g invalid", fn, threshold);
+  if (!(min_scale > 0.0f) || isinf(min_scale))
+    return fail(PTQ_ERR_ARG, "%s: min_scale=%g must be positive", fn, (double)min_scale);
+  if (!aligned16(w) || (s && !aligned16(s)) || (wq && !aligned16(wq)))
+    return fail(PTQ_ERR_ALIGN, "%s: w, s and wq must be 16-byte aligned", fn);
+  return from_hip(ptq::launch_ssz_asym(w, dtype, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                       iters, mse, (hipStream_t)stream),
                   fn);
 }
 

@@ -24,6 +24,10 @@ hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const floa
                       double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,
                       hipStream_t stream);
 
+hipError_t launch_ssz_asym(const void* w, int dtype, int64_t N, int64_t K, const float* s, int max_iter,
+                           double threshold, float min_scale, float* scale, int32_t* zero_point, int8_t* wq,
+                           int32_t* iters, double* mse, hipStream_t stream);
+
 hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
                                int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, hipStream_t stream);
 

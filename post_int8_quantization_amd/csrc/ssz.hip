@@ -1,4 +1,5 @@
-// ssz.hip -- MinMax + SSZ per-output-channel symmetric weight quantization (gfx950).
+// ssz.hip -- MinMax + SSZ per-output-channel weight quantization (gfx950):
+// symmetric int8/int4 (k_ssz) and asymmetric int8 (k_ssz_asym, further down).
 //
 // [SSZ] flow: MinMax initial scale, then least-squares refits of the scale for
 // the current codes, a refit kept only when it lowers the quantization error,
@@ -8,7 +9,7 @@
 //
 // One block of TPR threads owns one row (output channel).  The row is read
 // from HBM once and stays in registers (CPT chunks of 16 elements per
-// thread, in fp32 and, when it fits, also widened to fp64) for every pass;
+// thread, in fp32, widened to fp64 where a pass needs it) for every pass;
 // all passes are ALU work.  One pass over the row for a scale S computes, per
 // element, the code q = clamp(rne(w_hat * inv S)) and accumulates A =
 // sum(w_hat q) in fp64 and B = sum(q^2) exactly (fp32 per lane, integer
@@ -70,6 +71,47 @@ __device__ __forceinline__ PassSums row_pass(const float (&wh)[CPT][16], const d
   return r;
 }
 
+// Row n of w, folded (w_hat = fl32(w * s_j)), into registers: CPT chunks of 16 elements per thread,
+// chunk c8 of thread tid at elements (tid + TPR*c8)*16 ..; chunks past the row are zeros (they add
+// nothing to any sum and never change a max of magnitudes).  WIDE also keeps an fp64 copy.
+template <int DT, bool HAS_S, int TPR, int CPT, bool WIDE>
+__device__ __forceinline__ void load_row(const void* __restrict__ w, int64_t n, int64_t K, const float* __restrict__ s,
+                                         int tid, float (&wh)[CPT][16], double (&wd)[WIDE ? CPT : 1][16]) {
+  const int64_t nchunk = K / 16;
+#pragma unroll
+  for (int c8 = 0; c8 < CPT; ++c8) {
+    const int64_t c = tid + (int64_t)TPR * c8;
+    if (c < nchunk) {
+      float a8[8], b8[8];
+      load8<DT>(w, n * K + c * 16, a8);
+      load8<DT>(w, n * K + c * 16 + 8, b8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wh[c8][e] = a8[e];
+        wh[c8][e + 8] = b8[e];
+      }
+      if constexpr (HAS_S) {
+        const float4* sp = reinterpret_cast<const float4*>(s + c * 16);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 sv = sp[q4];
+          wh[c8][4 * q4 + 0] = wh[c8][4 * q4 + 0] * sv.x;
+          wh[c8][4 * q4 + 1] = wh[c8][4 * q4 + 1] * sv.y;
+          wh[c8][4 * q4 + 2] = wh[c8][4 * q4 + 2] * sv.z;
+          wh[c8][4 * q4 + 3] = wh[c8][4 * q4 + 3] * sv.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
+    }
+    if constexpr (WIDE) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wd[c8][e] = (double)wh[c8][e];
+    }
+  }
+}
+
 // K * mse(S) from the pass sums: W2 - 2 S A + S^2 B, never below 0
 __device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) {
   const double Sd = (double)S;
@@ -77,13 +119,16 @@ __device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) 
   return e > 0.0 ? e : 0.0;
 }
 
-template <int DT, bool HAS_S, int BITS, int TPR, int CPT>
+// WIDE_MODE 1 keeps an fp64 copy of the row in registers, saving one conversion per element and pass;
+// the default (0) widens on the fly: the row copy triples the register footprint, and the occupancy it
+// costs outweighs the conversion (measured 25-30% slower on 4096- and 16384-wide rows, int8 and int4).
+template <int DT, bool HAS_S, int BITS, int TPR, int CPT, int WIDE_MODE = 0>
 __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t N, int64_t K,
                                              const float* __restrict__ s, int max_iter, double thr, float min_scale,
                                              float* __restrict__ scale, void* __restrict__ wq,
                                              int32_t* __restrict__ iters, double* __restrict__ mse) {
   constexpr int NW = TPR / kWave;
-  constexpr bool WIDE = CPT <= 4 && TPR <= 256;  // fp64 copy of the row fits the register budget
+  constexpr bool WIDE = WIDE_MODE == 1;
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
   __shared__ double red_d[NW];
   __shared__ int red_i[NW];
@@ -93,43 +138,17 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
   const double Kd = (double)K;
 
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-    // load + fold; out-of-row chunks are zeros (they add nothing to any sum)
     float wh[CPT][16];
     double wd[WIDE ? CPT : 1][16];
+    load_row<DT, HAS_S, TPR, CPT, WIDE>(w, n, K, s, tid, wh, wd);
     float m = 0.0f;
     double w2 = 0.0;
 #pragma unroll
     for (int c8 = 0; c8 < CPT; ++c8) {
-      const int64_t c = tid + (int64_t)TPR * c8;
-      if (c < nchunk) {
-        float a8[8], b8[8];
-        load8<DT>(w, n * K + c * 16, a8);
-        load8<DT>(w, n * K + c * 16 + 8, b8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          wh[c8][e] = a8[e];
-          wh[c8][e + 8] = b8[e];
-        }
-        if constexpr (HAS_S) {
-          const float4* sp = reinterpret_cast<const float4*>(s + c * 16);
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 sv = sp[q4];
-            wh[c8][4 * q4 + 0] = wh[c8][4 * q4 + 0] * sv.x;
-            wh[c8][4 * q4 + 1] = wh[c8][4 * q4 + 1] * sv.y;
-            wh[c8][4 * q4 + 2] = wh[c8][4 * q4 + 2] * sv.z;
-            wh[c8][4 * q4 + 3] = wh[c8][4 * q4 + 3] * sv.w;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
-      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         m = fmaxf(m, fabsf(wh[c8][e]));
         const double x = (double)wh[c8][e];
-        if constexpr (WIDE) wd[c8][e] = x;
         w2 = __builtin_fma(x, x, w2);
       }
     }
@@ -231,6 +250,255 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Asymmetric int8 ([SSZ] asymmetric mode: scale and offset fitted together;
+// [INT8] 2.1 Q = round(R/S) + Z with saturation).  Codes
+//   q = clamp(rne(fl32(w_hat * inv S)) + Z, -128, 127),  dequantized S (q - Z).
+// A pass for (S, Z) accumulates A = sum w_hat q (fp64), B = sum q^2 and
+// C = sum q (exact).  With the row's W1 = sum w_hat and W2 = sum w_hat^2:
+//   K mse = W2 - 2 S (A - Z W1) + S^2 (B - 2 Z C + K Z^2),
+// and the least-squares line w_hat ~ a q + b through the pass's codes solves
+// the 2x2 normal equations: det = K B - C^2, a = (K A - W1 C) / det,
+// b = (W1 - a C) / K, giving S' = max(fl32(a), min_scale) and
+// Z' = clamp(rne(-b / a), -128, 127).  MinMax init from the row's min lo and
+// max hi: S0 = max(fl32(fl32(hi - lo) / 255), min_scale),
+// Z0 = clamp(-128 - rne(fl32(lo * inv S0)), -128, 127).
+// Register slots past the row hold w_hat = 0, whose code is Z: each adds Z^2
+// to B and Z to C, which the pass subtracts exactly.
+
+struct PassSumsA {
+  double a;  // sum w_hat q
+  double b;  // sum q^2 (an exact integer)
+  double c;  // sum q   (an exact integer)
+};
+
+__device__ __forceinline__ float code_asym_f(float x, float inv, float zf) {
+  return fminf(fmaxf(__builtin_rintf(x * inv) + zf, -128.0f), 127.0f);
+}
+
+template <int TPR, int CPT, bool WIDE>
+__device__ __forceinline__ PassSumsA row_pass_asym(const float (&wh)[CPT][16], const double (&wd)[WIDE ? CPT : 1][16],
+                                                   float S, int Z, double pad, double* red_d, int tid) {
+  const float inv = 1.0f / S;
+  const float zf = (float)Z;
+  double a = 0.0;
+  float bq = 0.0f;  // at most 16*CPT terms of <= 128^2 each: exact in fp32
+  float cq = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float q = code_asym_f(wh[m][k], inv, zf);
+      const double w = WIDE ? wd[WIDE ? m : 0][k] : (double)wh[m][k];
+      a = __builtin_fma(w, (double)q, a);
+      bq = __builtin_fmaf(q, q, bq);
+      cq += q;
+    }
+  }
+  PassSumsA r;
+  r.a = wave_sum(a);
+  r.b = (double)wave_sum((int)bq);
+  r.c = (double)wave_sum((int)cq);
+  constexpr int NW = TPR / kWave;
+  if constexpr (NW > 1) {
+    const int w = tid / kWave;
+    __syncthreads();  // previous readers of the LDS slots are done
+    if ((tid & (kWave - 1)) == 0) {
+      red_d[w] = r.a;
+      red_d[NW + w] = r.b;
+      red_d[2 * NW + w] = r.c;
+    }
+    __syncthreads();
+    r.a = red_d[0];
+    r.b = red_d[NW];
+    r.c = red_d[2 * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      r.a += red_d[i];
+      r.b += red_d[NW + i];
+      r.c += red_d[2 * NW + i];
+    }
+  }
+  const double zd = (double)Z;
+  r.b -= pad * zd * zd;
+  r.c -= pad * zd;
+  return r;
+}
+
+// K * mse(S, Z) from the pass sums, never below 0
+__device__ __forceinline__ double sq_err_asym(double w2, double w1, double Kd, float S, int Z, const PassSumsA& p) {
+  const double Sd = (double)S, zd = (double)Z;
+  const double cross = p.a - zd * w1;
+  const double quad = (p.b - 2.0 * zd * p.c) + Kd * zd * zd;  // sum (q - Z)^2, exact
+  const double e = (w2 - 2.0 * Sd * cross) + Sd * Sd * quad;
+  return e > 0.0 ? e : 0.0;
+}
+
+template <int DT, bool HAS_S, int TPR, int CPT, int WIDE_MODE = 0>
+__global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, int64_t N, int64_t K,
+                                                  const float* __restrict__ s, int max_iter, double thr,
+                                                  float min_scale, float* __restrict__ scale,
+                                                  int32_t* __restrict__ zero_point, int8_t* __restrict__ wq,
+                                                  int32_t* __restrict__ iters, double* __restrict__ mse) {
+  constexpr int NW = TPR / kWave;
+  constexpr bool WIDE = WIDE_MODE == 1;
+  __shared__ double red_d[3 * NW];
+  __shared__ float red_f[2 * NW];
+  const int tid = threadIdx.x;
+  const int64_t nchunk = K / 16;
+  const double Kd = (double)K;
+  const double pad = (double)((int64_t)TPR * CPT * 16 - K);  // zero slots per row
+
+  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    float wh[CPT][16];
+    double wd[WIDE ? CPT : 1][16];
+    load_row<DT, HAS_S, TPR, CPT, WIDE>(w, n, K, s, tid, wh, wd);
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    double w1 = 0.0, w2 = 0.0;
+#pragma unroll
+    for (int c8 = 0; c8 < CPT; ++c8) {
+      const bool in = tid + (int64_t)TPR * c8 < nchunk;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v = wh[c8][e];
+        lo = fminf(lo, in ? v : lo);
+        hi = fmaxf(hi, in ? v : hi);
+        const double x = (double)v;
+        w1 += x;
+        w2 = __builtin_fma(x, x, w2);
+      }
+    }
+    lo = -wave_max(-lo);
+    hi = wave_max(hi);
+    w1 = wave_sum(w1);
+    w2 = wave_sum(w2);
+    if constexpr (NW > 1) {
+      __syncthreads();
+      if ((tid & (kWave - 1)) == 0) {
+        red_f[tid / kWave] = lo;
+        red_f[NW + tid / kWave] = hi;
+        red_d[tid / kWave] = w1;
+        red_d[NW + tid / kWave] = w2;
+      }
+      __syncthreads();
+      lo = red_f[0];
+      hi = red_f[NW];
+      w1 = red_d[0];
+      w2 = red_d[NW];
+#pragma unroll
+      for (int i = 1; i < NW; ++i) {
+        lo = fminf(lo, red_f[i]);
+        hi = fmaxf(hi, red_f[NW + i]);
+        w1 += red_d[i];
+        w2 += red_d[NW + i];
+      }
+    }
+
+    // MinMax init
+    const float range = hi - lo;
+    float S = range / 255.0f;
+    S = S < min_scale ? min_scale : S;
+    int Z;
+    {
+      const float inv0 = 1.0f / S;
+      const float z0 = -128.0f - __builtin_rintf(lo * inv0);
+      Z = (int)fminf(fmaxf(z0, -128.0f), 127.0f);
+    }
+    PassSumsA cur = row_pass_asym<TPR, CPT, WIDE>(wh, wd, S, Z, pad, red_d, tid);
+    double best = sq_err_asym(w2, w1, Kd, S, Z, cur) / Kd;
+
+    int it = 0;
+    for (int i = 1; i <= max_iter; ++i) {
+      it = i;
+      const double det = Kd * cur.b - cur.c * cur.c;  // exact: integers below 2^53
+      if (det <= 0.0) break;
+      const double a = (Kd * cur.a - w1 * cur.c) / det;
+      const double b = (w1 - a * cur.c) / Kd;
+      float Sc = (float)a;
+      Sc = Sc < min_scale ? min_scale : Sc;
+      const double zr = __builtin_rint(-b / a);
+      const int Zc = zr < -128.0 ? -128 : (zr > 127.0 ? 127 : (int)zr);
+      const PassSumsA p = row_pass_asym<TPR, CPT, WIDE>(wh, wd, Sc, Zc, pad, red_d, tid);
+      const double c = sq_err_asym(w2, w1, Kd, Sc, Zc, p) / Kd;
+      const double d = best - c;
+      const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+      if (c < best) {
+        S = Sc;
+        Z = Zc;
+        best = c;
+        cur = p;
+      }
+      if (conv) break;
+    }
+
+    // codes of the kept (S, Z) and their error summed directly (the reported mse)
+    double e_dir = 0.0;
+    if (wq || mse) {
+      const float inv = 1.0f / S;
+      const float zf = (float)Z;
+      const double Sd = (double)S;
+#pragma unroll
+      for (int c8 = 0; c8 < CPT; ++c8) {
+        const int64_t c = tid + (int64_t)TPR * c8;
+        float q[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          q[e] = code_asym_f(wh[c8][e], inv, zf);
+          // slots past the row: w_hat = 0 and q = Z, so they add 0
+          const double dd = __builtin_fma(-Sd, (double)(q[e] - zf), (double)wh[c8][e]);  // S*(q-Z) exact in fp64
+          e_dir = __builtin_fma(dd, dd, e_dir);
+        }
+        if (wq && c < nchunk) {
+          uint4 o;
+          o.x = pack4_i8(q[0], q[1], q[2], q[3]);
+          o.y = pack4_i8(q[4], q[5], q[6], q[7]);
+          o.z = pack4_i8(q[8], q[9], q[10], q[11]);
+          o.w = pack4_i8(q[12], q[13], q[14], q[15]);
+          *reinterpret_cast<uint4*>(wq + n * K + c * 16) = o;
+        }
+      }
+      if (mse) {
+        e_dir = wave_sum(e_dir);
+        if constexpr (NW > 1) {
+          __syncthreads();
+          if ((tid & (kWave - 1)) == 0) red_d[tid / kWave] = e_dir;
+          __syncthreads();
+          e_dir = red_d[0];
+#pragma unroll
+          for (int i = 1; i < NW; ++i) e_dir += red_d[i];
+        }
+      }
+    }
+    if (tid == 0) {
+      scale[n] = S;
+      zero_point[n] = Z;
+      if (iters) iters[n] = it;
+      if (mse) mse[n] = e_dir / Kd;
+    }
+  }
+}
+
+template <int DT, bool HAS_S>
+hipError_t dispatch_asym(const void* w, int64_t N, int64_t K, const float* s, int max_iter, double thr,
+                         float min_scale, float* scale, int32_t* zp, int8_t* wq, int32_t* iters, double* mse,
+                         hipStream_t stream) {
+  const int64_t nchunk = K / 16;
+  int tpr = 64;
+  while (tpr < 1024 && (nchunk + tpr - 1) / tpr > 4) tpr *= 2;
+  const int64_t cpt = (nchunk + tpr - 1) / tpr;
+#define PTQ_SA(TPR_, CPT_)                                                                                \
+  if (tpr == TPR_ && cpt <= CPT_) {                                                                       \
+    k_ssz_asym<DT, HAS_S, TPR_, CPT_><<<(unsigned)N, TPR_, 0, stream>>>(w, N, K, s, max_iter, thr,        \
+                                                                        min_scale, scale, zp, wq, iters,  \
+                                                                        mse);                             \
+    return hipGetLastError();                                                                             \
+  }
+  PTQ_SA(64, 1) PTQ_SA(64, 2) PTQ_SA(64, 4)
+  PTQ_SA(128, 4) PTQ_SA(256, 4) PTQ_SA(512, 4) PTQ_SA(1024, 4) PTQ_SA(1024, 8)
+#undef PTQ_SA
+  return hipErrorInvalidValue;
+}
+
 template <int DT, bool HAS_S, int BITS>
 hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max_iter, double thr, float min_scale,
                     float* scale, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
@@ -260,6 +528,20 @@ hipError_t dispatch_bits(const void* w, int64_t N, int64_t K, const float* s, in
 }
 
 }  // namespace
+
+hipError_t launch_ssz_asym(const void* w, int dtype, int64_t N, int64_t K, const float* s, int max_iter,
+                           double threshold, float min_scale, float* scale, int32_t* zero_point, int8_t* wq,
+                           int32_t* iters, double* mse, hipStream_t stream) {
+  if (dtype == PTQ_BF16)
+    return s ? dispatch_asym<PTQ_BF16, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                             iters, mse, stream)
+             : dispatch_asym<PTQ_BF16, false>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                              iters, mse, stream);
+  return s ? dispatch_asym<PTQ_F32, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq, iters,
+                                          mse, stream)
+           : dispatch_asym<PTQ_F32, false>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq, iters,
+                                           mse, stream);
+}
 
 hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits, int max_iter,
                       double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,

@@ -87,3 +87,21 @@ def compare_ssz(g_scale, g_codes, g_iters, g_mse, ref, what, allow_scale_mismatc
         rel[ref["mse"] == 0] = np.abs(g_mse[ref["mse"] == 0])
         assert np.max(rel) <= MSE_RTOL, f"{what}: mse rel err {np.max(rel):.3e}"
     return n_diff
+
+
+def compare_ssz_asym(g_scale, g_zp, g_codes, g_iters, g_mse, ref, what, allow_scale_mismatch=0):
+    """Asymmetric SSZ parity: as compare_ssz, plus zero points equal on rows whose scale is identical."""
+    same = (g_scale == ref["S"]) & (g_zp == ref["Z"])
+    n_diff = int(np.sum(~same))
+    assert n_diff <= allow_scale_mismatch, f"{what}: {n_diff} rows with a different scale or zero point"
+    assert_scales(g_scale, ref["S"], what + " scale")
+    if g_iters is not None:
+        bad = np.nonzero((g_iters != ref["iters"]) & same)[0]
+        assert bad.size == 0, f"{what}: iteration counts differ on rows {bad[:10]}"
+    if g_codes is not None:
+        np.testing.assert_array_equal(g_codes[same], ref["q"][same], err_msg=what + " codes")
+    if g_mse is not None:
+        rel = np.abs(g_mse - ref["mse"]) / np.maximum(ref["mse"], 1e-300)
+        rel[ref["mse"] == 0] = np.abs(g_mse[ref["mse"] == 0])
+        assert np.max(rel) <= MSE_RTOL, f"{what}: mse rel err {np.max(rel):.3e}"
+    return n_diff

@@ -41,6 +41,7 @@ def lib():
     L.sq_absmax_calib.argtypes = [vp, ci, i64, i64, vp, ci, vp]
     L.sq_smooth_factors.argtypes = [vp, vp, i64, f32, vp, vp]
     L.ssz_weight_qparams.argtypes = [vp, ci, i64, i64, vp, ci, ci, ci, f64, f32, vp, vp, vp, vp, vp]
+    L.ssz_weight_qparams_asym.argtypes = [vp, ci, i64, i64, vp, ci, f64, f32, vp, vp, vp, vp, vp, vp]
     L.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
     L.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     L.ptq_last_error.restype = ctypes.c_char_p
@@ -61,7 +62,8 @@ def header_define(name):
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
-                          "sq_smooth_factors", "ssz_weight_qparams", "quant_per_token_i8", "w8a8_gemm_dequant"}
+                          "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
+                          "quant_per_token_i8", "w8a8_gemm_dequant"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.ptq_abi_version() == int(header_define("PTQ_ABI_VERSION"))
@@ -124,13 +126,35 @@ def test_ssz_errors(lib):
     _expect(lib, call(K=131072 + 16), SHAPE)
     _expect(lib, call(bits=2), UNSUP)
     _expect(lib, call(bits=16), UNSUP)
-    _expect(lib, call(sym=0), UNSUP, "symmetric")
+    _expect(lib, call(sym=0), UNSUP, "ssz_weight_qparams_asym")
     _expect(lib, call(it=-1), ARG)
     _expect(lib, call(it=21), ARG)
     _expect(lib, call(thr=-1.0), ARG)
     _expect(lib, call(thr=math.nan), ARG)
     _expect(lib, call(ms=0.0), ARG)
     _expect(lib, call(ms=-1e-5), ARG)
+    _expect(lib, call(w=MIS), ALIGN)
+    _expect(lib, call(s=MIS), ALIGN)
+    _expect(lib, call(wq=MIS), ALIGN)
+
+
+def test_ssz_asym_errors(lib):
+    c = lib.ssz_weight_qparams_asym
+
+    def call(w=P, dt=BF16, N=8, K=64, s=None, it=20, thr=1e-10, ms=1e-5, scale=P, zp=P, wq=P):
+        return c(w, dt, N, K, s, it, thr, ms, scale, zp, wq, None, None, None)
+
+    _expect(lib, call(w=None), NULL)
+    _expect(lib, call(scale=None), NULL)
+    _expect(lib, call(zp=None), NULL, "zero_point")
+    _expect(lib, call(dt=2), DTYPE)
+    _expect(lib, call(N=0), SHAPE)
+    _expect(lib, call(K=40), SHAPE)
+    _expect(lib, call(K=131072 + 16), SHAPE)
+    _expect(lib, call(it=-1), ARG)
+    _expect(lib, call(it=21), ARG)
+    _expect(lib, call(thr=math.inf), ARG)
+    _expect(lib, call(ms=0.0), ARG)
     _expect(lib, call(w=MIS), ALIGN)
     _expect(lib, call(s=MIS), ALIGN)
     _expect(lib, call(wq=MIS), ALIGN)

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import synth
-from parity_util import announce, assert_scales, assert_y, compare_ssz, dev, host, sample_rows, unpack_int4
+from parity_util import (announce, assert_scales, assert_y, compare_ssz, compare_ssz_asym, dev, host, sample_rows,
+                         unpack_int4)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +121,34 @@ def test_ssz_scale(pq, layer, bits):
         S, wq, it, mse = pq.ssz_weight_qparams(dev(w_host), None, bits=bits)
         codes = host(wq) if bits == 8 else unpack_int4(host(wq))
         compare_ssz(host(S)[rows], codes[rows], host(it)[rows], host(mse)[rows], ref, case.name)
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_ssz_scale_asym(pq, layer):
+    """Asymmetric int8 SSZ at full size on the 4 matrices of a layer (sampled rows on the oracle)."""
+    for case in synth.cases("ssz_scale")[4 * layer: 4 * layer + 4]:
+        w_host = case.w()
+        rows = sample_rows(case.N, 256, 19 + layer)
+        ref = oracle.ssz_asym(synth.widen(w_host)[rows], None)
+        announce(f"{case.name}: ssz_weight_qparams_asym N={case.N} K={case.K}")
+        S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w_host), None)
+        compare_ssz_asym(host(S)[rows], host(Z)[rows], host(wq)[rows], host(it)[rows], host(mse)[rows], ref,
+                         case.name + " asym")
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_opt67b_asym_weights(pq, idx):
+    """Asymmetric int8 SSZ of the smoothed hidden-4096 weights (alpha 0.5), sampled rows on the oracle."""
+    case = synth.cases("opt67b")[idx]
+    w_host = case.w()
+    w_f = synth.widen(w_host)
+    ax = None
+    for b in range(case.calib_batches):
+        ax = oracle.absmax_cols(synth.widen(case.x_batch(b)), ax)
+    s_ref = oracle.smooth_factors(ax, oracle.absmax_cols(w_f), 0.5)
+    rows = sample_rows(case.N, 256, 23 + idx)
+    ref = oracle.ssz_asym(w_f[rows], s_ref)
+    announce(f"{case.name}: ssz_weight_qparams_asym N={case.N} K={case.K} smoothed")
+    S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w_host), dev(s_ref))
+    compare_ssz_asym(host(S)[rows], host(Z)[rows], host(wq)[rows], host(it)[rows], host(mse)[rows], ref,
+                     case.name + " asym")

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import synth
-from parity_util import (announce, assert_scales, assert_y, compare_ssz, dev, host, unpack_int4)
+from parity_util import (announce, assert_scales, assert_y, compare_ssz, compare_ssz_asym, dev, host,
+                         unpack_int4)
 
 pytestmark = pytest.mark.gpu
 
@@ -141,6 +142,58 @@ def test_ssz_outputs_optional(pq):
     S, wq, it, mse = pq.ssz_weight_qparams(dev(w), None, bits=8, want_codes=False, want_stats=False)
     assert wq is None and it is None
     np.testing.assert_array_equal(host(S), ref["S"])
+
+
+# ------------------------------------------------------------------ asymmetric SSZ
+
+def _edge_rows_asym(K):
+    rows = np.zeros((6, K), dtype=np.float32)
+    k = (np.arange(K) % 256) - 128
+    rows[1] = (k - 37) * 2.0 ** -9      # exact grid with offset 37: lossless
+    rows[2, K // 3] = -0.37             # a single non-zero element
+    rows[3] = 0.5                       # constant: floor scale, saturated offset, nothing to fit
+    rows[4] = np.linspace(0.0, 1.0, K)  # one-sided: offset at the bottom of the range
+    rows[5] = -np.linspace(0.0, 1.0, K)
+    return rows
+
+
+@pytest.mark.parametrize("N,K,dtype,smooth,tail,shift", [
+    (128, 64, synth.F32, True, 0.0, 0.0), (300, 1040, synth.BF16, True, 0.001, 0.01),
+    (96, 4096, synth.BF16, False, 0.001, 0.0), (96, 4096, synth.F32, True, 0.0, 0.005),
+    (40, 16384, synth.BF16, True, 0.001, 0.0), (23, 8192, synth.BF16, False, 0.0, 0.02),
+    (17, 2064, synth.F32, False, 0.002, 0.0), (9, 16, synth.F32, False, 0.0, 0.0),
+    (6, 36864, synth.BF16, True, 0.001, 0.0)])
+def test_ssz_asym(pq, N, K, dtype, smooth, tail, shift):
+    w = _w(f"ssza/{N}x{K}", N, K, dtype, tail)
+    wf = synth.widen(w).copy()
+    if dtype == synth.F32:
+        wf[::2] += np.float32(shift)
+        wf[:6] = _edge_rows_asym(K)
+        w = wf
+    s = np.exp(np.random.default_rng(N * 3 + K).uniform(-1, 1, K)).astype(np.float32) if smooth else None
+    ref = oracle.ssz_asym(wf, s)
+    announce(f"ssz_weight_qparams_asym N={N} K={K} dtype={dtype} smooth={smooth}")
+    S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w), None if s is None else dev(s))
+    compare_ssz_asym(host(S), host(Z), host(wq), host(it), host(mse), ref, f"ssz asym {N}x{K}")
+
+
+@pytest.mark.parametrize("max_iter", [0, 1, 3])
+def test_ssz_asym_max_iter(pq, max_iter):
+    w = _w("ssza/iter", 64, 1024, synth.BF16, 0.001)
+    ref = oracle.ssz_asym(synth.widen(w), None, max_iter=max_iter)
+    announce(f"ssz_weight_qparams_asym max_iter={max_iter}")
+    S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w), None, max_iter=max_iter)
+    compare_ssz_asym(host(S), host(Z), host(wq), host(it), host(mse), ref, f"asym max_iter={max_iter}")
+
+
+def test_ssz_asym_scale_only(pq):
+    w = _w("ssza/opt", 32, 512, synth.BF16)
+    ref = oracle.ssz_asym(synth.widen(w), None)
+    announce("ssz_weight_qparams_asym scale and offset only")
+    S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w), None, want_codes=False, want_stats=False)
+    assert wq is None and it is None and mse is None
+    np.testing.assert_array_equal(host(S), ref["S"])
+    np.testing.assert_array_equal(host(Z), ref["Z"])
 
 
 # ------------------------------------------------------------------ GEMM + dequant
