@@ -119,9 +119,11 @@ __device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) 
   return e > 0.0 ? e : 0.0;
 }
 
-// WIDE_MODE 1 keeps an fp64 copy of the row in registers, saving one conversion per element and pass;
-// the default (0) widens on the fly: the row copy triples the register footprint, and the occupancy it
-// costs outweighs the conversion (measured 25-30% slower on 4096- and 16384-wide rows, int8 and int4).
+// WIDE_MODE 1 keeps an explicit fp64 copy of the row in registers.  The default (0) leaves the
+// widening to the compiler, which hoists it out of the pass loop: the same 6 VALU operations per
+// element and pass in about 2/3 of the registers (2 waves per SIMD instead of 1 on 4096- and
+// 16384-wide rows; measured 25-30% faster, int8 and int4).  Forcing the conversion into every pass
+// (3 waves per SIMD, 7 operations) measured 5% slower than the default.
 template <int DT, bool HAS_S, int BITS, int TPR, int CPT, int WIDE_MODE = 0>
 __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t N, int64_t K,
                                              const float* __restrict__ s, int max_iter, double thr, float min_scale,
