@@ -65,6 +65,10 @@ def _load():
             "o_mse_row_asym": [vp, vp, i64, f32, ci],
             "o_lsq_affine": [vp, vp, i64, vp, vp],
             "o_ssz_asym": [vp, vp, i64, i64, ci, f64, f32, vp, vp, vp, vp, vp, vp],
+            "o_epilogue": [vp, i64, i64, vp, vp, vp, ci, ci, vp, f32, vp],
+            "o_absmax_tensor": [vp, i64, i64, vp, ci, vp],
+            "o_ema_update": [vp, f32, f32, ci],
+            "o_quant_static": [vp, i64, i64, vp, ci, f32, vp],
             "o_pack_int4": [vp, i64, i64, vp],
             "o_quant_per_token": [vp, vp, i64, i64, vp, vp],
             "o_gemm_i8": [vp, vp, i64, i64, i64, vp],
@@ -79,6 +83,12 @@ def _load():
         lib.o_lsq_scale.restype = f64
         lib.o_mse_row.restype = f64
         lib.o_mse_row_asym.restype = f64
+        lib.o_bf16_rne.argtypes = [f32]
+        lib.o_bf16_rne.restype = ctypes.c_uint16
+        lib.o_act_static_scale.argtypes = [f32]
+        lib.o_act_static_scale.restype = f32
+        lib.o_weight_scale_per_tensor.argtypes = [f32, f32]
+        lib.o_weight_scale_per_tensor.restype = f32
         _lib = lib
     return _lib
 
@@ -296,3 +306,62 @@ def run_linear(x_calib, w, x_eval, alpha=0.5, smooth=True, bits=8, max_iter=20, 
             acc = gemm_i8(xq, q["q"])
             out.update(acc=acc, y=dequant(acc, d, q["S"]))
     return out
+
+
+# ---------------------------------------------------------------- epilogue fusion, static scales
+
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+OUT_F32, OUT_BF16, OUT_I8 = 0, 1, 2
+FOLD_NONE, FOLD_DIV, FOLD_MUL = 0, 1, 2
+
+
+def bf16_rne(f):
+    """fp32 -> bf16 bit pattern, round to nearest even."""
+    return int(_load().o_bf16_rne(float(np.float32(f))))
+
+
+def epilogue(acc, tok_scale, ch_scale, bias=None, act=ACT_NONE, out=OUT_F32, next_s=None, out_scale=1.0):
+    """Fused epilogue on int sums acc[M,N]: dequant, bias, activation, then fp32 / bf16 bits (uint16) / int8."""
+    acc = np.ascontiguousarray(acc, dtype=np.int64)
+    M, N = acc.shape
+    ts, cs = _f32(tok_scale), _f32(ch_scale)
+    b = None if bias is None else _f32(bias)
+    ns = None if next_s is None else _f32(next_s)
+    dt = {OUT_F32: np.float32, OUT_BF16: np.uint16, OUT_I8: np.int8}[out]
+    y = np.empty((M, N), dtype=dt)
+    _check(_load().o_epilogue(acc.ctypes.data, M, N, ts.ctypes.data, cs.ctypes.data, _p(b), int(act), int(out),
+                              _p(ns), float(out_scale), y.ctypes.data), "epilogue")
+    return y
+
+
+def absmax_tensor(x, s=None, fold=FOLD_NONE):
+    x = _f32(x)
+    s = None if s is None else _f32(s)
+    a = np.zeros(1, dtype=np.float32)
+    _check(_load().o_absmax_tensor(x.ctypes.data, x.shape[0], x.shape[1], _p(s), int(fold), a.ctypes.data),
+           "absmax_tensor")
+    return np.float32(a[0])
+
+
+def ema_update(state, a, momentum, first):
+    st = np.array([state if state is not None else 0.0], dtype=np.float32)
+    _check(_load().o_ema_update(st.ctypes.data, float(np.float32(a)), float(np.float32(momentum)), int(bool(first))),
+           "ema_update")
+    return np.float32(st[0])
+
+
+def act_static_scale(state):
+    return np.float32(_load().o_act_static_scale(float(np.float32(state))))
+
+
+def weight_scale_per_tensor(amax, min_scale=1e-5):
+    return np.float32(_load().o_weight_scale_per_tensor(float(np.float32(amax)), float(np.float32(min_scale))))
+
+
+def quant_static(x, S, s=None, fold=FOLD_NONE):
+    x = _f32(x)
+    s = None if s is None else _f32(s)
+    q = np.empty(x.shape, dtype=np.int8)
+    _check(_load().o_quant_static(x.ctypes.data, x.shape[0], x.shape[1], _p(s), int(fold), float(np.float32(S)),
+                                  q.ctypes.data), "quant_static")
+    return q

@@ -557,3 +557,145 @@ int o_dequant(const int64_t* acc, const float* delta, const float* S, int64_t M,
     for (int64_t n = 0; n < N; ++n) y[t * N + n] = (double)acc[t * N + n] * (double)delta[t] * (double)S[n];
   return O_OK;
 }
+
+/* ===========================================================================
+ * Epilogue fusion ([INT8] 4.2: quantize -> op -> dequantize -> activation in
+ * one kernel) and the output formats the next layer consumes.
+ *
+ * Readings (the pages give the fused chain, not its arithmetic):
+ *   - the epilogue works in fp32, in this order, each operation rounded:
+ *       v = fl32(fl32(acc) * fl32(tok_scale[t] * ch_scale[n]))   (the dequant)
+ *       v = fl32(v + bias[n])                                     (optional bias)
+ *       relu: v > 0 ? v : +0;   gelu: fl32(0.5 v (1 + erf(v / sqrt 2))) (fp32 erff)
+ *   - output f32: v;  bf16: v rounded to nearest-even bf16;  int8: the next
+ *     layer's static per-tensor quantization of v, with its smoothing fold
+ *     x_hat = fl32(v * fl32(1/next_s[n])) when next_s is given, then
+ *     clamp(rne(fl32(x_hat * fl32(1/out_scale))), -127, 127).
+ *   - the q_sigmoid snippet of [INT8] 3.3 is an integer sigmoid for a
+ *     convolutional network; the linear layers here use ReLU (OPT) or GELU
+ *     (GPT) instead.
+ * ========================================================================= */
+#define O_ACT_NONE 0
+#define O_ACT_RELU 1
+#define O_ACT_GELU 2
+#define O_OUT_F32 0
+#define O_OUT_BF16 1
+#define O_OUT_I8 2
+
+/* float -> bf16 bits, round to nearest, ties to even (finite inputs) */
+uint16_t o_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+static float o_gelu32(float v) {
+  const float c = 0.70710678118654752440f; /* fl32(1/sqrt(2)) */
+  float e = erff(v * c);
+  float h = 0.5f * v;
+  return h * (1.0f + e);
+}
+
+int o_epilogue(const int64_t* acc, int64_t M, int64_t N, const float* tok_scale, const float* ch_scale,
+               const float* bias, int act, int out_type, const float* next_s, float out_scale, void* out) {
+  if (!acc || !tok_scale || !ch_scale || !out || M < 0 || N < 0) return O_EARG;
+  if (act < O_ACT_NONE || act > O_ACT_GELU || out_type < O_OUT_F32 || out_type > O_OUT_I8) return O_EARG;
+  if (out_type == O_OUT_I8 && !(out_scale > 0.0f)) return O_EARG;
+  const float inv_out = out_type == O_OUT_I8 ? 1.0f / out_scale : 0.0f;
+  for (int64_t t = 0; t < M; ++t) {
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t a = acc[t * N + n];
+      if (a > INT32_MAX || a < INT32_MIN) return O_EOVERFLOW;
+      float sc = tok_scale[t] * ch_scale[n];
+      float v = (float)a * sc;
+      if (bias) v = v + bias[n];
+      if (act == O_ACT_RELU) v = v > 0.0f ? v : 0.0f;
+      else if (act == O_ACT_GELU) v = o_gelu32(v);
+      if (out_type == O_OUT_F32) {
+        ((float*)out)[t * N + n] = v;
+      } else if (out_type == O_OUT_BF16) {
+        ((uint16_t*)out)[t * N + n] = o_bf16_rne(v);
+      } else {
+        float xh = next_s ? v * (1.0f / next_s[n]) : v;
+        ((int8_t*)out)[t * N + n] = (int8_t)code_of(xh, inv_out, 127);
+      }
+    }
+  }
+  return O_OK;
+}
+
+/* ===========================================================================
+ * Static (calibrated) per-tensor scales: the moving-average absmax of the
+ * activations ([INT8] 2.1 tip: a moving average of the range is more robust
+ * than the raw min/max; [QAT] 六: activation_quantize_type
+ * moving_average_abs_max) and the per-tensor (per-layer) weight scale ([PTQ]
+ * 逐层量化: one scale for the whole tensor).
+ *
+ * Readings:
+ *   - the tracked range is per tensor: a = max over the batch of |x_hat|,
+ *     x_hat the smoothed activation fl32(x * fl32(1/s_j)) (s may be NULL);
+ *   - moving average: the first batch sets the state, later batches update
+ *     state = fl32(fl32(m * state) + fl32(fl32(1 - m) * a)) with momentum m in
+ *     [0, 1) -- the pages give no momentum; it is a labelled parameter
+ *     (0.9 in the tests and the bench);
+ *   - static activation scale = state > 0 ? fl32(state / 127) : 1;
+ *   - per-tensor weight scale = max(fl32(max|w_hat| / 127), fl32(min_scale)),
+ *     w_hat = fl32(w * s_j) (the MinMax rule of the per-channel path on the
+ *     whole tensor; the SSZ search itself is per-channel only, [SSZ] 使用限制).
+ * Both are computed from column maxima: for a positive constant r and RNE,
+ * max_t |fl32(x_tj * r)| = fl32(max_t |x_tj| * r) (rounding is monotone).
+ * ========================================================================= */
+#define O_FOLD_NONE 0
+#define O_FOLD_DIV 1 /* activation side: x * fl32(1/s_j) */
+#define O_FOLD_MUL 2 /* weight side: w * s_j */
+
+static float fold_one(float x, const float* s, int64_t j, int fold) {
+  if (!s || fold == O_FOLD_NONE) return x;
+  return fold == O_FOLD_DIV ? x * (1.0f / s[j]) : x * s[j];
+}
+
+/* max over the whole [rows, cols] tensor of |fold(x)| (element by element, no shortcut) */
+int o_absmax_tensor(const float* x, int64_t rows, int64_t cols, const float* s, int fold, float* amax) {
+  if (!x || !amax || rows < 0 || cols <= 0 || fold < O_FOLD_NONE || fold > O_FOLD_MUL) return O_EARG;
+  if (!all_finite(x, rows * cols)) return O_ENONFINITE;
+  float m = 0.0f;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j) {
+      float v = fabsf(fold_one(x[r * cols + j], s, j, fold));
+      if (v > m) m = v;
+    }
+  *amax = m;
+  return O_OK;
+}
+
+int o_ema_update(float* state, float a, float momentum, int first) {
+  if (!state || !(momentum >= 0.0f && momentum < 1.0f) || !(a >= 0.0f)) return O_EARG;
+  if (first) {
+    *state = a;
+  } else {
+    float t1 = momentum * *state;
+    float w = 1.0f - momentum;
+    float t2 = w * a;
+    *state = t1 + t2;
+  }
+  return O_OK;
+}
+
+float o_act_static_scale(float state) { return state > 0.0f ? state / 127.0f : 1.0f; }
+
+float o_weight_scale_per_tensor(float amax, float min_scale) {
+  float S = amax / 127.0f;
+  return S < min_scale ? min_scale : S;
+}
+
+/* codes of a whole tensor with one static scale S: clamp(rne(fl32(fold(x) * fl32(1/S))), -127, 127) */
+int o_quant_static(const float* x, int64_t rows, int64_t cols, const float* s, int fold, float S, int8_t* q) {
+  if (!x || !q || rows < 0 || cols <= 0 || !(S > 0.0f) || fold < O_FOLD_NONE || fold > O_FOLD_MUL) return O_EARG;
+  if (!all_finite(x, rows * cols)) return O_ENONFINITE;
+  float inv = 1.0f / S;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j) q[r * cols + j] = (int8_t)code_of(fold_one(x[r * cols + j], s, j, fold), inv, 127);
+  return O_OK;
+}
