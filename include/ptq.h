@@ -10,6 +10,7 @@
  *   ssz_weight_qparams_asym   the same with a per-channel offset (int8)
  *   quant_per_token_i8   per-token int8 activation quantization (with X/s)
  *   w8a8_gemm_dequant    int8 x int8 -> int32 GEMM, fused dequantization
+ *   w8a8_gemm_fused      the same with bias, activation and fp32/bf16/int8 output
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (hipMalloc'd or equivalent), owned by the
@@ -73,6 +74,9 @@ extern "C" {
 
 /* Every K must be a multiple of this (16-byte vector rows, [INT8] 3.1). */
 #define PTQ_K_MULTIPLE 16
+
+typedef enum { PTQ_ACT_NONE = 0, PTQ_ACT_RELU = 1, PTQ_ACT_GELU = 2 } ptq_act;
+typedef enum { PTQ_OUT_F32 = 0, PTQ_OUT_BF16 = 1, PTQ_OUT_I8 = 2 } ptq_out;
 
 typedef enum {
   PTQ_OK = 0,
@@ -232,6 +236,37 @@ PTQ_API ptq_status quant_per_token_i8(const void* x, int dtype, int64_t T, int64
  */
 PTQ_API ptq_status w8a8_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
                              int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, void* stream);
+
+/*
+ * The GEMM of w8a8_gemm_dequant with a fused epilogue: bias, activation and
+ * the output format the next layer consumes.  [INT8] 4.2 (quantize -> op ->
+ * dequantize -> activation fused into one kernel), [INT8] 2.1 (the int8
+ * output's quantization and saturation), [SQ] (the next layer's fold).
+ *
+ * In fp32, each operation rounded, for every output element (t, n):
+ *   v = fl32(acc) * fl32(tok_scale[t] * ch_scale[n])      (as w8a8_gemm_dequant)
+ *   v = v + bias[n]                                       (bias may be NULL)
+ *   act PTQ_ACT_RELU: v = v > 0 ? v : +0
+ *       PTQ_ACT_GELU: v = 0.5 v (1 + erf(v / sqrt 2))     (device erff)
+ *   out_type PTQ_OUT_F32:  out[t,n] = v                     float  [M, N]
+ *            PTQ_OUT_BF16: out[t,n] = bf16 RNE of v         uint16 [M, N]
+ *            PTQ_OUT_I8:   x = next_s ? fl32(v * fl32(1/next_s[n])) : v;
+ *                          out[t,n] = clamp(rne(fl32(x * fl32(1/out_scale[0]))), -127, 127)   int8 [M, N]
+ *              -- the next layer's static per-tensor activation quantization
+ *              (see sq_act_scale_ema) with its smoothing fold; its token
+ *              scales are then out_scale[0] for every row.
+ *
+ *   bias       [N] fp32 or NULL
+ *   act        PTQ_ACT_NONE / RELU / GELU (else PTQ_ERR_UNSUPPORTED)
+ *   out_type   PTQ_OUT_F32 / BF16 / I8 (else PTQ_ERR_DTYPE)
+ *   next_s     [N] fp32 or NULL; int8 output only (else PTQ_ERR_ARG)
+ *   out_scale  [1] fp32 device scalar > 0, required for the int8 output only
+ *   out        16-B aligned;  acc as in w8a8_gemm_dequant (may be NULL)
+ */
+PTQ_API ptq_status w8a8_gemm_fused(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
+                                   const float* bias, int act, int out_type, const float* next_s,
+                                   const float* out_scale, int64_t M, int64_t N, int64_t K, void* out, int32_t* acc,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

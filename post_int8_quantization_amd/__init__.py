@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   ssz_weight_qparams(w, s=None, bits=8, ...) -> (scale[N], wq, iters[N], mse[N])
   quant_per_token_i8(x, s=None) -> (xq[T,K] int8, tok_scale[T] fp32)
   w8a8_gemm_dequant(xq, wq, tok_scale, ch_scale, want_acc=False) -> y[M,N] fp32 (, acc int32)
+  w8a8_gemm_fused(xq, wq, tok_scale, ch_scale, bias=None, act="none", out="f32", next_s=None,
+                  out_scale=None) -> out[M,N] fp32 / bf16 / int8
 """
 from __future__ import annotations
 
@@ -33,7 +35,8 @@ STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE"
           5: "PTQ_ERR_ARG", 6: "PTQ_ERR_ALIGN", 7: "PTQ_ERR_HIP"}
 
 EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
-           "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant")
+           "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant",
+           "w8a8_gemm_fused")
 
 
 class PtqError(RuntimeError):
@@ -59,8 +62,9 @@ def _load():
     lib.ssz_weight_qparams_asym.argtypes = [vp, ci, i64, i64, vp, ci, f64, f32, vp, vp, vp, vp, vp, vp]
     lib.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
     lib.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.w8a8_gemm_fused.argtypes = [vp, vp, vp, vp, vp, ci, ci, vp, vp, i64, i64, i64, vp, vp, vp]
     for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
-               "quant_per_token_i8", "w8a8_gemm_dequant"):
+               "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused"):
         getattr(lib, fn).restype = ci
     return lib
 
@@ -209,4 +213,32 @@ def w8a8_gemm_dequant(xq, wq, tok_scale, ch_scale, want_acc=False, y=None, strea
     acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
     _check(lib.w8a8_gemm_dequant(_ptr(xq), _ptr(wq), _ptr(tok_scale), _ptr(ch_scale), M, N, K, _ptr(y), _ptr(acc),
                                  _stream(stream)))
+    return (y, acc) if want_acc else y
+
+
+ACT = {"none": 0, "relu": 1, "gelu": 2}
+OUT = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16), "i8": (2, torch.int8)}
+
+
+def w8a8_gemm_fused(xq, wq, tok_scale, ch_scale, bias=None, act="none", out="f32", next_s=None, out_scale=None,
+                    want_acc=False, y=None, stream=None):
+    """GEMM + dequant + bias + activation, output fp32, bf16 or int8 (the next layer's static quantization:
+    next_s [N] its smoothing factors or None, out_scale a 1-element device tensor, its static scale)."""
+    _dev(xq, "xq", (torch.int8,))
+    _dev(wq, "wq", (torch.int8,))
+    _dev(tok_scale, "tok_scale", (torch.float32,))
+    _dev(ch_scale, "ch_scale", (torch.float32,))
+    for t, nm in ((bias, "bias"), (next_s, "next_s"), (out_scale, "out_scale")):
+        if t is not None:
+            _dev(t, nm, (torch.float32,))
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K:
+        raise ValueError("xq and wq differ in K")
+    code, dt = OUT[out]
+    if y is None:
+        y = torch.empty((M, N), dtype=dt, device=xq.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
+    _check(lib.w8a8_gemm_fused(_ptr(xq), _ptr(wq), _ptr(tok_scale), _ptr(ch_scale), _ptr(bias), ACT[act], code,
+                               _ptr(next_s), _ptr(out_scale), M, N, K, _ptr(y), _ptr(acc), _stream(stream)))
     return (y, acc) if want_acc else y

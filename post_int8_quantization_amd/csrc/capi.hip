@@ -162,4 +162,31 @@ ptq_status w8a8_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* to
   return from_hip(ptq::launch_gemm_dequant(xq, wq, tok_scale, ch_scale, M, N, K, y, acc, (hipStream_t)stream), fn);
 }
 
+ptq_status w8a8_gemm_fused(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
+                           const float* bias, int act, int out_type, const float* next_s, const float* out_scale,
+                           int64_t M, int64_t N, int64_t K, void* out, int32_t* acc, void* stream) {
+  const char* fn = "w8a8_gemm_fused";
+  if (!xq || !wq || !tok_scale || !ch_scale || !out)
+    return fail(PTQ_ERR_NULL, "%s: xq, wq, tok_scale, ch_scale and out are required", fn);
+  if (act != PTQ_ACT_NONE && act != PTQ_ACT_RELU && act != PTQ_ACT_GELU)
+    return fail(PTQ_ERR_UNSUPPORTED, "%s: act=%d (none, relu and gelu are supported)", fn, act);
+  if (out_type != PTQ_OUT_F32 && out_type != PTQ_OUT_BF16 && out_type != PTQ_OUT_I8)
+    return fail(PTQ_ERR_DTYPE, "%s: out_type=%d unknown", fn, out_type);
+  if (out_type == PTQ_OUT_I8 && !out_scale)
+    return fail(PTQ_ERR_NULL, "%s: the int8 output needs out_scale", fn);
+  if (out_type != PTQ_OUT_I8 && (next_s || out_scale))
+    return fail(PTQ_ERR_ARG, "%s: next_s and out_scale apply to the int8 output only", fn);
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(PTQ_ERR_SHAPE, "%s: M=%lld N=%lld K=%lld must be >= 1", fn, (long long)M, (long long)N, (long long)K);
+  if (K % PTQ_K_MULTIPLE) return fail(PTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+  if (K > PTQ_GEMM_MAX_K)
+    return fail(PTQ_ERR_SHAPE, "%s: K=%lld exceeds %d, int32 sums could overflow", fn, (long long)K, PTQ_GEMM_MAX_K);
+  if (M > 0x7fffffff || N > 0x7fffffff) return fail(PTQ_ERR_SHAPE, "%s: M or N too large", fn);
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) || (acc && !aligned16(acc)))
+    return fail(PTQ_ERR_ALIGN, "%s: xq, wq, out and acc must be 16-byte aligned", fn);
+  return from_hip(ptq::launch_gemm_fused(xq, wq, tok_scale, ch_scale, bias, act, out_type, next_s, out_scale, M, N, K,
+                                         out, acc, (hipStream_t)stream),
+                  fn);
+}
+
 }  // extern "C"

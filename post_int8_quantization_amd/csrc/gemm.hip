@@ -112,11 +112,63 @@ __device__ __forceinline__ void dma16_lds(const void* g, uint32_t lds_byte_addr)
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, bool PERSIST, int OCC, bool NTS = true>
+// ---------------------------------------------------------------------------
+// Fused epilogue ([INT8] 4.2: dequantize and activate inside the GEMM).  In fp32, each operation
+// rounded: v = fl32(acc) * fl32(ts[t] * cs[n]);  v += bias[n];  relu (v > 0 ? v : +0) or gelu
+// (0.5 v (1 + erf(v / sqrt 2)));  then one of three outputs: fp32; bf16 (round to nearest even);
+// int8 for the next layer: clamp(rne(fl32(fl32(v * fl32(1/next_s[n])) * fl32(1/out_scale))), -127, 127),
+// its static per-tensor quantization with its smoothing fold.
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_I8 = 2 };
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
+
+struct Epi {
+  const float* bias;       // [N] or null
+  const float* next_s;     // [N] or null (int8 output)
+  const float* out_scale;  // [1] (int8 output)
+  int act;
+};
+
+__device__ __forceinline__ float epi_act(float v, int act) {
+  if (act == ACT_RELU) return v > 0.0f ? v : 0.0f;
+  if (act == ACT_GELU) {
+    const float e = erff(v * 0.70710678118654752440f);
+    const float h = 0.5f * v;
+    return h * (1.0f + e);
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent)
+template <int OUT, bool NTS>
+__device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
+                                          float inv_out, const Epi& epi) {
+  if (epi.bias) v = v + bn;
+  v = epi_act(v, epi.act);
+  if constexpr (OUT == EPI_F32) {
+    float* y = reinterpret_cast<float*>(Y) + idx;
+    if constexpr (NTS) __builtin_nontemporal_store(v, y);  // written once, not re-read
+    else *y = v;
+  } else if constexpr (OUT == EPI_BF16) {
+    reinterpret_cast<uint16_t*>(Y)[idx] = bf16_rne(v);
+  } else {
+    const float xh = epi.next_s ? v * nrn : v;
+    reinterpret_cast<int8_t*>(Y)[idx] = (int8_t)(int)code_f(xh, inv_out, 127.0f);
+  }
+}
+
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, bool PERSIST, int OCC, bool NTS = true,
+          int OUT = EPI_F32>
 __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           const float* __restrict__ ts, const float* __restrict__ cs,
-                                                          int M, int N, int K, float* __restrict__ Y,
-                                                          int32_t* __restrict__ ACC, int tiles_m, int tiles_n) {
+                                                          int M, int N, int K, void* __restrict__ Y,
+                                                          int32_t* __restrict__ ACC, int tiles_m, int tiles_n,
+                                                          Epi epi) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / MF, FN = TN / MF;
@@ -133,6 +185,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
   __shared__ uint4 sm[ST * S_CH];
   __shared__ __attribute__((aligned(16))) float s_ts[BM];  // the tile's token scales
   __shared__ float s_cs[BN];                               // and channel scales
+  __shared__ float s_b[BN];                                // and bias (epilogue fusion)
+  __shared__ float s_nr[BN];                               // and 1/next_s (int8 output)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,7 +203,12 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   __syncthreads();  // the previous tile's epilogue and last K steps are done with LDS
   for (int t = tid; t < BM; t += NW * 64) s_ts[t] = m0 + t < M ? ts[m0 + t] : 0.0f;
-  for (int t = tid; t < BN; t += NW * 64) s_cs[t] = n0 + t < N ? cs[n0 + t] : 0.0f;
+  for (int t = tid; t < BN; t += NW * 64) {
+    const bool in = n0 + t < N;
+    s_cs[t] = in ? cs[n0 + t] : 0.0f;
+    s_b[t] = (in && epi.bias) ? epi.bias[n0 + t] : 0.0f;
+    if constexpr (OUT == EPI_I8) s_nr[t] = (in && epi.next_s) ? 1.0f / epi.next_s[n0 + t] : 1.0f;
+  }
   __syncthreads();
 
   // per-lane source rows/chunks of the loads (the LDS slot is fixed by lane order and the swizzle)
@@ -257,12 +316,15 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
   // consecutive rows (16x16: rows 4*(lane/16)+0..3; 32x32: rows 8*g + 4*(lane/32) + 0..3, g = 0..3),
   // so the token scales of a group are one 16-byte LDS read.
   const bool full = m0 + BM <= M && n0 + BN <= N;
+  const float inv_out = OUT == EPI_I8 ? 1.0f / epi.out_scale[0] : 0.0f;
   constexpr int NG = NR / 4;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
     const int n = n0 + cl;
     const float csn = s_cs[cl];
+    const float bn = s_b[cl];
+    const float nrn = OUT == EPI_I8 ? s_nr[cl] : 1.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -275,9 +337,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
           const int m = m0 + rl0 + q;
           const int a = acc[i][j][g * 4 + q];
           if (full || (m < M && n < N)) {
-            const float yv = (float)a * (tsv[q] * csn);
-            if constexpr (NTS) __builtin_nontemporal_store(yv, &Y[(int64_t)m * N + n]);  // written once, not re-read
-            else Y[(int64_t)m * N + n] = yv;
+            epi_store<OUT, NTS>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
             if (ACC) ACC[(int64_t)m * N + n] = a;
           }
         }
@@ -367,11 +427,11 @@ __device__ __forceinline__ void mma_slab(const Slab<MT, NT>& r, uint4* ws, v4i (
 
 // M <= 16*MT tokens; a block of KS waves owns 16*NT output channels; wave w takes slabs w, w+KS, ...
 // PF: the next slab's loads are issued before the current slab's transpose and MFMAs.
-template <int MT, int NT, int KS, bool PF>
+template <int MT, int NT, int KS, bool PF, int OUT = EPI_F32>
 __global__ __launch_bounds__(KS * 64) void k_gemm_dec(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                      const float* __restrict__ ts, const float* __restrict__ cs,
-                                                     int M, int N, int K, float* __restrict__ Y,
-                                                     int32_t* __restrict__ ACC) {
+                                                     int M, int N, int K, void* __restrict__ Y,
+                                                     int32_t* __restrict__ ACC, Epi epi) {
   constexpr int WAVE_CH = (NT + MT) * 128;
   static_assert(MT * NT * 64 <= WAVE_CH, "the partials fit in the slab area");
   __shared__ uint4 sm[KS * WAVE_CH];
@@ -424,11 +484,14 @@ __global__ __launch_bounds__(KS * 64) void k_gemm_dec(const int8_t* __restrict__
     const int n = n0 + u * 16 + mrow;
     if (n < N) {
       const float csn = cs[n];
+      const float bn = epi.bias ? epi.bias[n] : 0.0f;
+      const float nrn = (OUT == EPI_I8 && epi.next_s) ? 1.0f / epi.next_s[n] : 1.0f;
+      const float inv_out = OUT == EPI_I8 ? 1.0f / epi.out_scale[0] : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = t * 16 + mg * 4 + r;
         if (m < M) {
-          Y[(int64_t)m * N + n] = (float)s[r] * (ts[m] * csn);
+          epi_store<OUT, false>(Y, (int64_t)m * N + n, (float)s[r] * (ts[m] * csn), bn, nrn, inv_out, epi);
           if (ACC) ACC[(int64_t)m * N + n] = s[r];
         }
       }
@@ -436,43 +499,57 @@ __global__ __launch_bounds__(KS * 64) void k_gemm_dec(const int8_t* __restrict__
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int MF>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, int OUT>
 hipError_t launch_tiled(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
-                        float* y, int32_t* acc, hipStream_t stream) {
+                        void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  k_gemm_pipe<BM, BN, BK, WM, WN, ST, 4, MF, false, 1><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
-      xq, wq, ts, cs, M, N, K, y, acc, tm, tn);
+  k_gemm_pipe<BM, BN, BK, WM, WN, ST, 4, MF, false, 1, true, OUT><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
+      xq, wq, ts, cs, M, N, K, y, acc, tm, tn, epi);
   return hipGetLastError();
 }
 
-template <int MT, int NT, int KS, bool PF>
+template <int MT, int NT, int KS, bool PF, int OUT>
 hipError_t launch_dec(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
-                      float* y, int32_t* acc, hipStream_t stream) {
+                      void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
   const int blocks = (N + 16 * NT - 1) / (16 * NT);
-  k_gemm_dec<MT, NT, KS, PF><<<(unsigned)blocks, KS * 64, 0, stream>>>(xq, wq, ts, cs, M, N, K, y, acc);
+  k_gemm_dec<MT, NT, KS, PF, OUT><<<(unsigned)blocks, KS * 64, 0, stream>>>(xq, wq, ts, cs, M, N, K, y, acc, epi);
   return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t dispatch_gemm(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int64_t M, int64_t N,
+                         int64_t K, void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (M <= 16) return launch_dec<1, 1, 8, false, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  if (M <= 32) return launch_dec<2, 1, 8, false, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  if (M <= 64) {
+    // 64 channels per block re-read the token rows 4x less often, once that still fills the CUs
+    if ((N + 63) / 64 >= 256) return launch_dec<4, 4, 4, false, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+    return launch_dec<4, 2, 8, true, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  }
+  // the largest tile that still gives about one tile per CU (256 CUs)
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 200) return launch_tiled<256, 256, 128, 2, 4, 2, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  // smaller tiles: three 48 KB stages in flight instead of two 64 KB ones
+  if (M >= N) return launch_tiled<256, 128, 128, 4, 2, 3, 32, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  return launch_tiled<128, 256, 128, 2, 4, 3, 32, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
                                int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, hipStream_t stream) {
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (M <= 16) return launch_dec<1, 1, 8, false>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  if (M <= 32) return launch_dec<2, 1, 8, false>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  if (M <= 64) {
-    // 64 channels per block re-read the token rows 4x less often, once that still fills the CUs
-    if ((N + 63) / 64 >= 256) return launch_dec<4, 4, 4, false>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-    return launch_dec<4, 2, 8, true>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  }
-  // the largest tile that still gives about one tile per CU (256 CUs)
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 200)
-    return launch_tiled<256, 256, 128, 2, 4, 2, 16>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  // smaller tiles: three 48 KB stages in flight instead of two 64 KB ones
-  if (M >= N)
-    return launch_tiled<256, 128, 128, 4, 2, 3, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
-  return launch_tiled<128, 256, 128, 2, 4, 3, 32>(xq, wq, tok_scale, ch_scale, m, n, k, y, acc, stream);
+  const Epi epi{nullptr, nullptr, nullptr, ACT_NONE};
+  return dispatch_gemm<EPI_F32>(xq, wq, tok_scale, ch_scale, M, N, K, y, acc, epi, stream);
+}
+
+hipError_t launch_gemm_fused(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
+                             const float* bias, int act, int out_type, const float* next_s, const float* out_scale,
+                             int64_t M, int64_t N, int64_t K, void* out, int32_t* acc, hipStream_t stream) {
+  const Epi epi{bias, next_s, out_scale, act};
+  if (out_type == EPI_BF16) return dispatch_gemm<EPI_BF16>(xq, wq, tok_scale, ch_scale, M, N, K, out, acc, epi, stream);
+  if (out_type == EPI_I8) return dispatch_gemm<EPI_I8>(xq, wq, tok_scale, ch_scale, M, N, K, out, acc, epi, stream);
+  return dispatch_gemm<EPI_F32>(xq, wq, tok_scale, ch_scale, M, N, K, out, acc, epi, stream);
 }
 
 }  // namespace ptq

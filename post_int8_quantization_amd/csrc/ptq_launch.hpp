@@ -31,6 +31,11 @@ hipError_t launch_ssz_asym(const void* w, int dtype, int64_t N, int64_t K, const
 hipError_t launch_gemm_dequant(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
                                int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, hipStream_t stream);
 
+// act: 0 none, 1 relu, 2 gelu;  out_type: 0 fp32, 1 bf16, 2 int8
+hipError_t launch_gemm_fused(const int8_t* xq, const int8_t* wq, const float* tok_scale, const float* ch_scale,
+                             const float* bias, int act, int out_type, const float* next_s, const float* out_scale,
+                             int64_t M, int64_t N, int64_t K, void* out, int32_t* acc, hipStream_t stream);
+
 // Largest K the row-resident kernels (per-token quantization, SSZ) accept.
 constexpr int64_t kMaxRowK = 131072;
 

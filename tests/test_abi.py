@@ -44,6 +44,7 @@ def lib():
     L.ssz_weight_qparams_asym.argtypes = [vp, ci, i64, i64, vp, ci, f64, f32, vp, vp, vp, vp, vp, vp]
     L.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
     L.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    L.w8a8_gemm_fused.argtypes = [vp, vp, vp, vp, vp, ci, ci, vp, vp, i64, i64, i64, vp, vp, vp]
     L.ptq_last_error.restype = ctypes.c_char_p
     L.ptq_status_string.restype = ctypes.c_char_p
     return L
@@ -63,7 +64,7 @@ def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
                           "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
-                          "quant_per_token_i8", "w8a8_gemm_dequant"}
+                          "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.ptq_abi_version() == int(header_define("PTQ_ABI_VERSION"))
@@ -185,6 +186,26 @@ def test_gemm_errors(lib):
     _expect(lib, c(MIS, P, P, P, 4, 4, 64, P, None, None), ALIGN)
     _expect(lib, c(P, P, P, P, 4, 4, 64, MIS, None, None), ALIGN)
     _expect(lib, c(P, P, P, P, 4, 4, 64, P, MIS, None), ALIGN)
+
+
+def test_gemm_fused_errors(lib):
+    c = lib.w8a8_gemm_fused
+
+    def call(xq=P, act=0, out=0, ns=None, osc=None, M=4, N=4, K=64, y=P, acc=None, bias=None):
+        return c(xq, P, P, P, bias, act, out, ns, osc, M, N, K, y, acc, None)
+
+    _expect(lib, call(xq=None), NULL)
+    _expect(lib, call(y=None), NULL)
+    _expect(lib, call(act=3), UNSUP, "act")
+    _expect(lib, call(out=3), DTYPE, "out_type")
+    _expect(lib, call(out=2), NULL, "out_scale")
+    _expect(lib, call(out=0, osc=P), ARG, "int8 output only")
+    _expect(lib, call(out=1, ns=P), ARG, "int8 output only")
+    _expect(lib, call(M=0), SHAPE)
+    _expect(lib, call(K=40), SHAPE)
+    _expect(lib, call(K=133152), SHAPE, "overflow")
+    _expect(lib, call(xq=MIS), ALIGN)
+    _expect(lib, call(out=2, osc=P, y=MIS), ALIGN)
 
 
 def test_binding_rejects_host_tensors():

@@ -247,3 +247,52 @@ def test_gemm_deterministic(pq):
     y1 = pq.w8a8_gemm_dequant(a, b, ts, cs)
     y2 = pq.w8a8_gemm_dequant(a, b, ts, cs)
     assert torch.equal(y1, y2)
+
+
+# ------------------------------------------------------------------ fused epilogue
+
+@pytest.mark.parametrize("M,N,K", [(16, 1000, 8192), (5, 77, 160), (64, 300, 4096), (300, 520, 1040),
+                                   (257, 259, 4096), (1024, 1024, 4096)])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "i8"])
+def test_gemm_fused(pq, M, N, K, act, out):
+    rng = np.random.default_rng(M * 11 + N * 5 + K + len(act) + len(out))
+    a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    ts = rng.uniform(0.002, 0.02, M).astype(np.float32)
+    cs = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    bias = rng.normal(0, 0.5, N).astype(np.float32) if (M + N) % 2 else None
+    ns = np.exp(rng.uniform(-1, 1, N)).astype(np.float32) if out == "i8" and M % 2 == 0 else None
+    acc_ref = oracle.gemm_i8(a, b)
+    code = {"f32": oracle.OUT_F32, "bf16": oracle.OUT_BF16, "i8": oracle.OUT_I8}[out]
+    # a static output scale near the output range, so that the int8 codes use the whole range
+    y32 = oracle.epilogue(acc_ref, ts, cs, bias, oracle.ACT_RELU if act == "relu" else oracle.ACT_NONE)
+    osc = np.float32(np.max(np.abs(y32)) / 100.0) if out == "i8" else 1.0
+    ref = oracle.epilogue(acc_ref, ts, cs, bias, {"none": 0, "relu": 1, "gelu": 2}[act], code, ns, osc)
+    announce(f"w8a8_gemm_fused M={M} N={N} K={K} act={act} out={out} bias={bias is not None} "
+             f"next_s={ns is not None}")
+    y, acc = pq.w8a8_gemm_fused(dev(a), dev(b), dev(ts), dev(cs), None if bias is None else dev(bias), act, out,
+                                None if ns is None else dev(ns),
+                                dev(np.array([osc], np.float32)) if out == "i8" else None, want_acc=True)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    if out == "bf16":
+        got = host(y.view(torch.int16)).view(np.uint16)
+    else:
+        got = host(y)
+    if act != "gelu":
+        np.testing.assert_array_equal(got, ref)  # exact: the same fp32 operations in the same order
+        return
+    # GELU: the device erff and the host erff may differ in the last bit.  For negative inputs
+    # 1 + erf(v / sqrt 2) cancels, so that bit is a small absolute (not relative) difference; bf16 rounding
+    # can turn a tiny fp32 difference into one bf16 step.
+    den = max(1.0, float(np.max(np.abs(y32))))
+    if out == "f32":
+        assert np.max(np.abs(got.astype(np.float64) - ref)) <= 4e-7 * den
+    elif out == "bf16":
+        g = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        r = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 4e-7 * den)
+        assert np.mean(got != ref) < 1e-3
+    else:
+        diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+        assert diff.max() <= 1 and np.mean(diff) < 1e-3
