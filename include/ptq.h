@@ -11,6 +11,9 @@
  *   quant_per_token_i8   per-token int8 activation quantization (with X/s)
  *   w8a8_gemm_dequant    int8 x int8 -> int32 GEMM, fused dequantization
  *   w8a8_gemm_fused      the same with bias, activation and fp32/bf16/int8 output
+ *   sq_act_scale_ema     static per-tensor activation scale, moving-average range
+ *   weight_scale_per_tensor   per-tensor (per-layer) weight scale
+ *   quant_static_i8      int8 codes of a whole tensor with one static scale
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (hipMalloc'd or equivalent), owned by the
@@ -76,6 +79,7 @@ extern "C" {
 #define PTQ_K_MULTIPLE 16
 
 typedef enum { PTQ_ACT_NONE = 0, PTQ_ACT_RELU = 1, PTQ_ACT_GELU = 2 } ptq_act;
+typedef enum { PTQ_FOLD_DIV = 1, PTQ_FOLD_MUL = 2 } ptq_fold;
 typedef enum { PTQ_OUT_F32 = 0, PTQ_OUT_BF16 = 1, PTQ_OUT_I8 = 2 } ptq_out;
 
 typedef enum {
@@ -267,6 +271,49 @@ PTQ_API ptq_status w8a8_gemm_fused(const int8_t* xq, const int8_t* wq, const flo
                                    const float* bias, int act, int out_type, const float* next_s,
                                    const float* out_scale, int64_t M, int64_t N, int64_t K, void* out, int32_t* acc,
                                    void* stream);
+
+/*
+ * Static per-tensor activation scale from a moving average of the
+ * activation range.  [INT8] 2.1 (tracking the range with a moving average is
+ * more robust than the raw min/max), [QAT] 六 (activation quantizer type
+ * moving_average_abs_max), [SQ] (the quantized tensor is the smoothed one).
+ *
+ * Per calibration batch: col_amax = sq_absmax_calib of the batch (not
+ * accumulated), then this call:
+ *   a     = max_j fl32(col_amax[j] * fl32(1/s[j]))      (max |x_hat| of the batch; s may be NULL)
+ *   state = first ? a : fl32(fl32(momentum * state) + fl32(fl32(1 - momentum) * a))
+ *   scale = state > 0 ? fl32(state / 127) : 1
+ * The pages give no momentum: it is the caller's parameter, in [0, 1).
+ *
+ *   col_amax   [K] fp32 (device)      state  [1] fp32 in/out (device)
+ *   scale      [1] fp32 output        row_scale [rows] fp32 output filled with scale, or NULL
+ */
+PTQ_API ptq_status sq_act_scale_ema(const float* col_amax, const float* s, int64_t K, float momentum, int first,
+                                    float* state, float* scale, float* row_scale, int64_t rows, void* stream);
+
+/*
+ * Per-tensor (per-layer) weight scale: one scale for the whole weight
+ * ([PTQ] 逐层量化 vs 逐通道量化; the MinMax rule of the per-channel path on
+ * the whole tensor -- the SSZ search is per-channel only, [SSZ] 使用限制):
+ *   a = max_j fl32(col_amax[j] * s[j]);  scale = max(fl32(a / 127), min_scale)
+ * with col_amax = sq_absmax_calib of the weight; ch_scale [N] (or NULL)
+ * receives the same value for every output channel (what the GEMM reads).
+ */
+PTQ_API ptq_status weight_scale_per_tensor(const float* col_amax, const float* s, int64_t K, float min_scale,
+                                           float* scale, float* ch_scale, int64_t N, void* stream);
+
+/*
+ * Int8 codes of a whole [rows, cols] tensor with one static scale (scale[0],
+ * device): the static per-tensor activation quantization (fold =
+ * PTQ_FOLD_DIV: x_hat = fl32(x * fl32(1/s_j))) or the per-tensor weight
+ * quantization (fold = PTQ_FOLD_MUL: w_hat = fl32(w * s_j)); s may be NULL
+ * (no fold, fold ignored).  [INT8] 2.1.
+ *   q[r, j] = clamp(rne(fl32(x_hat[r, j] * fl32(1/scale[0]))), -127, 127)
+ *   row_scale [rows] fp32 output filled with scale[0] (the GEMM's token scales), or NULL
+ * Shapes, dtypes and alignment as quant_per_token_i8.
+ */
+PTQ_API ptq_status quant_static_i8(const void* x, int dtype, int64_t rows, int64_t cols, const float* s, int fold,
+                                   const float* scale, int8_t* q, float* row_scale, void* stream);
 
 #ifdef __cplusplus
 }

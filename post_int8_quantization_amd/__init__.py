@@ -14,6 +14,9 @@ Entry points (same names as the C ABI):
   w8a8_gemm_dequant(xq, wq, tok_scale, ch_scale, want_acc=False) -> y[M,N] fp32 (, acc int32)
   w8a8_gemm_fused(xq, wq, tok_scale, ch_scale, bias=None, act="none", out="f32", next_s=None,
                   out_scale=None) -> out[M,N] fp32 / bf16 / int8
+  sq_act_scale_ema(col_amax, s=None, momentum=0.9, first=False, state=None, rows=0) -> (state, scale, row_scale)
+  weight_scale_per_tensor(col_amax, s=None, min_scale=1e-5, n=0) -> (scale[1], ch_scale[n] or None)
+  quant_static_i8(x, scale, s=None, fold="div") -> (q int8, row_scale)
 """
 from __future__ import annotations
 
@@ -36,7 +39,7 @@ STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE"
 
 EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
            "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant",
-           "w8a8_gemm_fused")
+           "w8a8_gemm_fused", "sq_act_scale_ema", "weight_scale_per_tensor", "quant_static_i8")
 
 
 class PtqError(RuntimeError):
@@ -63,8 +66,12 @@ def _load():
     lib.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
     lib.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     lib.w8a8_gemm_fused.argtypes = [vp, vp, vp, vp, vp, ci, ci, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.sq_act_scale_ema.argtypes = [vp, vp, i64, f32, ci, vp, vp, vp, i64, vp]
+    lib.weight_scale_per_tensor.argtypes = [vp, vp, i64, f32, vp, vp, i64, vp]
+    lib.quant_static_i8.argtypes = [vp, ci, i64, i64, vp, ci, vp, vp, vp, vp]
     for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
-               "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused"):
+               "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused", "sq_act_scale_ema",
+               "weight_scale_per_tensor", "quant_static_i8"):
         getattr(lib, fn).restype = ci
     return lib
 
@@ -242,3 +249,61 @@ def w8a8_gemm_fused(xq, wq, tok_scale, ch_scale, bias=None, act="none", out="f32
     _check(lib.w8a8_gemm_fused(_ptr(xq), _ptr(wq), _ptr(tok_scale), _ptr(ch_scale), _ptr(bias), ACT[act], code,
                                _ptr(next_s), _ptr(out_scale), M, N, K, _ptr(y), _ptr(acc), _stream(stream)))
     return (y, acc) if want_acc else y
+
+
+FOLD = {"div": 1, "mul": 2}
+
+
+def sq_act_scale_ema(col_amax, s=None, momentum=0.9, first=False, state=None, scale=None, rows=0, row_scale=None,
+                     stream=None):
+    """Moving-average static activation scale from one batch's column maxima.  state / scale are
+    1-element fp32 device tensors (created when None); row_scale [rows] is filled with the scale."""
+    _dev(col_amax, "col_amax", (torch.float32,))
+    K = col_amax.numel()
+    dev = col_amax.device
+    if s is not None:
+        _dev(s, "s", (torch.float32,))
+    if state is None:
+        state = torch.zeros(1, dtype=torch.float32, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if row_scale is None and rows > 0:
+        row_scale = torch.empty(rows, dtype=torch.float32, device=dev)
+    n = row_scale.numel() if row_scale is not None else 0
+    _check(lib.sq_act_scale_ema(_ptr(col_amax), _ptr(s), K, float(momentum), int(bool(first)), _ptr(state),
+                                _ptr(scale), _ptr(row_scale), n, _stream(stream)))
+    return state, scale, row_scale
+
+
+def weight_scale_per_tensor(col_amax, s=None, min_scale=SSZ_MIN_SCALE, n=0, scale=None, ch_scale=None, stream=None):
+    """Per-tensor weight scale from the weight's column maxima; ch_scale [n] gets it for every channel."""
+    _dev(col_amax, "col_amax", (torch.float32,))
+    K = col_amax.numel()
+    dev = col_amax.device
+    if s is not None:
+        _dev(s, "s", (torch.float32,))
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if ch_scale is None and n > 0:
+        ch_scale = torch.empty(n, dtype=torch.float32, device=dev)
+    nn = ch_scale.numel() if ch_scale is not None else 0
+    _check(lib.weight_scale_per_tensor(_ptr(col_amax), _ptr(s), K, float(min_scale), _ptr(scale), _ptr(ch_scale),
+                                       nn, _stream(stream)))
+    return scale, ch_scale
+
+
+def quant_static_i8(x, scale, s=None, fold="div", q=None, row_scale=None, want_row_scale=True, stream=None):
+    """Int8 codes of x with one static scale (1-element device tensor); fold "div" (activations) or "mul"
+    (weights) when s is given."""
+    _dev(x, "x", _FLOATS)
+    _dev(scale, "scale", (torch.float32,))
+    R, C = x.shape
+    if s is not None:
+        _dev(s, "s", (torch.float32,))
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    if row_scale is None and want_row_scale:
+        row_scale = torch.empty(R, dtype=torch.float32, device=x.device)
+    _check(lib.quant_static_i8(_ptr(x), _dtype_code(x), R, C, _ptr(s), FOLD[fold] if s is not None else 0,
+                               _ptr(scale), _ptr(q), _ptr(row_scale), _stream(stream)))
+    return q, row_scale

@@ -121,6 +121,61 @@ __global__ void k_smooth(const float* __restrict__ ax, const float* __restrict__
   s[j] = (float)v;
 }
 
+// Static per-tensor scales from column maxima (one block).  For a positive constant r, rounding is
+// monotone, so max_t |fl32(x_tj * r)| = fl32(max_t |x_tj| * r): the maximum of the folded tensor is
+// the maximum over columns of the folded column maxima.
+//   mode 0 (activation, [INT8] 2.1 moving-average range): a = max_j fl32(colmax_j * fl32(1/s_j));
+//          state = first ? a : fl32(fl32(m * state) + fl32(fl32(1 - m) * a));
+//          scale = state > 0 ? fl32(state / 127) : 1
+//   mode 1 (weight, per-tensor MinMax): a = max_j fl32(colmax_j * s_j);  scale = max(fl32(a / 127), min_scale)
+// bcast[0 .. n_bcast) receives the scale too (the per-row / per-channel vector a GEMM reads).
+constexpr int kScaleThreads = 1024;
+
+__global__ __launch_bounds__(kScaleThreads) void k_tensor_scale(const float* __restrict__ colmax,
+                                                                const float* __restrict__ s, int64_t K, int mode,
+                                                                float momentum, int first, float min_scale,
+                                                                float* __restrict__ state, float* __restrict__ scale,
+                                                                float* __restrict__ bcast, int64_t n_bcast) {
+  __shared__ float red[kScaleThreads / kWave];
+  __shared__ float s_out;
+  const int tid = threadIdx.x;
+  float a = 0.0f;
+  for (int64_t j = tid; j < K; j += kScaleThreads) {
+    float c = colmax[j];
+    if (s) c = mode == 0 ? c * (1.0f / s[j]) : c * s[j];
+    a = fmaxf(a, c);
+  }
+  a = wave_max(a);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = a;
+  __syncthreads();
+  if (tid == 0) {
+    float m = red[0];
+    for (int w = 1; w < kScaleThreads / kWave; ++w) m = fmaxf(m, red[w]);
+    float S;
+    if (mode == 0) {
+      float st;
+      if (first) {
+        st = m;
+      } else {
+        const float t1 = momentum * state[0];
+        const float wgt = 1.0f - momentum;
+        const float t2 = wgt * m;
+        st = t1 + t2;
+      }
+      state[0] = st;
+      S = st > 0.0f ? st / 127.0f : 1.0f;
+    } else {
+      S = m / 127.0f;
+      S = S < min_scale ? min_scale : S;
+    }
+    scale[0] = S;
+    s_out = S;
+  }
+  __syncthreads();
+  const float S = s_out;
+  for (int64_t i = tid; i < n_bcast; i += kScaleThreads) bcast[i] = S;
+}
+
 }  // namespace
 
 hipError_t launch_absmax_cols(const void* x, int dtype, int64_t rows, int64_t cols, float* amax, int accumulate,
@@ -145,6 +200,14 @@ hipError_t launch_absmax_cols(const void* x, int dtype, int64_t rows, int64_t co
   else
     k_absmax_cols<PTQ_F32><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
                                                            rows_per_block, reinterpret_cast<unsigned*>(amax));
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_scale(const float* col_amax, const float* s, int64_t K, int mode, float momentum, int first,
+                               float min_scale, float* state, float* scale, float* bcast, int64_t n_bcast,
+                               hipStream_t stream) {
+  k_tensor_scale<<<1, kScaleThreads, 0, stream>>>(col_amax, s, K, mode, momentum, first, min_scale, state, scale,
+                                                  bcast, bcast ? n_bcast : 0);
   return hipGetLastError();
 }
 

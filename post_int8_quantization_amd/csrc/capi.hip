@@ -189,4 +189,50 @@ ptq_status w8a8_gemm_fused(const int8_t* xq, const int8_t* wq, const float* tok_
                   fn);
 }
 
+ptq_status sq_act_scale_ema(const float* col_amax, const float* s, int64_t K, float momentum, int first, float* state,
+                            float* scale, float* row_scale, int64_t rows, void* stream) {
+  const char* fn = "sq_act_scale_ema";
+  if (!col_amax || !state || !scale) return fail(PTQ_ERR_NULL, "%s: col_amax, state and scale are required", fn);
+  if (K <= 0) return fail(PTQ_ERR_SHAPE, "%s: K=%lld must be >= 1", fn, (long long)K);
+  if (row_scale && rows <= 0) return fail(PTQ_ERR_SHAPE, "%s: rows=%lld must be >= 1", fn, (long long)rows);
+  if (!(momentum >= 0.0f && momentum < 1.0f))
+    return fail(PTQ_ERR_ARG, "%s: momentum=%g must lie in [0, 1)", fn, (double)momentum);
+  return from_hip(ptq::launch_tensor_scale(col_amax, s, K, 0, momentum, first != 0, 0.0f, state, scale, row_scale,
+                                           rows, (hipStream_t)stream),
+                  fn);
+}
+
+ptq_status weight_scale_per_tensor(const float* col_amax, const float* s, int64_t K, float min_scale, float* scale,
+                                   float* ch_scale, int64_t N, void* stream) {
+  const char* fn = "weight_scale_per_tensor";
+  if (!col_amax || !scale) return fail(PTQ_ERR_NULL, "%s: col_amax and scale are required", fn);
+  if (K <= 0) return fail(PTQ_ERR_SHAPE, "%s: K=%lld must be >= 1", fn, (long long)K);
+  if (ch_scale && N <= 0) return fail(PTQ_ERR_SHAPE, "%s: N=%lld must be >= 1", fn, (long long)N);
+  if (!(min_scale > 0.0f) || isinf(min_scale))
+    return fail(PTQ_ERR_ARG, "%s: min_scale=%g must be positive", fn, (double)min_scale);
+  return from_hip(ptq::launch_tensor_scale(col_amax, s, K, 1, 0.0f, 0, min_scale, nullptr, scale, ch_scale, N,
+                                           (hipStream_t)stream),
+                  fn);
+}
+
+ptq_status quant_static_i8(const void* x, int dtype, int64_t rows, int64_t cols, const float* s, int fold,
+                           const float* scale, int8_t* q, float* row_scale, void* stream) {
+  const char* fn = "quant_static_i8";
+  if (!x || !scale || !q) return fail(PTQ_ERR_NULL, "%s: x, scale and q are required", fn);
+  if (!known_dtype(dtype)) return fail(PTQ_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+  if (rows <= 0 || cols <= 0)
+    return fail(PTQ_ERR_SHAPE, "%s: rows=%lld cols=%lld must be >= 1", fn, (long long)rows, (long long)cols);
+  if (cols % PTQ_K_MULTIPLE) return fail(PTQ_ERR_SHAPE, "%s: cols=%lld is not a multiple of 16", fn, (long long)cols);
+  if (cols > ptq::kMaxRowK) return fail(PTQ_ERR_SHAPE, "%s: cols=%lld exceeds %lld", fn, (long long)cols,
+                                        (long long)ptq::kMaxRowK);
+  if (rows > INT64_MAX / cols) return fail(PTQ_ERR_SHAPE, "%s: rows*cols overflows", fn);
+  if (s && fold != PTQ_FOLD_DIV && fold != PTQ_FOLD_MUL)
+    return fail(PTQ_ERR_ARG, "%s: fold=%d (PTQ_FOLD_DIV or PTQ_FOLD_MUL with s)", fn, fold);
+  if (!aligned16(x) || !aligned16(q) || (s && !aligned16(s)))
+    return fail(PTQ_ERR_ALIGN, "%s: x, q and s must be 16-byte aligned", fn);
+  return from_hip(ptq::launch_quant_static(x, dtype, rows, cols, s, fold == PTQ_FOLD_MUL, scale, q, row_scale,
+                                           (hipStream_t)stream),
+                  fn);
+}
+
 }  // extern "C"

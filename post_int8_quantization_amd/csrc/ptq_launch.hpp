@@ -20,6 +20,17 @@ hipError_t launch_quant_per_token(const void* x, int dtype, int64_t T, int64_t K
 hipError_t launch_quant_per_token_rpb(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,
                                       float* tok_scale, int64_t rows_per_block, hipStream_t stream);
 
+// static per-tensor quantization: one scale (scale[0], device) for every row; fold_mul: x * s_j instead of
+// x * fl32(1/s_j); row_scale (may be null) receives scale[0] per row
+hipError_t launch_quant_static(const void* x, int dtype, int64_t rows, int64_t cols, const float* s, int fold_mul,
+                               const float* scale, int8_t* q, float* row_scale, hipStream_t stream);
+
+// single-block scale kernels over column maxima: activation (moving average, mode 0) or weight
+// (per-tensor MinMax, mode 1); see calib.hip
+hipError_t launch_tensor_scale(const float* col_amax, const float* s, int64_t K, int mode, float momentum, int first,
+                               float min_scale, float* state, float* scale, float* bcast, int64_t n_bcast,
+                               hipStream_t stream);
+
 hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits, int max_iter,
                       double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,
                       hipStream_t stream);

@@ -78,11 +78,13 @@ __device__ __forceinline__ void unpack16(const uint4 (&raw)[Piece<DT>::P], float
   }
 }
 
-// One row: fold, absmax (wave butterfly + LDS across waves), codes, store.
-template <int DT, bool HAS_S, int TPR, int CPT>
+// One row: fold, absmax (wave butterfly + LDS across waves), codes, store.  STATIC: the scale is
+// given (static_delta, its reciprocal static_inv) and no maximum is taken.
+template <int DT, bool HAS_S, int TPR, int CPT, bool STATIC>
 __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P], const float (&r)[CPT][16], int64_t t,
                                           int64_t T, int64_t K, int tid, int8_t* __restrict__ xq,
-                                          float* __restrict__ tok_scale, float (*red)[TPR / kWave], int parity) {
+                                          float* __restrict__ tok_scale, float (*red)[TPR / kWave], int parity,
+                                          float static_delta, float static_inv) {
   constexpr int NW = TPR / kWave;
   constexpr int E = Piece<DT>::E, P = Piece<DT>::P;
   float v[CPT][16];
@@ -93,19 +95,25 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       if constexpr (HAS_S) v[m][e] = v[m][e] * r[m][e];
-      amax = fmaxf(amax, fabsf(v[m][e]));
+      if constexpr (!STATIC) amax = fmaxf(amax, fabsf(v[m][e]));
     }
   }
-  amax = wave_max(amax);
-  if constexpr (NW > 1) {
-    if ((tid & (kWave - 1)) == 0) red[parity][tid / kWave] = amax;
-    __syncthreads();
-    amax = red[parity][0];
+  float delta, inv;
+  if constexpr (STATIC) {
+    delta = static_delta;
+    inv = static_inv;
+  } else {
+    amax = wave_max(amax);
+    if constexpr (NW > 1) {
+      if ((tid & (kWave - 1)) == 0) red[parity][tid / kWave] = amax;
+      __syncthreads();
+      amax = red[parity][0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red[parity][w]);
+      for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red[parity][w]);
+    }
+    delta = amax > 0.0f ? amax / 127.0f : 1.0f;
+    inv = 1.0f / delta;
   }
-  const float delta = amax > 0.0f ? amax / 127.0f : 1.0f;
-  const float inv = 1.0f / delta;
   const bool live = t < T;
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + (live ? t : 0) * K, live ? (uint32_t)K : 0u);
 #pragma unroll
@@ -126,8 +134,10 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
       }
     }
   }
-  // lane 0 writes delta: the other lanes' offsets fall past the 4-byte range
-  const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tok_scale + (live ? t : 0), live ? 4u : 0u);
+  // lane 0 writes delta: the other lanes' offsets fall past the 4-byte range (a NULL tok_scale, allowed
+  // in the static mode, gets a zero-length range)
+  const bool put = live && tok_scale != nullptr;
+  const __amdgpu_buffer_rsrc_t rt = buf_rsrc(put ? tok_scale + t : reinterpret_cast<float*>(xq), put ? 4u : 0u);
   buf_store4(rt, tid == 0 ? 0u : 4u, __float_as_uint(delta));
 }
 
@@ -135,10 +145,13 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
 // refilled with the row D strides ahead as soon as its row is quantized.  A
 // block walks whole rounds of D rows; the rows of a round past T are no-ops
 // (zero-length descriptors).
-template <int DT, bool HAS_S, int TPR, int CPT, int D>
+// STATIC: one given scale (scale[0]) for every row, as a per-tensor static quantization; fold_mul
+// folds by s_j (the weight side) instead of by fl32(1/s_j) (the activation side).
+template <int DT, bool HAS_S, int TPR, int CPT, int D, bool STATIC>
 __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, int64_t T, int64_t K,
                                                    const float* __restrict__ s, int8_t* __restrict__ xq,
-                                                   float* __restrict__ tok_scale) {
+                                                   float* __restrict__ tok_scale, const float* __restrict__ scale,
+                                                   int fold_mul) {
   constexpr int E = Piece<DT>::E, P = Piece<DT>::P;
   __shared__ float red[2][TPR / kWave];
   const int tid = threadIdx.x;
@@ -173,7 +186,10 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
           const uint4 w = sv[m][p * (E / 4) + h];
           const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) r[m][p * E + 4 * h + i] = in ? 1.0f / __uint_as_float(u[i]) : 1.0f;
+          for (int i = 0; i < 4; ++i) {
+            const float sj = __uint_as_float(u[i]);
+            r[m][p * E + 4 * h + i] = in ? (fold_mul ? sj : 1.0f / sj) : 1.0f;
+          }
         }
       }
     }
@@ -183,28 +199,35 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 #pragma unroll
       for (int e = 0; e < 16; ++e) r[m][e] = 1.0f;
   }
+  float static_delta = 1.0f, static_inv = 1.0f;
+  if constexpr (STATIC) {
+    static_delta = scale[0];
+    static_inv = 1.0f / static_delta;
+  }
   int parity = 0;
   for (int64_t base = blockIdx.x; base < T; base += D * G) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int64_t t = base + d * G;
-      quant_row<DT, HAS_S, TPR, CPT>(ring[d], r, t, T, K, tid, xq, tok_scale, red, parity);
+      quant_row<DT, HAS_S, TPR, CPT, STATIC>(ring[d], r, t, T, K, tid, xq, tok_scale, red, parity, static_delta,
+                                             static_inv);
       parity ^= 1;
       load_raw<DT, TPR, CPT>(x, t + D * G, T, K, tid, ring[d]);
     }
   }
 }
 
-template <int DT, bool HAS_S, int TPR, int CPT>
-void launch_one(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, int64_t blocks,
-                hipStream_t stream) {
+template <int DT, bool HAS_S, int TPR, int CPT, bool STATIC>
+void launch_one(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, const float* scale,
+                int fold_mul, int64_t blocks, hipStream_t stream) {
   constexpr int D = CPT >= 4 ? 1 : 4 / CPT;  // rows in flight per block: about 4 groups of 16 elements per thread
-  k_quant_tok<DT, HAS_S, TPR, CPT, D><<<(unsigned)blocks, TPR, 0, stream>>>(x, T, K, s, xq, ts);
+  k_quant_tok<DT, HAS_S, TPR, CPT, D, STATIC><<<(unsigned)blocks, TPR, 0, stream>>>(x, T, K, s, xq, ts, scale,
+                                                                                    fold_mul);
 }
 
-template <int DT, bool HAS_S>
-hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, int64_t rows_per_block,
-                    hipStream_t stream) {
+template <int DT, bool HAS_S, bool STATIC>
+hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, const float* scale,
+                    int fold_mul, int64_t rows_per_block, hipStream_t stream) {
   const int64_t ngroup = K / 16;
   // the narrowest block with at most 2 groups of 16 elements per thread (up to 8 at 1024 threads)
   int tpr = 64;
@@ -218,7 +241,7 @@ hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t*
   if (blocks < 1) blocks = 1;
 #define PTQ_Q(TPR_, CPT_)                                                           \
   if (tpr == TPR_ && cpt <= CPT_) {                                                 \
-    launch_one<DT, HAS_S, TPR_, CPT_>(x, T, K, s, xq, ts, blocks, stream);          \
+    launch_one<DT, HAS_S, TPR_, CPT_, STATIC>(x, T, K, s, xq, ts, scale, fold_mul, blocks, stream); \
     return hipGetLastError();                                                       \
   }
   PTQ_Q(64, 1) PTQ_Q(64, 2) PTQ_Q(128, 2) PTQ_Q(256, 2) PTQ_Q(512, 2)
@@ -229,19 +252,31 @@ hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t*
 
 }  // namespace
 
+static int64_t default_rows_per_block(int64_t T, int64_t K) {
+  // enough blocks to keep rows in flight on every CU, enough rows per block to reuse the reciprocals
+  int64_t r = T / (K >= 8192 ? 512 : 1024);
+  return r < 1 ? 1 : (r > 16 ? 16 : r);
+}
+
 // rows_per_block <= 0 picks the default
 hipError_t launch_quant_per_token_rpb(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,
                                       float* tok_scale, int64_t rows_per_block, hipStream_t stream) {
-  if (rows_per_block <= 0) {
-    // enough blocks to keep rows in flight on every CU, enough rows per block to reuse the reciprocals
-    rows_per_block = T / (K >= 8192 ? 512 : 1024);
-    rows_per_block = rows_per_block < 1 ? 1 : (rows_per_block > 16 ? 16 : rows_per_block);
-  }
+  if (rows_per_block <= 0) rows_per_block = default_rows_per_block(T, K);
   if (dtype == PTQ_BF16)
-    return s ? dispatch<PTQ_BF16, true>(x, T, K, s, xq, tok_scale, rows_per_block, stream)
-             : dispatch<PTQ_BF16, false>(x, T, K, s, xq, tok_scale, rows_per_block, stream);
-  return s ? dispatch<PTQ_F32, true>(x, T, K, s, xq, tok_scale, rows_per_block, stream)
-           : dispatch<PTQ_F32, false>(x, T, K, s, xq, tok_scale, rows_per_block, stream);
+    return s ? dispatch<PTQ_BF16, true, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream)
+             : dispatch<PTQ_BF16, false, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream);
+  return s ? dispatch<PTQ_F32, true, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream)
+           : dispatch<PTQ_F32, false, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream);
+}
+
+hipError_t launch_quant_static(const void* x, int dtype, int64_t rows, int64_t cols, const float* s, int fold_mul,
+                               const float* scale, int8_t* q, float* row_scale, hipStream_t stream) {
+  const int64_t rpb = default_rows_per_block(rows, cols);
+  if (dtype == PTQ_BF16)
+    return s ? dispatch<PTQ_BF16, true, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream)
+             : dispatch<PTQ_BF16, false, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream);
+  return s ? dispatch<PTQ_F32, true, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream)
+           : dispatch<PTQ_F32, false, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream);
 }
 
 hipError_t launch_quant_per_token(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,

@@ -45,6 +45,9 @@ def lib():
     L.quant_per_token_i8.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
     L.w8a8_gemm_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     L.w8a8_gemm_fused.argtypes = [vp, vp, vp, vp, vp, ci, ci, vp, vp, i64, i64, i64, vp, vp, vp]
+    L.sq_act_scale_ema.argtypes = [vp, vp, i64, f32, ci, vp, vp, vp, i64, vp]
+    L.weight_scale_per_tensor.argtypes = [vp, vp, i64, f32, vp, vp, i64, vp]
+    L.quant_static_i8.argtypes = [vp, ci, i64, i64, vp, ci, vp, vp, vp, vp]
     L.ptq_last_error.restype = ctypes.c_char_p
     L.ptq_status_string.restype = ctypes.c_char_p
     return L
@@ -64,7 +67,8 @@ def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
                           "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
-                          "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused"}
+                          "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused", "sq_act_scale_ema",
+                          "weight_scale_per_tensor", "quant_static_i8"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.ptq_abi_version() == int(header_define("PTQ_ABI_VERSION"))
@@ -206,6 +210,30 @@ def test_gemm_fused_errors(lib):
     _expect(lib, call(K=133152), SHAPE, "overflow")
     _expect(lib, call(xq=MIS), ALIGN)
     _expect(lib, call(out=2, osc=P, y=MIS), ALIGN)
+
+
+def test_static_scale_errors(lib):
+    e = lib.sq_act_scale_ema
+    _expect(lib, e(None, None, 16, 0.9, 1, P, P, None, 0, None), NULL)
+    _expect(lib, e(P, None, 16, 0.9, 1, None, P, None, 0, None), NULL)
+    _expect(lib, e(P, None, 0, 0.9, 1, P, P, None, 0, None), SHAPE)
+    _expect(lib, e(P, None, 16, 0.9, 1, P, P, P, 0, None), SHAPE)
+    for m in (-0.1, 1.0, math.nan):
+        _expect(lib, e(P, None, 16, m, 0, P, P, None, 0, None), ARG, "momentum")
+    w = lib.weight_scale_per_tensor
+    _expect(lib, w(None, None, 16, 1e-5, P, None, 0, None), NULL)
+    _expect(lib, w(P, None, 16, 1e-5, None, None, 0, None), NULL)
+    _expect(lib, w(P, None, 0, 1e-5, P, None, 0, None), SHAPE)
+    _expect(lib, w(P, None, 16, 1e-5, P, P, 0, None), SHAPE)
+    _expect(lib, w(P, None, 16, 0.0, P, None, 0, None), ARG)
+    q = lib.quant_static_i8
+    _expect(lib, q(None, BF16, 4, 64, None, 0, P, P, None, None), NULL)
+    _expect(lib, q(P, BF16, 4, 64, None, 0, None, P, None, None), NULL)
+    _expect(lib, q(P, 9, 4, 64, None, 0, P, P, None, None), DTYPE)
+    _expect(lib, q(P, BF16, 4, 40, None, 0, P, P, None, None), SHAPE)
+    _expect(lib, q(P, BF16, 4, 64, P, 0, P, P, None, None), ARG, "fold")
+    _expect(lib, q(P, BF16, 4, 64, P, 3, P, P, None, None), ARG, "fold")
+    _expect(lib, q(MIS, BF16, 4, 64, None, 0, P, P, None, None), ALIGN)
 
 
 def test_binding_rejects_host_tensors():

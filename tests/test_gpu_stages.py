@@ -296,3 +296,55 @@ def test_gemm_fused(pq, M, N, K, act, out):
     else:
         diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
         assert diff.max() <= 1 and np.mean(diff) < 1e-3
+
+
+# ------------------------------------------------------------------ static per-tensor scales
+
+@pytest.mark.parametrize("T,K,dtype,smooth", [(16, 64, synth.F32, True), (300, 1040, synth.BF16, True),
+                                              (257, 4096, synth.BF16, False), (64, 16384, synth.F32, True)])
+def test_act_scale_ema(pq, T, K, dtype, smooth):
+    s = np.exp(np.random.default_rng(T + K).uniform(-1, 1, K)).astype(np.float32) if smooth else None
+    state_ref = None
+    state = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    for b in range(5):
+        x = _x(f"ema/{T}x{K}/{b}", T, K, dtype, factor=40.0 if b != 2 else 200.0)
+        a = oracle.absmax_tensor(synth.widen(x), s, oracle.FOLD_DIV)
+        state_ref = oracle.ema_update(state_ref, a, 0.9, b == 0)
+        announce(f"sq_act_scale_ema T={T} K={K} batch {b}")
+        col = pq.sq_absmax_calib(dev(x))
+        st, sc, rs = pq.sq_act_scale_ema(col, None if s is None else dev(s), 0.9, first=b == 0, state=state, rows=T)
+        assert host(st)[0] == state_ref, (b, host(st)[0], state_ref)
+        assert host(sc)[0] == oracle.act_static_scale(state_ref)
+        assert np.all(host(rs) == host(sc)[0])
+
+
+@pytest.mark.parametrize("N,K,smooth", [(128, 64, True), (300, 1040, False), (4096, 4096, True)])
+def test_weight_scale_per_tensor(pq, N, K, smooth):
+    w = _w(f"wpt/{N}x{K}", N, K, synth.BF16, 0.001)
+    s = np.exp(np.random.default_rng(N + K).uniform(-1, 1, K)).astype(np.float32) if smooth else None
+    S_ref = oracle.weight_scale_per_tensor(oracle.absmax_tensor(synth.widen(w), s, oracle.FOLD_MUL))
+    announce(f"weight_scale_per_tensor N={N} K={K}")
+    col = pq.sq_absmax_calib(dev(w))
+    sc, ch = pq.weight_scale_per_tensor(col, None if s is None else dev(s), n=N)
+    assert host(sc)[0] == S_ref
+    assert np.all(host(ch) == S_ref)
+    tiny = np.zeros(64, np.float32)
+    sc0, _ = pq.weight_scale_per_tensor(dev(tiny))
+    assert host(sc0)[0] == np.float32(1e-5)  # the floor
+
+
+@pytest.mark.parametrize("R,C,dtype,fold", [(16, 64, synth.F32, "div"), (300, 1040, synth.BF16, "div"),
+                                            (257, 4096, synth.BF16, "mul"), (33, 16384, synth.F32, "mul"),
+                                            (5, 8192, synth.BF16, None), (1, 16, synth.F32, None)])
+def test_quant_static(pq, R, C, dtype, fold):
+    x = _x(f"qs/{R}x{C}", R, C, dtype)
+    s = np.exp(np.random.default_rng(R + C).uniform(-1, 1, C)).astype(np.float32) if fold else None
+    fcode = {"div": oracle.FOLD_DIV, "mul": oracle.FOLD_MUL, None: oracle.FOLD_NONE}[fold]
+    S = np.float32(oracle.absmax_tensor(synth.widen(x), s, fcode) / 150.0)  # the largest codes saturate
+    ref = oracle.quant_static(synth.widen(x), S, s, fcode)
+    announce(f"quant_static_i8 R={R} C={C} fold={fold}")
+    q, rs = pq.quant_static_i8(dev(x), dev(np.array([S], np.float32)), None if s is None else dev(s),
+                               fold or "div")
+    np.testing.assert_array_equal(host(q), ref)
+    assert np.all(host(rs) == S)
+    assert np.any(np.abs(ref) == 127)
