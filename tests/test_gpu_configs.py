@@ -152,3 +152,93 @@ def test_opt67b_asym_weights(pq, idx):
     S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w_host), dev(s_ref))
     compare_ssz_asym(host(S)[rows], host(Z)[rows], host(wq)[rows], host(it)[rows], host(mse)[rows], ref,
                      case.name + " asym")
+
+
+def test_mlp_block_static_chain(pq):
+    """The hidden-4096 MLP block with static activation scales and the fused epilogue, end to end.
+    fc1: smoothing and a moving-average static activation scale from its 8 calibration batches.  fc2:
+    smoothing and static scale from fc1's own W8A8 ReLU outputs on 64 tokens of each calibration batch
+    (so the int8 intermediate is calibrated on what it will carry).  Forward: static fc1 input codes,
+    fc1 GEMM + ReLU writing fc2's int8 input (fc2's fold and static scale in the epilogue), fc2 GEMM.
+    GPU at full size; the oracle quantizes all of fc1's weight (fc2 reads every fc1 channel) and checks
+    sampled tokens and fc2 channels, every stage bit for bit."""
+    c1, c2 = synth.cases("opt67b")
+    T = c1.T
+    toks = sample_rows(T, 32, 29)
+    rows2 = sample_rows(c2.N, 128, 37)
+    momentum = 0.9
+    ct = 64  # calibration tokens per batch for fc2
+    w1, w2 = c1.w(), c2.w()
+    w1f, w2f = synth.widen(w1), synth.widen(w2)
+    xs = [c1.x_batch(b) for b in range(c1.calib_batches)]
+
+    # fc1 calibration
+    ax1 = None
+    for xb in xs:
+        ax1 = oracle.absmax_cols(synth.widen(xb), ax1)
+    s1 = oracle.smooth_factors(ax1, oracle.absmax_cols(w1f), 0.5)
+    st1_ref = None
+    st1 = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    d1 = None
+    for b, xb in enumerate(xs):
+        st1_ref = oracle.ema_update(st1_ref, oracle.absmax_tensor(synth.widen(xb), s1, oracle.FOLD_DIV), momentum,
+                                    b == 0)
+        announce(f"mlp chain: fc1 activation scale, batch {b}")
+        _, d1, _ = pq.sq_act_scale_ema(pq.sq_absmax_calib(dev(xb)), dev(s1), momentum, first=b == 0, state=st1)
+    d1_ref = oracle.act_static_scale(st1_ref)
+    assert host(d1)[0] == d1_ref
+    announce("mlp chain: ssz fc1")
+    S1, wq1, _, _ = pq.ssz_weight_qparams(dev(w1), dev(s1), bits=8)
+    r1 = oracle.ssz(w1f, s1, 8)
+    np.testing.assert_array_equal(host(S1), r1["S"])
+
+    # fc2 calibration on fc1's W8A8 ReLU outputs
+    hs_ref, hs = [], []
+    for b, xb in enumerate(xs):
+        xc = xb[:ct]
+        q_ref = oracle.quant_static(synth.widen(xb[:ct]), d1_ref, s1, oracle.FOLD_DIV)
+        hs_ref.append(oracle.epilogue(oracle.gemm_i8(q_ref, r1["q"]), np.full(ct, d1_ref, np.float32), r1["S"],
+                                      act=oracle.ACT_RELU))
+        announce(f"mlp chain: fc1 on fc2 calibration tokens, batch {b}")
+        q, rsc = pq.quant_static_i8(dev(np.ascontiguousarray(xc)), d1, dev(s1), "div")
+        hs.append(pq.w8a8_gemm_fused(q, wq1, rsc, S1, act="relu", out="f32"))
+        np.testing.assert_array_equal(host(hs[-1]), hs_ref[-1])
+    ax2 = None
+    for h in hs_ref:
+        ax2 = oracle.absmax_cols(h, ax2)
+    s2 = oracle.smooth_factors(ax2, oracle.absmax_cols(w2f), 0.5)
+    st2_ref = None
+    st2 = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    d2 = None
+    for b, (h_ref, h) in enumerate(zip(hs_ref, hs)):
+        st2_ref = oracle.ema_update(st2_ref, oracle.absmax_tensor(h_ref, s2, oracle.FOLD_DIV), momentum, b == 0)
+        _, d2, _ = pq.sq_act_scale_ema(pq.sq_absmax_calib(h), dev(s2), momentum, first=b == 0, state=st2)
+    d2_ref = oracle.act_static_scale(st2_ref)
+    assert host(d2)[0] == d2_ref
+    announce("mlp chain: ssz fc2")
+    S2, wq2, _, _ = pq.ssz_weight_qparams(dev(w2), dev(s2), bits=8)
+    r2 = oracle.ssz(w2f[rows2], s2, 8)
+    np.testing.assert_array_equal(host(S2)[rows2], r2["S"])
+    del xs, hs
+
+    # forward
+    x = c1.x_batch(c1.eval_index())
+    announce("mlp chain: quant_static_i8 fc1 input")
+    xq1, rs1 = pq.quant_static_i8(dev(x), d1, dev(s1), "div")
+    xq1_ref = oracle.quant_static(synth.widen(x)[toks], d1_ref, s1, oracle.FOLD_DIV)
+    np.testing.assert_array_equal(host(xq1)[toks], xq1_ref)
+    announce("mlp chain: fc1 GEMM + ReLU -> int8 (fc2 fold, static scale)")
+    h = pq.w8a8_gemm_fused(xq1, wq1, rs1, S1, act="relu", out="i8", next_s=dev(s2), out_scale=d2)
+    h_ref = oracle.epilogue(oracle.gemm_i8(xq1_ref, r1["q"]), np.full(len(toks), d1_ref, np.float32), r1["S"],
+                            act=oracle.ACT_RELU, out=oracle.OUT_I8, next_s=s2, out_scale=d2_ref)
+    np.testing.assert_array_equal(host(h)[toks], h_ref)
+    announce("mlp chain: fc2 GEMM")
+    rs2 = torch.full((T,), float(d2_ref), dtype=torch.float32, device="cuda:0")
+    y = pq.w8a8_gemm_dequant(h, wq2, rs2, S2)
+    y_ref = oracle.epilogue(oracle.gemm_i8(h_ref, r2["q"]), np.full(len(toks), d2_ref, np.float32), r2["S"])
+    np.testing.assert_array_equal(host(y)[np.ix_(toks, rows2)], y_ref)
+    # accuracy of the chained static int8 block against the fp64 block on the same tokens (reported, unpinned)
+    h64 = np.maximum(synth.widen(x)[toks].astype(np.float64) @ w1f.astype(np.float64).T, 0.0)
+    y64 = h64 @ w2f[rows2].astype(np.float64).T
+    rel = np.max(np.abs(y_ref - y64)) / np.max(np.abs(y64))
+    announce(f"mlp chain: static W8A8 block vs fp64 block {rel:.3e}")
