@@ -24,6 +24,14 @@ out [4096,4096], fc1 [16384,4096], fc2 [4096,16384], bf16, heavy-tailed rows),
 back to back on one stream, once as symmetric int8, once as symmetric int4
 and once as asymmetric int8; a step is the three passes over all matrices.
 
+--workload mlp_static measures the hidden-4096 MLP block (fc1 -> ReLU -> fc2,
+4096 tokens) with static activation scales from a moving average over the
+calibration batches: static int8 quantization of the block input, fc1 GEMM
+with ReLU writing fc2's int8 input in its epilogue (fc2's smoothing fold and
+static scale), fc2 GEMM.  Beside it, the unfused chain: fc1 GEMM + ReLU to
+fp32, per-token quantization of that intermediate, fc2 GEMM; and the
+per-tensor weight quantization (weight absmax, scale, codes) beside SSZ.
+
 --workload decode measures the decode configuration instead (16 tokens,
 X [16,8192] against W [28672,8192]): the weight is calibrated and quantized
 once, untimed; a step is the per-token quantization of the token batch and
@@ -63,7 +71,8 @@ def parse():
     p.add_argument("--calib-batches", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle GEMM time of the CPU baseline")
-    p.add_argument("--workload", choices=("opt67b", "decode", "ssz_scale"), default="opt67b")
+    p.add_argument("--workload", choices=("opt67b", "decode", "ssz_scale", "mlp_static"), default="opt67b")
+    p.add_argument("--momentum", type=float, default=0.9, help="mlp_static: moving-average momentum")
     p.add_argument("--layers", type=int, default=32, help="ssz_scale workload: number of 4-matrix layers")
     p.add_argument("--copy-ref", action="store_true",
                    help="only run a plain 1 GiB device copy three times (reference for scaling the "
@@ -148,6 +157,9 @@ def main():
         return
     if args.workload == "ssz_scale":
         ssz_scale(args)
+        return
+    if args.workload == "mlp_static":
+        mlp_static(args)
         return
 
     import numpy as np
@@ -495,6 +507,137 @@ def ssz_scale(args):
         out["cpu_baseline"] = {"value": nb / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
                                "kind": "oracle", "sample": f"symmetric int8 SSZ of the first {len(sample)} matrices "
                                "(4 layers), every row", "seconds": secs}
+    print(json.dumps(out), flush=True)
+
+
+def mlp_static(args):
+    import numpy as np
+    import torch
+
+    import post_int8_quantization_amd as pq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    c1, c2 = synth.cases("opt67b")
+    B = args.calib_batches
+    T = c1.T
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # untimed calibration, as a deployment would do once
+    w1, w2 = up(c1.w()), up(c2.w())
+    xs = [up(c1.x_batch(b)) for b in range(B)]
+    ax1 = None
+    for b, xb in enumerate(xs):
+        ax1 = pq.sq_absmax_calib(xb, ax1, accumulate=b > 0)
+    aw1 = pq.sq_absmax_calib(w1)
+    s1 = pq.sq_smooth_factors(ax1, aw1, args.alpha)
+    st1 = torch.zeros(1, dtype=torch.float32, device=dev)
+    for b, xb in enumerate(xs):
+        _, d1, _ = pq.sq_act_scale_ema(pq.sq_absmax_calib(xb), s1, args.momentum, first=b == 0, state=st1)
+    S1, wq1, _, _ = pq.ssz_weight_qparams(w1, s1, bits=8)
+    hs = []
+    for xb in xs:
+        q, rsc = pq.quant_static_i8(xb[:256], d1, s1, "div")
+        hs.append(pq.w8a8_gemm_fused(q, wq1, rsc, S1, act="relu", out="f32"))
+    ax2 = None
+    for b, h in enumerate(hs):
+        ax2 = pq.sq_absmax_calib(h, ax2, accumulate=b > 0)
+    aw2 = pq.sq_absmax_calib(w2)
+    s2 = pq.sq_smooth_factors(ax2, aw2, args.alpha)
+    st2 = torch.zeros(1, dtype=torch.float32, device=dev)
+    for b, h in enumerate(hs):
+        _, d2, _ = pq.sq_act_scale_ema(pq.sq_absmax_calib(h), s2, args.momentum, first=b == 0, state=st2)
+    S2, wq2, _, _ = pq.ssz_weight_qparams(w2, s2, bits=8)
+    del xs, hs
+    x = up(c1.x_batch(B))
+    xq1 = torch.empty((T, c1.K), dtype=torch.int8, device=dev)
+    rs1 = torch.empty(T, dtype=torch.float32, device=dev)
+    h8 = torch.empty((T, c1.N), dtype=torch.int8, device=dev)
+    rs2 = torch.empty(T, dtype=torch.float32, device=dev)
+    hf = torch.empty((T, c1.N), dtype=torch.float32, device=dev)
+    y = torch.empty((T, c2.N), dtype=torch.float32, device=dev)
+    dtok = torch.empty(T, dtype=torch.float32, device=dev)
+    # per-tensor weight path buffers
+    wpt = [dict(w=w1, q=torch.empty_like(wq1), ch=torch.empty(c1.N, dtype=torch.float32, device=dev), s=s1, c=c1),
+           dict(w=w2, q=torch.empty_like(wq2), ch=torch.empty(c2.N, dtype=torch.float32, device=dev), s=s2, c=c2)]
+    sc = torch.empty(1, dtype=torch.float32, device=dev)
+    colw = torch.empty(max(c1.K, c2.K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def fused(tm):
+        tm.stage("quant_static", lambda: pq.quant_static_i8(x, d1, s1, "div", q=xq1, row_scale=rs1, stream=stream))
+        tm.stage("fc1_relu_requant", lambda: pq.w8a8_gemm_fused(xq1, wq1, rs1, S1, act="relu", out="i8", next_s=s2,
+                                                                  out_scale=d2, y=h8, stream=stream))
+        tm.stage("fc2", lambda: pq.w8a8_gemm_dequant(h8, wq2, rs2, S2, y=y, stream=stream))
+
+    def unfused(tm):
+        tm.stage("u_quant_tok", lambda: pq.quant_per_token_i8(x, s1, xq=xq1, tok_scale=dtok, stream=stream))
+        tm.stage("u_fc1_relu_f32", lambda: pq.w8a8_gemm_fused(xq1, wq1, dtok, S1, act="relu", out="f32", y=hf,
+                                                                stream=stream))
+        tm.stage("u_quant_tok_h", lambda: pq.quant_per_token_i8(hf, s2, xq=h8, tok_scale=rs2, stream=stream))
+        tm.stage("u_fc2", lambda: pq.w8a8_gemm_dequant(h8, wq2, rs2, S2, y=y, stream=stream))
+
+    def per_tensor(tm):
+        for L in wpt:
+            c = L["c"]
+            def run(L=L, c=c):
+                col = colw[: c.K]
+                pq.sq_absmax_calib(L["w"], col, stream=stream)
+                pq.weight_scale_per_tensor(col, L["s"], n=c.N, scale=sc, ch_scale=L["ch"], stream=stream)
+                pq.quant_static_i8(L["w"], sc, L["s"], "mul", q=L["q"], want_row_scale=False, stream=stream)
+            tm.stage("w_per_tensor", run)
+
+    rs2.fill_(float(d2.item()))  # the static token scale of fc2's int8 input
+    for fn in (fused, unfused, per_tensor):
+        for _ in range(args.warmup):
+            fn(Timer(torch))
+    torch.cuda.synchronize()
+    res = {}
+    walls = {}
+    for fn in (fused, unfused, per_tensor):
+        tm = Timer(torch)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn(tm)
+        torch.cuda.synchronize()
+        walls[fn.__name__] = (time.perf_counter() - t0) * 1e3 / args.steps
+        res.update(tm.totals())
+    K = args.steps
+
+    def ms(name):
+        return res[name][0] / K
+
+    ops = 2 * T * c1.N * c1.K + 2 * T * c2.N * c2.K
+    fused_ms = ms("quant_static") + ms("fc1_relu_requant") + ms("fc2")
+    unfused_ms = ms("u_quant_tok") + ms("u_fc1_relu_f32") + ms("u_quant_tok_h") + ms("u_fc2")
+    wpt_bytes = sum(L["c"].N * L["c"].K * (2 + 2 + 1) + L["c"].N * 4 for L in wpt)
+    stages = {k: {"ms": ms(k)} for k in res}
+    stages["w_per_tensor"]["GB/s"] = wpt_bytes / (ms("w_per_tensor") / 1e3) / 1e9
+    stages["w_per_tensor"]["frac_hbm"] = stages["w_per_tensor"]["GB/s"] * 1e9 / PEAK_HBM
+    stages["w_per_tensor"]["note"] = "both weights: column absmax read + code pass read/write (5 B/elem)"
+    fc1_ops = 2 * T * c1.N * c1.K
+    roof = {"kernel": "k_gemm_pipe", "bound": "mfma", "achieved": fc1_ops / (ms("fc1_relu_requant") / 1e3) / 1e12,
+            "peak": PEAK_I8 / 1e12, "unit": "TOP/s", "per_launch_ops": fc1_ops}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    rec = load_counters("k_gemm_pipe")
+    roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
+    roof["avg_launch_us"] = ms("fc1_relu_requant") * 1e3
+    out = {
+        "metric": METRIC, "value": ops / (fused_ms / 1e3) / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": walls["fused"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "mlp_static: hidden-4096 MLP block fc1 [16384,4096] -> ReLU -> fc2 [4096,16384] on "
+                               f"{T} bf16 tokens, static activation scales (moving average, momentum "
+                               f"{args.momentum:g}, {B} calibration batches), alpha {args.alpha:g}; value = fused "
+                               "block GEMM TOPS (static input codes + fc1 GEMM/ReLU/int8 requant + fc2 GEMM)",
+                   "tokens": T, "hidden": c1.K, "parallelism": "single GPU"},
+        "fused_block_ms": fused_ms, "unfused_block_ms": unfused_ms, "fusion_saving": 1 - fused_ms / unfused_ms,
+        "wall_ms": walls, "stages": stages, "roofline": roof,
+    }
     print(json.dumps(out), flush=True)
 
 
