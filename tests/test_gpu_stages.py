@@ -80,7 +80,7 @@ def test_smooth_factors(pq, alpha):
     (16, 64, synth.F32, True), (1, 16, synth.BF16, False), (257, 1040, synth.BF16, True),
     (300, 4096, synth.BF16, True), (300, 4096, synth.F32, False), (33, 16384, synth.BF16, True),
     (5, 8192, synth.BF16, False), (64, 3072, synth.BF16, True), (9, 36864, synth.BF16, True),
-    (3, 65536 + 16, synth.BF16, True)])
+    (3, 65536 + 16, synth.BF16, True), (2, 131072, synth.BF16, True), (2, 131072, synth.F32, False)])
 def test_quant_per_token(pq, T, K, dtype, smooth):
     x = _x(f"q/{T}x{K}", T, K, dtype)
     if T > 2:
@@ -111,7 +111,8 @@ def _edge_rows(K, qmax):
     (300, 1040, synth.BF16, 4, False, 0.001), (96, 4096, synth.BF16, 8, False, 0.001),
     (96, 4096, synth.BF16, 4, True, 0.0), (40, 16384, synth.BF16, 8, True, 0.001),
     (40, 16384, synth.BF16, 4, False, 0.001), (23, 8192, synth.BF16, 8, True, 0.0),
-    (17, 2064, synth.F32, 4, True, 0.002), (6, 36864, synth.BF16, 8, False, 0.001)])
+    (17, 2064, synth.F32, 4, True, 0.002), (6, 36864, synth.BF16, 8, False, 0.001),
+    (3, 131072, synth.BF16, 8, True, 0.001), (3, 131072, synth.BF16, 4, False, 0.001)])
 def test_ssz(pq, N, K, dtype, bits, smooth, tail):
     w = _w(f"ssz/{N}x{K}", N, K, dtype, tail)
     wf = synth.widen(w).copy()
@@ -162,7 +163,7 @@ def _edge_rows_asym(K):
     (96, 4096, synth.BF16, False, 0.001, 0.0), (96, 4096, synth.F32, True, 0.0, 0.005),
     (40, 16384, synth.BF16, True, 0.001, 0.0), (23, 8192, synth.BF16, False, 0.0, 0.02),
     (17, 2064, synth.F32, False, 0.002, 0.0), (9, 16, synth.F32, False, 0.0, 0.0),
-    (6, 36864, synth.BF16, True, 0.001, 0.0)])
+    (6, 36864, synth.BF16, True, 0.001, 0.0), (3, 131072, synth.BF16, False, 0.001, 0.0)])
 def test_ssz_asym(pq, N, K, dtype, smooth, tail, shift):
     w = _w(f"ssza/{N}x{K}", N, K, dtype, tail)
     wf = synth.widen(w).copy()
@@ -335,7 +336,8 @@ def test_weight_scale_per_tensor(pq, N, K, smooth):
 
 @pytest.mark.parametrize("R,C,dtype,fold", [(16, 64, synth.F32, "div"), (300, 1040, synth.BF16, "div"),
                                             (257, 4096, synth.BF16, "mul"), (33, 16384, synth.F32, "mul"),
-                                            (5, 8192, synth.BF16, None), (1, 16, synth.F32, None)])
+                                            (5, 8192, synth.BF16, None), (1, 16, synth.F32, None),
+                                            (2, 131072, synth.BF16, "div")])
 def test_quant_static(pq, R, C, dtype, fold):
     x = _x(f"qs/{R}x{C}", R, C, dtype)
     s = np.exp(np.random.default_rng(R + C).uniform(-1, 1, C)).astype(np.float32) if fold else None
