@@ -115,8 +115,8 @@ class Timer:
         return out
 
 
-KERNEL_SOURCES = {"k_ssz": "ssz.hip", "k_gemm_pipe": "gemm.hip", "k_gemm_dec": "gemm.hip",
-                  "k_absmax_cols": "calib.hip", "k_quant_tok": "quant.hip"}
+KERNEL_SOURCES = {"k_ssz": "ssz.hip", "k_ssz_asym": "ssz.hip", "k_gemm_pipe": "gemm.hip", "k_gemm_dec": "gemm.hip",
+                  "k_absmax_cols": "calib.hip", "k_tensor_scale": "calib.hip", "k_quant_tok": "quant.hip"}
 
 
 def kernel_source_sha(kernel_tag):
@@ -128,14 +128,16 @@ def kernel_source_sha(kernel_tag):
     return h.hexdigest()[:16]
 
 
-def load_counters(kernel_tag):
-    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE), from the committed
-    summaries under profiles/, if they were taken on the kernel's current source (hash match); else None."""
+def load_counters(kernel_tag, workload):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE) on this workload, from the
+    committed summaries under profiles/, if they were taken on the kernel's current source (hash match);
+    else None."""
     digest = kernel_source_sha(kernel_tag)
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*counters*.md"))):
         for m in re.finditer(r"traffic-record:\s*(\{.*\})", open(f).read()):
             rec = json.loads(m.group(1))
-            if rec.get("kernel") == kernel_tag and rec.get("source_sha") == digest:
+            if rec.get("kernel") == kernel_tag and rec.get("workload") == workload and \
+                    rec.get("source_sha") == digest:
                 return rec
     return None
 
@@ -281,7 +283,7 @@ def main():
         roof = {"kernel": "k_quant_tok", "bound": "hbm", "achieved": quant_bytes / sec("quant") / 1e9,
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = load_counters(roof["kernel"])
+    rec = load_counters(roof["kernel"], "opt67b")
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = tot[dom][0] * 1e3 / tot[dom][1]
 
@@ -368,7 +370,7 @@ def decode(args):
     roof = {"kernel": "k_gemm_dec", "bound": "hbm", "achieved": gemm_bytes / gemm_s / 1e9, "peak": PEAK_HBM / 1e9,
             "unit": "GB/s", "per_launch_bytes": gemm_bytes}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = load_counters("k_gemm_dec")
+    rec = load_counters("k_gemm_dec", "decode")
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = tot["gemm"][0] * 1e3 / tot["gemm"][1]
     out = {
@@ -480,7 +482,7 @@ def ssz_scale(args):
             "achieved": SSZ_OPS_PER_ELEM_PASS * v["element_passes"] / (v["ms"] / 1e3) / 1e12,
             "peak": PEAK_ALU / 1e12, "unit": "Tlane-op/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = load_counters("k_ssz")
+    rec = load_counters("k_ssz", "ssz_scale")
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = v["ms"] * 1e3 / len(mats)
     out = {
@@ -623,7 +625,7 @@ def mlp_static(args):
     roof = {"kernel": "k_gemm_pipe", "bound": "mfma", "achieved": fc1_ops / (ms("fc1_relu_requant") / 1e3) / 1e12,
             "peak": PEAK_I8 / 1e12, "unit": "TOP/s", "per_launch_ops": fc1_ops}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = load_counters("k_gemm_pipe")
+    rec = load_counters("k_gemm_pipe", "mlp_static")
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = ms("fc1_relu_requant") * 1e3
     out = {
