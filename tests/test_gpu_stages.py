@@ -350,3 +350,88 @@ def test_quant_static(pq, R, C, dtype, fold):
     np.testing.assert_array_equal(host(q), ref)
     assert np.all(host(rs) == S)
     assert np.any(np.abs(ref) == 127)
+
+
+# ------------------------------------------------------------------ streams, graphs, determinism
+
+def test_repeatable_bit_for_bit(pq):
+    """Every kernel is deterministic: two runs give identical bits (no order-dependent float sums)."""
+    x = dev(_x("det/x", 300, 4096, synth.BF16))
+    w = dev(_w("det/w", 200, 4096, synth.BF16, 0.001))
+    s = dev(np.exp(np.random.default_rng(7).uniform(-1, 1, 4096)).astype(np.float32))
+    announce("repeatability: calib, ssz, ssz_asym, quant, static quant")
+    r1 = (pq.sq_absmax_calib(x), pq.ssz_weight_qparams(w, s), pq.ssz_weight_qparams_asym(w, s),
+          pq.quant_per_token_i8(x, s))
+    r2 = (pq.sq_absmax_calib(x), pq.ssz_weight_qparams(w, s), pq.ssz_weight_qparams_asym(w, s),
+          pq.quant_per_token_i8(x, s))
+    flat = lambda r: [t for item in r for t in (item if isinstance(item, tuple) else (item,)) if t is not None]
+    for a, b in zip(flat(r1), flat(r2)):
+        assert torch.equal(a, b)
+
+
+def test_side_stream_ordering(pq):
+    """Work enqueued on a caller's stream runs in order on that stream and matches the default stream."""
+    x = _x("strm/x", 257, 4096, synth.BF16)
+    w = _w("strm/w", 384, 4096, synth.BF16)
+    ref_S = oracle.ssz(synth.widen(w), None, 8)["S"]
+    side = torch.cuda.Stream()
+    announce("side stream: calib -> smooth -> ssz -> quant -> gemm")
+    with torch.cuda.stream(side):
+        xd, wd = dev(x), dev(w)
+        ax = pq.sq_absmax_calib(xd, stream=side)
+        aw = pq.sq_absmax_calib(wd, stream=side)
+        sm = pq.sq_smooth_factors(ax, aw, 0.5, stream=side)
+        S, wq, _, _ = pq.ssz_weight_qparams(wd, None, stream=side)
+        xq, d = pq.quant_per_token_i8(xd, sm, stream=side)
+        y = pq.w8a8_gemm_dequant(xq, wq, d, S, stream=side)
+    side.synchronize()
+    np.testing.assert_array_equal(host(S), ref_S)
+    y0 = pq.w8a8_gemm_dequant(xq, wq, d, S)
+    assert torch.equal(y, y0)
+
+
+def test_graph_replay_matches_eager(pq):
+    """The whole path captured once in a HIP graph and replayed several times, with eager work and
+    synchronisation between replays; every replay equals the eager result (the path clears its own
+    outputs with fill kernels, no memset nodes)."""
+    x = dev(_x("graph/x", 512, 4096, synth.BF16))
+    w = dev(_w("graph/w", 1024, 4096, synth.BF16, 0.001))
+    ax = torch.empty(4096, dtype=torch.float32, device="cuda:0")
+    aw = torch.empty_like(ax)
+    s = torch.empty_like(ax)
+    S = torch.empty(1024, dtype=torch.float32, device="cuda:0")
+    wq = torch.empty((1024, 4096), dtype=torch.int8, device="cuda:0")
+    xq = torch.empty((512, 4096), dtype=torch.int8, device="cuda:0")
+    d = torch.empty(512, dtype=torch.float32, device="cuda:0")
+    y = torch.empty((512, 1024), dtype=torch.float32, device="cuda:0")
+
+    def path(stream):
+        pq.sq_absmax_calib(x, ax, stream=stream)
+        pq.sq_absmax_calib(w, aw, stream=stream)
+        pq.sq_smooth_factors(ax, aw, 0.5, s=s, stream=stream)
+        pq.ssz_weight_qparams(w, s, scale=S, wq=wq, want_stats=False, stream=stream)
+        pq.quant_per_token_i8(x, s, xq=xq, tok_scale=d, stream=stream)
+        pq.w8a8_gemm_fused(xq, wq, d, S, act="relu", out="f32", y=y, stream=stream)
+
+    announce("graph: eager reference")
+    path(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        path(cap)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    announce("graph: capture")
+    with torch.cuda.graph(g, stream=cap):
+        path(cap)
+    for r in range(4):
+        for t in (ax, aw, s, S, wq, xq, d, y):
+            t.fill_(7)  # eager work between replays
+        torch.cuda.synchronize()
+        announce(f"graph: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {r}"
