@@ -128,6 +128,41 @@ def kernel_source_sha(kernel_tag):
     return h.hexdigest()[:16]
 
 
+class _NoTimer:
+    """Stage runner without events (for graph capture)."""
+
+    @staticmethod
+    def stage(name, fn):
+        fn()
+
+
+def graph_step_ms(torch, step, steps):
+    """The same step captured once in a HIP graph and replayed `steps` times: the step's time without
+    per-launch host overhead (stage events are not captured).  None if capture is not possible."""
+    try:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            step(_NoTimer)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            step(_NoTimer)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    except RuntimeError:
+        return None
+
+
 def load_counters(kernel_tag, workload):
     """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE) on this workload, from the
     committed summaries under profiles/, if they were taken on the kernel's current source (hash match);
@@ -203,15 +238,15 @@ def main():
 
     def step(tm):
         for L in layers:
-            tm.stage("calib_x", lambda: pq.sq_absmax_calib(L["calib"], L["ax"], stream=stream))
-            tm.stage("calib_w", lambda: pq.sq_absmax_calib(L["w"], L["aw"], stream=stream))
-            tm.stage("smooth", lambda: pq.sq_smooth_factors(L["ax"], L["aw"], args.alpha, s=L["s"], stream=stream))
+            tm.stage("calib_x", lambda: pq.sq_absmax_calib(L["calib"], L["ax"], stream=None))
+            tm.stage("calib_w", lambda: pq.sq_absmax_calib(L["w"], L["aw"], stream=None))
+            tm.stage("smooth", lambda: pq.sq_smooth_factors(L["ax"], L["aw"], args.alpha, s=L["s"], stream=None))
             tm.stage("ssz", lambda: pq.ssz_weight_qparams(L["w"], L["s"], bits=8, scale=L["S"], wq=L["wq"],
-                                                          iters=L["it"], mse=L["mse"], stream=stream))
+                                                          iters=L["it"], mse=L["mse"], stream=None))
             tm.stage("quant", lambda: pq.quant_per_token_i8(L["x"], L["s"], xq=L["xq"], tok_scale=L["d"],
-                                                            stream=stream))
+                                                            stream=None))
             tm.stage("gemm", lambda: pq.w8a8_gemm_dequant(L["xq"], L["wq"], L["d"], L["S"], y=L["y"],
-                                                          stream=stream))
+                                                          stream=None))
 
     for _ in range(args.warmup):
         step(Timer(torch))
@@ -225,6 +260,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     tot = tm.totals()
+    graph_ms = graph_step_ms(torch, step, args.steps)
 
     # algorithmic work per step
     it_mean = {}
@@ -297,6 +333,7 @@ def main():
                    "tokens": 4096, "hidden": 4096, "calib_batches": B, "alpha": args.alpha, "bits": 8,
                    "parallelism": "single GPU"},
         "gpu_ms_per_step": gpu_ms, "step_tops": gemm_ops / (ms_per_step / 1e3) / 1e12,
+        "graph_ms_per_step": graph_ms,
         "stages": stages, "roofline": roof,
     }
     if not args.no_cpu_baseline:
