@@ -234,8 +234,8 @@ def main():
         L["y"] = torch.empty((c.T, c.N), dtype=torch.float32, device=dev)
         layers.append(L)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
 
+    # every launch goes to the current stream (None), so the same step also captures into a graph
     def step(tm):
         for L in layers:
             tm.stage("calib_x", lambda: pq.sq_absmax_calib(L["calib"], L["ax"], stream=None))
