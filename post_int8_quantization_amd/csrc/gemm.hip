@@ -64,24 +64,32 @@ __device__ __forceinline__ int swz(int row, int kc) {
 // ---------------------------------------------------------------------------
 // Prefill kernel pieces.
 //
-// Loads: global_load_lds_dwordx4 writes the 64 lanes' 16-byte chunks to 64
-// consecutive LDS slots (base in M0), so each lane picks the global chunk
+// Loads: buffer_load_dwordx4 ... lds writes the 64 lanes' 16-byte chunks to
+// 64 consecutive LDS slots (base in M0), so each lane picks the global chunk
 // that belongs in its slot under the XOR swizzle; the MFMA operand reads are
-// then bank-conflict free.  Chunks outside the matrix (M, N or K tails) load
-// from a 16-byte block of zeros.  The loads are issued with inline asm and
-// their completion is tracked only by explicit vmcnt waits that leave the
-// ST-2 younger stages in flight (the compiler, tracking such loads itself,
-// would drain the whole ring before every LDS read).  The asm has no output
-// registers -- the data goes to LDS through M0 -- so no register is ever
-// pending.  The barrier is an asm s_barrier with a memory clobber: the LDS
-// reads of a stage stay after it, and the loads into a buffer are issued
+// then bank-conflict free.  Each tile addresses its A and B panels through a
+// buffer descriptor whose size is the panel's rows times K: a chunk outside
+// the matrix (M or N tail rows, K tail) gets an offset past that size, and the
+// hardware's range check makes it load zeros.  So the per-step address work is
+// one add and one select per load, with no branch.  The loads are issued with
+// inline asm and their completion is tracked only by explicit vmcnt waits
+// that leave the ST-2 younger stages in flight (the compiler, tracking such
+// loads itself, would drain the whole ring before every LDS read).  The asm
+// has no output registers -- the data goes to LDS through M0 -- so no register
+// is ever pending.  The barrier is an asm s_barrier with a memory clobber: the
+// LDS reads of a stage stay after it, and the loads into a buffer are issued
 // only after every wave has passed it, i.e. finished reading that buffer.
+//
+// The loads of stage k+ST-1 are spread through the MFMA stream of step k, one
+// after each group of MFMAs that shares an A fragment, starting with the
+// first group.  Issued as one burst, the block's loads of a stage queue up in
+// the texture address unit and hold every wave's instruction stream (and so
+// its MFMAs) until the queue drains; spread out, they overlap the MFMAs and
+// still land a half step early.
 //
 // Tile order: the hardware deals block i to XCD i % 8; tile_of gives each XCD
 // a contiguous range of tiles, walked in groups of GM tile rows, so the
 // blocks resident on one XCD share A and B panels in that XCD's L2.
-__device__ const uint4 g_zero16 = {0u, 0u, 0u, 0u};
-
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 layout: vmcnt bits [3:0] and [15:14],
 // expcnt [6:4] and lgkmcnt [11:8] left at their maxima)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
@@ -100,13 +108,28 @@ __device__ __forceinline__ void tile_of(int tm, int tn, int gm_group, int& tile_
   tile_n = in / gsz;
 }
 
-__device__ __forceinline__ void dma16_lds(const void* g, uint32_t lds_byte_addr) {
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// raw buffer descriptor: 48-bit base, stride 0, size in bytes, range-checked offsets
+__device__ __forceinline__ u32x4 panel_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r.x = (uint32_t)a;
+  r.y = (uint32_t)(a >> 32) & 0xFFFFu;
+  r.z = bytes;
+  r.w = 0x00020000u;
+  return r;
+}
+
+constexpr uint32_t OFF_OUT = 0x80000000u;  // an offset past every panel (panels stay below 2^31 bytes)
+
+__device__ __forceinline__ void dma16_lds(u32x4 rsrc, uint32_t voff, uint32_t lds_byte_addr) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds\n\t"
       :
-      : "v"(g), "s"(lds_byte_addr)
+      : "v"(voff), "s"(rsrc), "s"(lds_byte_addr)
       : "memory", "m0");
 }
 
@@ -144,7 +167,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 
 // v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent)
-template <int OUT, bool NTS>
+template <int OUT, bool NTS = true>
 __device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
                                           float inv_out, const Epi& epi) {
   if (epi.bias) v = v + bn;
@@ -162,13 +185,11 @@ __device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, flo
 }
 
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, bool PERSIST, int OCC, bool NTS = true,
-          int OUT = EPI_F32>
-__global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
-                                                          const float* __restrict__ ts, const float* __restrict__ cs,
-                                                          int M, int N, int K, void* __restrict__ Y,
-                                                          int32_t* __restrict__ ACC, int tiles_m, int tiles_n,
-                                                          Epi epi) {
+template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, int OUT = EPI_F32>
+__global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                        const float* __restrict__ ts, const float* __restrict__ cs,
+                                                        int M, int N, int K, void* __restrict__ Y,
+                                                        int32_t* __restrict__ ACC, int tiles_m, int tiles_n, Epi epi) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / MF, FN = TN / MF;
@@ -180,8 +201,10 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
   static_assert(ST >= 2 && ST <= 8, "2..8 stages");
   using acc_t = typename std::conditional<MF == 32, v16i, v4i>::type;
   constexpr int NR = MF == 32 ? 16 : 4;
-  constexpr int PER = A_PW + B_PW;  // loads per stage per thread
+  constexpr int PER = A_PW + B_PW;                     // loads per stage per thread
+  constexpr int KS = (MF == 32 ? 2 : 1) * (BK / 64);  // MFMA k-steps per K step
   static_assert((ST - 2) * PER <= 63, "vmcnt range");
+  static_assert(PER <= FM * KS, "one load after each MFMA group at most");
   __shared__ uint4 sm[ST * S_CH];
   __shared__ __attribute__((aligned(16))) float s_ts[BM];  // the tile's token scales
   __shared__ float s_cs[BN];                               // and channel scales
@@ -194,14 +217,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lk = lane >> 4;
   const uint32_t sm_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
-  const int ntiles = tiles_m * tiles_n;
-  // persistent: block b takes virtual ids b, b + grid, ...; the grid is a multiple of 8 so every
-  // virtual id stays on the block's XCD and tile_of keeps each round's tiles grouped per XCD
-  for (int vt = blockIdx.x; vt < ntiles; vt += (PERSIST ? gridDim.x : ntiles)) {
   int tile_m, tile_n;
-  tile_of(tiles_m, tiles_n, GM, tile_m, tile_n, vt, PERSIST ? ntiles : gridDim.x);
+  tile_of(tiles_m, tiles_n, GM, tile_m, tile_n, blockIdx.x, gridDim.x);
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  __syncthreads();  // the previous tile's epilogue and last K steps are done with LDS
   for (int t = tid; t < BM; t += NW * 64) s_ts[t] = m0 + t < M ? ts[m0 + t] : 0.0f;
   for (int t = tid; t < BN; t += NW * 64) {
     const bool in = n0 + t < N;
@@ -209,45 +227,38 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
     s_b[t] = (in && epi.bias) ? epi.bias[n0 + t] : 0.0f;
     if constexpr (OUT == EPI_I8) s_nr[t] = (in && epi.next_s) ? 1.0f / epi.next_s[n0 + t] : 1.0f;
   }
-  __syncthreads();
 
-  // per-lane source rows/chunks of the loads (the LDS slot is fixed by lane order and the swizzle)
-  const int8_t* a_src[A_PW];
-  bool a_ok[A_PW];
-  int a_k[A_PW];
+  // the tile's A and B panels (at most BM / BN rows of K bytes) and each lane's offsets into them
+  const int rows_a = M - m0 < BM ? M - m0 : BM, rows_b = N - n0 < BN ? N - n0 : BN;
+  const u32x4 rsrc_a = panel_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
+  const u32x4 rsrc_b = panel_rsrc(B + (int64_t)n0 * K, (uint32_t)rows_b * (uint32_t)K);
+  uint32_t a_off[A_PW], b_off[B_PW];
+  int a_k[A_PW], b_k[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
     const int slot = (i * NW + wave) * 64 + lane;
     const int row = slot / KC;
     a_k[i] = swz<KC>(row, slot % KC) * 16;
-    a_ok[i] = m0 + row < M;
-    a_src[i] = A + (int64_t)(a_ok[i] ? m0 + row : 0) * K;
+    a_off[i] = row < rows_a ? (uint32_t)(row * K + a_k[i]) : OFF_OUT;
   }
-  const int8_t* b_src[B_PW];
-  bool b_ok[B_PW];
-  int b_k[B_PW];
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
     const int slot = (i * NW + wave) * 64 + lane;
     const int row = slot / KC;
     b_k[i] = swz<KC>(row, slot % KC) * 16;
-    b_ok[i] = n0 + row < N;
-    b_src[i] = B + (int64_t)(b_ok[i] ? n0 + row : 0) * K;
+    b_off[i] = row < rows_b ? (uint32_t)(row * K + b_k[i]) : OFF_OUT;
   }
 
-  auto issue = [&](int buf, int k0) {
+  // load p (0..PER-1) of the stage that starts at byte k0 of K, into LDS buffer buf
+  auto load = [&](int p, int buf, int k0) {
     const uint32_t base = sm_base + (uint32_t)(buf * S_CH) * 16u;
-#pragma unroll
-    for (int i = 0; i < A_PW; ++i) {
-      const int gk = k0 + a_k[i];
-      const void* src = (a_ok[i] && gk < K) ? (const void*)(a_src[i] + gk) : (const void*)&g_zero16;
-      dma16_lds(src, base + (uint32_t)((i * NW + wave) * 64) * 16u);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const int gk = k0 + b_k[i];
-      const void* src = (b_ok[i] && gk < K) ? (const void*)(b_src[i] + gk) : (const void*)&g_zero16;
-      dma16_lds(src, base + (uint32_t)(A_CH + (i * NW + wave) * 64) * 16u);
+    if (p < A_PW) {
+      const uint32_t v = k0 + a_k[p] < K ? a_off[p] + (uint32_t)k0 : OFF_OUT;
+      dma16_lds(rsrc_a, v, base + (uint32_t)((p * NW + wave) * 64) * 16u);
+    } else {
+      const int q = p - A_PW;
+      const uint32_t v = k0 + b_k[q] < K ? b_off[q] + (uint32_t)k0 : OFF_OUT;
+      dma16_lds(rsrc_b, v, base + (uint32_t)(A_CH + (q * NW + wave) * 64) * 16u);
     }
   };
 
@@ -259,39 +270,50 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[i][j][r] = 0;
 
-  auto compute = [&](int buf) {
+  // the MFMAs of the stage in LDS buffer buf; with `more`, load p of the stage at byte nk0 of K
+  // into buffer nbuf goes right after MFMA group p
+  auto compute = [&](int buf, int nbuf, int nk0, bool more) {
     const uint4* sa = sm + buf * S_CH;
     const uint4* sb = sa + A_CH;
-    constexpr int KS = (MF == 32 ? 2 : 1) * (BK / 64);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int rl = MF == 32 ? (lane & 31) : lr;
       const int ch = MF == 32 ? ks * 2 + (lane >> 5) : ks * 4 + lk;
       uint4 a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * TM + i * MF + rl;
-        a[i] = sa[row * KC + swz<KC>(row, ch)];
-      }
-#pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int row = wn * TN + j * MF + rl;
         b[j] = sb[row * KC + swz<KC>(row, ch)];
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * TM + i * MF + rl;
+        a[i] = sa[row * KC + swz<KC>(row, ch)];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           if constexpr (MF == 32) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
           else acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
         }
+        const int g = ks * FM + i;
+        if (g < PER) {
+          __builtin_amdgcn_sched_barrier(0);  // keep the load between its MFMA groups
+          if (more) load(g, nbuf, nk0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   };
 
   const int nk = (K + BK - 1) / BK;
+  __syncthreads();  // scales staged
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
-    if (s < nk) issue(s, s * BK);
+    if (s < nk)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) load(p, s, s * BK);
 
   int buf = 0;
   for (int k = 0; k < nk; ++k) {
@@ -307,8 +329,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
       default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER)); break;
     }
     block_barrier();  // step k is in LDS for every wave; every wave is done with step k-1's buffer
-    if (k + ST - 1 < nk) issue(buf == 0 ? ST - 1 : buf - 1, (k + ST - 1) * BK);
-    compute(buf);
+    compute(buf, buf == 0 ? ST - 1 : buf - 1, (k + ST - 1) * BK, k + ST - 1 < nk);
     buf = buf + 1 == ST ? 0 : buf + 1;
   }
 
@@ -337,14 +358,13 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void k_gemm_pipe(const int8_t* __
           const int m = m0 + rl0 + q;
           const int a = acc[i][j][g * 4 + q];
           if (full || (m < M && n < N)) {
-            epi_store<OUT, NTS>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
+            epi_store<OUT>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
             if (ACC) ACC[(int64_t)m * N + n] = a;
           }
         }
       }
     }
   }
-  }  // tile loop
 }
 
 // ---------------------------------------------------------------------------
@@ -503,7 +523,7 @@ template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, int OUT>
 hipError_t launch_tiled(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
                         void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  k_gemm_pipe<BM, BN, BK, WM, WN, ST, 4, MF, false, 1, true, OUT><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
+  k_gemm_pipe<BM, BN, BK, WM, WN, ST, 4, MF, OUT><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
       xq, wq, ts, cs, M, N, K, y, acc, tm, tn, epi);
   return hipGetLastError();
 }
