@@ -88,7 +88,7 @@ __device__ __forceinline__ int swz(int row, int kc) {
 // still land a half step early.
 //
 // Tile order: the hardware deals block i to XCD i % 8; tile_of gives each XCD
-// a contiguous range of tiles, walked in groups of GM tile rows, so the
+// a contiguous range of tiles, walked in groups of gm tile rows, so the
 // blocks resident on one XCD share A and B panels in that XCD's L2.
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 layout: vmcnt bits [3:0] and [15:14],
 // expcnt [6:4] and lgkmcnt [11:8] left at their maxima)
@@ -166,12 +166,15 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent)
-template <int OUT, bool NTS = true>
+// v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent).
+// GEN = false is the plain dequantization (no bias, no activation): the per-element tests drop out.
+template <int OUT, bool NTS = true, bool GEN = true>
 __device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
                                           float inv_out, const Epi& epi) {
-  if (epi.bias) v = v + bn;
-  v = epi_act(v, epi.act);
+  if constexpr (GEN) {
+    if (epi.bias) v = v + bn;
+    v = epi_act(v, epi.act);
+  }
   if constexpr (OUT == EPI_F32) {
     float* y = reinterpret_cast<float*>(Y) + idx;
     if constexpr (NTS) __builtin_nontemporal_store(v, y);  // written once, not re-read
@@ -179,17 +182,18 @@ __device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, flo
   } else if constexpr (OUT == EPI_BF16) {
     reinterpret_cast<uint16_t*>(Y)[idx] = bf16_rne(v);
   } else {
-    const float xh = epi.next_s ? v * nrn : v;
-    reinterpret_cast<int8_t*>(Y)[idx] = (int8_t)(int)code_f(xh, inv_out, 127.0f);
+    // nrn is exactly 1 without next_s, and v * 1 = v
+    reinterpret_cast<int8_t*>(Y)[idx] = (int8_t)(int)code_f(v * nrn, inv_out, 127.0f);
   }
 }
 
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int GM, int MF, int OUT = EPI_F32>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, int OUT = EPI_F32>
 __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                         const float* __restrict__ ts, const float* __restrict__ cs,
                                                         int M, int N, int K, void* __restrict__ Y,
-                                                        int32_t* __restrict__ ACC, int tiles_m, int tiles_n, Epi epi) {
+                                                        int32_t* __restrict__ ACC, int tiles_m, int tiles_n, int gm,
+                                                        Epi epi) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / MF, FN = TN / MF;
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   const int lr = lane & 15, lk = lane >> 4;
   const uint32_t sm_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
   int tile_m, tile_n;
-  tile_of(tiles_m, tiles_n, GM, tile_m, tile_n, blockIdx.x, gridDim.x);
+  tile_of(tiles_m, tiles_n, gm, tile_m, tile_n, blockIdx.x, gridDim.x);
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   for (int t = tid; t < BM; t += NW * 64) s_ts[t] = m0 + t < M ? ts[m0 + t] : 0.0f;
   for (int t = tid; t < BN; t += NW * 64) {
@@ -335,36 +339,43 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
 
   // epilogue: dequantize and store.  Each lane holds, per fragment, one column and groups of 4
   // consecutive rows (16x16: rows 4*(lane/16)+0..3; 32x32: rows 8*g + 4*(lane/32) + 0..3, g = 0..3),
-  // so the token scales of a group are one 16-byte LDS read.
+  // so the token scales of a group are one 16-byte LDS read.  The plain dequantization (no bias,
+  // no activation, no int32 copy) is its own loop, free of per-element tests.
   const bool full = m0 + BM <= M && n0 + BN <= N;
   const float inv_out = OUT == EPI_I8 ? 1.0f / epi.out_scale[0] : 0.0f;
   constexpr int NG = NR / 4;
+  auto epilogue = [&](auto gen) {
+    constexpr bool GEN = decltype(gen)::value;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
-    const int n = n0 + cl;
-    const float csn = s_cs[cl];
-    const float bn = s_b[cl];
-    const float nrn = OUT == EPI_I8 ? s_nr[cl] : 1.0f;
+    for (int j = 0; j < FN; ++j) {
+      const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
+      const int n = n0 + cl;
+      const float csn = s_cs[cl];
+      const float bn = s_b[cl];
+      const float nrn = OUT == EPI_I8 ? s_nr[cl] : 1.0f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int rl0 = wm * TM + i * MF + (MF == 32 ? 8 * g + 4 * (lane >> 5) : lk * 4);
-        const float4 t4 = *reinterpret_cast<const float4*>(&s_ts[rl0]);
-        const float tsv[4] = {t4.x, t4.y, t4.z, t4.w};
+        for (int g = 0; g < NG; ++g) {
+          const int rl0 = wm * TM + i * MF + (MF == 32 ? 8 * g + 4 * (lane >> 5) : lk * 4);
+          const float4 t4 = *reinterpret_cast<const float4*>(&s_ts[rl0]);
+          const float tsv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + rl0 + q;
-          const int a = acc[i][j][g * 4 + q];
-          if (full || (m < M && n < N)) {
-            epi_store<OUT>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
-            if (ACC) ACC[(int64_t)m * N + n] = a;
+          for (int q = 0; q < 4; ++q) {
+            const int m = m0 + rl0 + q;
+            const int a = acc[i][j][g * 4 + q];
+            if (full || (m < M && n < N)) {
+              epi_store<OUT, true, GEN>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
+              if constexpr (GEN)
+                if (ACC) ACC[(int64_t)m * N + n] = a;
+            }
           }
         }
       }
     }
-  }
+  };
+  if (epi.bias || epi.act != ACT_NONE || ACC) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -523,8 +534,11 @@ template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, int OUT>
 hipError_t launch_tiled(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
                         void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  k_gemm_pipe<BM, BN, BK, WM, WN, ST, 4, MF, OUT><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
-      xq, wq, ts, cs, M, N, K, y, acc, tm, tn, epi);
+  // tile-row group: 4 rows share the A and B panels best in L2; a large fp32 output is written
+  // fastest with 1 (the tiles in flight on an XCD then cover whole output rows)
+  const int gm = (OUT == EPI_F32 && tm * tn > 256) ? 1 : 4;
+  k_gemm_pipe<BM, BN, BK, WM, WN, ST, MF, OUT><<<(unsigned)(tm * tn), WM * WN * 64, 0, stream>>>(
+      xq, wq, ts, cs, M, N, K, y, acc, tm, tn, gm, epi);
   return hipGetLastError();
 }
 

@@ -250,6 +250,34 @@ def test_gemm_deterministic(pq):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 1000, 8192), (65, 130, 1040), (300, 520, 1040), (257, 259, 4096),
+                                   (1024, 1024, 4096), (512, 4352, 1024), (4352, 4096, 64), (4300, 4100, 80)])
+@pytest.mark.parametrize("out", ["f32", "bf16", "i8"])
+def test_gemm_plain_epilogue(pq, M, N, K, out):
+    """No bias, no activation, no int32 copy: the prefill kernel's separate plain-dequantization loop,
+    bit-exact against the oracle's fp32 epilogue (also with the int8 output's next-layer fold)."""
+    rng = np.random.default_rng(M * 13 + N * 7 + K + len(out))
+    a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    ts = rng.uniform(0.002, 0.02, M).astype(np.float32)
+    cs = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    ns = np.exp(rng.uniform(-1, 1, N)).astype(np.float32) if out == "i8" and M % 2 == 1 else None
+    acc_ref = oracle.gemm_i8(a, b)
+    code = {"f32": oracle.OUT_F32, "bf16": oracle.OUT_BF16, "i8": oracle.OUT_I8}[out]
+    y32 = oracle.epilogue(acc_ref, ts, cs, None, oracle.ACT_NONE)
+    osc = np.float32(np.max(np.abs(y32)) / 100.0) if out == "i8" else 1.0
+    ref = oracle.epilogue(acc_ref, ts, cs, None, oracle.ACT_NONE, code, ns, osc)
+    announce(f"w8a8_gemm_fused plain M={M} N={N} K={K} out={out} next_s={ns is not None}")
+    y = pq.w8a8_gemm_fused(dev(a), dev(b), dev(ts), dev(cs), None, "none", out, None if ns is None else dev(ns),
+                           dev(np.array([osc], np.float32)) if out == "i8" else None)
+    got = host(y.view(torch.int16)).view(np.uint16) if out == "bf16" else host(y)
+    np.testing.assert_array_equal(got, ref)
+    if out == "f32":
+        announce(f"w8a8_gemm_dequant plain M={M} N={N} K={K}")
+        y2 = pq.w8a8_gemm_dequant(dev(a), dev(b), dev(ts), dev(cs))
+        np.testing.assert_array_equal(host(y2), ref)
+
+
 # ------------------------------------------------------------------ fused epilogue
 
 @pytest.mark.parametrize("M,N,K", [(16, 1000, 8192), (5, 77, 160), (64, 300, 4096), (300, 520, 1040),
