@@ -53,8 +53,9 @@ __device__ __forceinline__ PassSums row_pass(const float (&wh)[CPT][16], const d
   r.b = wave_sum((int)bq);
   constexpr int NW = TPR / kWave;
   if constexpr (NW > 1) {
+    // red_d / red_i point at this pass's half of a two-pass slot ring: the previous readers of
+    // these slots (two passes ago) finished before the barrier of the pass in between
     const int w = tid / kWave;
-    __syncthreads();  // previous readers of the LDS slots are done
     if ((tid & (kWave - 1)) == 0) {
       red_d[w] = r.a;
       red_i[w] = r.b;
@@ -112,6 +113,24 @@ __device__ __forceinline__ void load_row(const void* __restrict__ w, int64_t n, 
   }
 }
 
+// e / K in fp64.  For a power-of-two K the quotient is an exact scaling, so it is taken with
+// ldexp (one instruction) instead of the division sequence; the result is the same double.
+struct DivK {
+  double kd;
+  int lg;  // log2 K when K is a power of two, else -1
+  __device__ __forceinline__ double operator()(double e) const {
+    if (lg >= 0) return __builtin_ldexp(e, -lg);
+    return e / kd;
+  }
+};
+
+__device__ __forceinline__ DivK make_divk(int64_t K) {
+  DivK d;
+  d.kd = (double)K;
+  d.lg = (K & (K - 1)) == 0 ? 63 - __builtin_clzll((unsigned long long)K) : -1;
+  return d;
+}
+
 // K * mse(S) from the pass sums: W2 - 2 S A + S^2 B, never below 0
 __device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) {
   const double Sd = (double)S;
@@ -133,11 +152,13 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
   constexpr bool WIDE = WIDE_MODE == 1;
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
   __shared__ double red_d[NW];
-  __shared__ int red_i[NW];
   __shared__ float red_f[NW];
+  __shared__ double ring_d[2][NW];  // pass sums, alternating halves
+  __shared__ int ring_i[2][NW];
+  int par = 0;
   const int tid = threadIdx.x;
   const int64_t nchunk = K / 16;
-  const double Kd = (double)K;
+  const DivK per_elem = make_divk(K);
 
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
     float wh[CPT][16];
@@ -175,8 +196,9 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
     // MinMax init
     float S = m / QMAX;
     S = S < min_scale ? min_scale : S;
-    PassSums cur = row_pass<TPR, CPT, WIDE>(wh, wd, S, QMAX, red_d, red_i, tid);
-    double best = sq_err(w2, S, cur) / Kd;
+    PassSums cur = row_pass<TPR, CPT, WIDE>(wh, wd, S, QMAX, ring_d[par], ring_i[par], tid);
+    par ^= 1;
+    double best = per_elem(sq_err(w2, S, cur));
     double A = cur.a;
     int B = cur.b;
 
@@ -187,8 +209,9 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
       if (B == 0) break;
       float Sc = (float)(A / (double)B);
       Sc = Sc < min_scale ? min_scale : Sc;
-      const PassSums p = row_pass<TPR, CPT, WIDE>(wh, wd, Sc, QMAX, red_d, red_i, tid);
-      const double c = sq_err(w2, Sc, p) / Kd;
+      const PassSums p = row_pass<TPR, CPT, WIDE>(wh, wd, Sc, QMAX, ring_d[par], ring_i[par], tid);
+      par ^= 1;
+      const double c = per_elem(sq_err(w2, Sc, p));
       const double d = best - c;
       const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
       if (c < best) {
@@ -247,7 +270,7 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
     if (tid == 0) {
       scale[n] = S;
       if (iters) iters[n] = it;
-      if (mse) mse[n] = e_dir / Kd;
+      if (mse) mse[n] = per_elem(e_dir);
     }
   }
 }
@@ -303,8 +326,8 @@ __device__ __forceinline__ PassSumsA row_pass_asym(const float (&wh)[CPT][16], c
   r.c = (double)wave_sum((int)cq);
   constexpr int NW = TPR / kWave;
   if constexpr (NW > 1) {
+    // red_d points at this pass's half of a two-pass slot ring (see row_pass)
     const int w = tid / kWave;
-    __syncthreads();  // previous readers of the LDS slots are done
     if ((tid & (kWave - 1)) == 0) {
       red_d[w] = r.a;
       red_d[NW + w] = r.b;
@@ -346,9 +369,12 @@ __global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, in
   constexpr bool WIDE = WIDE_MODE == 1;
   __shared__ double red_d[3 * NW];
   __shared__ float red_f[2 * NW];
+  __shared__ double ring_d[2][3 * NW];  // pass sums, alternating halves
+  int par = 0;
   const int tid = threadIdx.x;
   const int64_t nchunk = K / 16;
   const double Kd = (double)K;
+  const DivK per_elem = make_divk(K);
   const double pad = (double)((int64_t)TPR * CPT * 16 - K);  // zero slots per row
 
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
@@ -406,8 +432,9 @@ __global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, in
       const float z0 = -128.0f - __builtin_rintf(lo * inv0);
       Z = (int)fminf(fmaxf(z0, -128.0f), 127.0f);
     }
-    PassSumsA cur = row_pass_asym<TPR, CPT, WIDE>(wh, wd, S, Z, pad, red_d, tid);
-    double best = sq_err_asym(w2, w1, Kd, S, Z, cur) / Kd;
+    PassSumsA cur = row_pass_asym<TPR, CPT, WIDE>(wh, wd, S, Z, pad, ring_d[par], tid);
+    par ^= 1;
+    double best = per_elem(sq_err_asym(w2, w1, Kd, S, Z, cur));
 
     int it = 0;
     for (int i = 1; i <= max_iter; ++i) {
@@ -415,13 +442,14 @@ __global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, in
       const double det = Kd * cur.b - cur.c * cur.c;  // exact: integers below 2^53
       if (det <= 0.0) break;
       const double a = (Kd * cur.a - w1 * cur.c) / det;
-      const double b = (w1 - a * cur.c) / Kd;
+      const double b = per_elem(w1 - a * cur.c);
       float Sc = (float)a;
       Sc = Sc < min_scale ? min_scale : Sc;
       const double zr = __builtin_rint(-b / a);
       const int Zc = zr < -128.0 ? -128 : (zr > 127.0 ? 127 : (int)zr);
-      const PassSumsA p = row_pass_asym<TPR, CPT, WIDE>(wh, wd, Sc, Zc, pad, red_d, tid);
-      const double c = sq_err_asym(w2, w1, Kd, Sc, Zc, p) / Kd;
+      const PassSumsA p = row_pass_asym<TPR, CPT, WIDE>(wh, wd, Sc, Zc, pad, ring_d[par], tid);
+      par ^= 1;
+      const double c = per_elem(sq_err_asym(w2, w1, Kd, Sc, Zc, p));
       const double d = best - c;
       const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
       if (c < best) {
@@ -475,7 +503,7 @@ __global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, in
       scale[n] = S;
       zero_point[n] = Z;
       if (iters) iters[n] = it;
-      if (mse) mse[n] = e_dir / Kd;
+      if (mse) mse[n] = per_elem(e_dir);
     }
   }
 }
