@@ -166,27 +166,54 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Output element type and size of each epilogue output.
+template <int OUT>
+struct EpiOut;
+template <>
+struct EpiOut<EPI_F32> {
+  typedef float T;
+  static constexpr int kBytes = 4;
+};
+template <>
+struct EpiOut<EPI_BF16> {
+  typedef uint16_t T;
+  static constexpr int kBytes = 2;
+};
+template <>
+struct EpiOut<EPI_I8> {
+  typedef int8_t T;
+  static constexpr int kBytes = 1;
+};
+
 // v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent).
 // GEN = false is the plain dequantization (no bias, no activation): the per-element tests drop out.
-template <int OUT, bool NTS = true, bool GEN = true>
-__device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
-                                          float inv_out, const Epi& epi) {
+template <int OUT, bool GEN>
+__device__ __forceinline__ typename EpiOut<OUT>::T epi_value(float v, float bn, float nrn, float inv_out,
+                                                             const Epi& epi) {
   if constexpr (GEN) {
     if (epi.bias) v = v + bn;
     v = epi_act(v, epi.act);
   }
-  if constexpr (OUT == EPI_F32) {
-    float* y = reinterpret_cast<float*>(Y) + idx;
-    if constexpr (NTS) __builtin_nontemporal_store(v, y);  // written once, not re-read
-    else *y = v;
-  } else if constexpr (OUT == EPI_BF16) {
-    reinterpret_cast<uint16_t*>(Y)[idx] = bf16_rne(v);
-  } else {
-    // nrn is exactly 1 without next_s, and v * 1 = v
-    reinterpret_cast<int8_t*>(Y)[idx] = (int8_t)(int)code_f(v * nrn, inv_out, 127.0f);
-  }
+  if constexpr (OUT == EPI_F32) return v;
+  else if constexpr (OUT == EPI_BF16) return bf16_rne(v);
+  else return (int8_t)(int)code_f(v * nrn, inv_out, 127.0f);  // nrn is exactly 1 without next_s, and v * 1 = v
 }
 
+template <int OUT, bool NTS = true, bool GEN = true>
+__device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
+                                          float inv_out, const Epi& epi) {
+  const typename EpiOut<OUT>::T o = epi_value<OUT, GEN>(v, bn, nrn, inv_out, epi);
+  typename EpiOut<OUT>::T* y = reinterpret_cast<typename EpiOut<OUT>::T*>(Y) + idx;
+  if constexpr (OUT == EPI_F32 && NTS) __builtin_nontemporal_store(o, y);  // written once, not re-read
+  else *y = o;
+}
+
+// smallest pass count p (a divisor of fm) whose 1/p of a bm-row tile, at `pitch` bytes per row, fits `area` bytes
+constexpr int staged_passes(int fm, int bm, int pitch, int area) {
+  for (int p = 1; p <= fm; ++p)
+    if (fm % p == 0 && (bm / p) * pitch <= area) return p;
+  return 0;
+}
 
 template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, int OUT = EPI_F32>
 __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
@@ -374,8 +401,78 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
       }
     }
   };
-  if (epi.bias || epi.act != ACT_NONE || ACC) epilogue(std::true_type{});
-  else epilogue(std::false_type{});
+  // Staged epilogue: the tile's outputs, converted, go through the (now idle) stage buffers in row-major
+  // order and leave as 16-byte row pieces -- a wave store covers whole rows of the tile (1 KB per
+  // instruction) instead of 64 single elements, and int8 / bf16 rows are written as full lines instead of
+  // 16-32-byte runs.  In NPASS passes of FPP fragment rows per wave; rows need 16-byte alignment, so N * size
+  // must be a multiple of 16 (else, and with the int32 copy, the per-element loop above).
+  constexpr int E = EpiOut<OUT>::kBytes;
+  constexpr int PITCH = BN * E + 16;
+  constexpr int NPASS = staged_passes(FM, BM, PITCH, ST * S_CH * 16);
+  static_assert(NPASS > 0, "the staged tile fits the stage buffers");
+  constexpr int FPP = FM / NPASS;            // fragment rows per wave and pass
+  constexpr int BAND = FPP * MF;             // rows per wave and pass
+  constexpr int RPP = WM * BAND;             // tile rows per pass
+  constexpr int LPR = BN * E / 16;           // lanes per tile row
+  static_assert(LPR <= 64 && 64 % LPR == 0, "whole rows per wave store");
+  constexpr int RPI = 64 / LPR;              // tile rows per wave store
+  static_assert(RPP % (RPI * NW) == 0, "passes split evenly over the waves");
+  auto staged = [&](auto gen) {
+    constexpr bool GEN = decltype(gen)::value;
+    typedef typename EpiOut<OUT>::T OT;
+    uint8_t* tl = reinterpret_cast<uint8_t*>(sm);
+    __syncthreads();  // every wave is done with the stage buffers
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
+        const float csn = s_cs[cl];
+        const float bn = s_b[cl];
+        const float nrn = OUT == EPI_I8 ? s_nr[cl] : 1.0f;
+#pragma unroll
+        for (int ii = 0; ii < FPP; ++ii) {
+          const int i = p * FPP + ii;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const int ro = ii * MF + (MF == 32 ? 8 * g + 4 * (lane >> 5) : lk * 4);  // row in the wave's band
+            const float4 t4 = *reinterpret_cast<const float4*>(&s_ts[wm * TM + p * BAND + ro]);
+            const float tsv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<OT*>(tl + (wm * BAND + ro + q) * PITCH + cl * E) =
+                  epi_value<OUT, GEN>((float)acc[i][j][g * 4 + q] * (tsv[q] * csn), bn, nrn, inv_out, epi);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < RPP / (RPI * NW); ++it) {
+        const int r = (it * NW + wave) * RPI + lane / LPR, c = lane % LPR;  // tile row of the pass, piece
+        const uint4 v = *reinterpret_cast<const uint4*>(tl + r * PITCH + c * 16);
+        const int m = m0 + (r / BAND) * TM + p * BAND + r % BAND;
+        const int n = n0 + c * (16 / E);
+        if (full || (m < M && n < N)) {
+          const u32x4 w4 = {v.x, v.y, v.z, v.w};
+          __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(Y) +
+                                                                   ((int64_t)m * N + n) * E));
+        }
+      }
+      if (p + 1 < NPASS) __syncthreads();  // the pass's pieces are read before the next pass writes
+    }
+  };
+  const bool gen = epi.bias || epi.act != ACT_NONE;
+  // measured: the staging pays for int8 and bf16 outputs everywhere and for fp32 on 256x256 tiles; fp32 on the
+  // smaller tiles (one pass of a 128-row tile at 1 KB a row) was 8% slower than the per-element stores
+  constexpr bool kStage = OUT != EPI_F32 || (BM == 256 && BN == 256);
+  if (kStage && ACC == nullptr && ((int64_t)N * E) % 16 == 0) {
+    if (gen) staged(std::true_type{});
+    else staged(std::false_type{});
+  } else if (gen || ACC) {
+    epilogue(std::true_type{});
+  } else {
+    epilogue(std::false_type{});
+  }
 }
 
 // ---------------------------------------------------------------------------
