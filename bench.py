@@ -185,7 +185,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the path "
-              "shards by token rows or weight rows with no collective on the hot path, and this build measures "
+              "shards by token rows or weight rows with no collective on the hot path, and this benchmark measures "
               "the one-GPU share.", file=sys.stderr)
         sys.exit(2)
 
