@@ -65,6 +65,7 @@ def _load():
             "o_mse_row_asym": [vp, vp, i64, f32, ci],
             "o_lsq_affine": [vp, vp, i64, vp, vp],
             "o_ssz_asym": [vp, vp, i64, i64, ci, f64, f32, vp, vp, vp, vp, vp, vp],
+            "o_ssz_variant": [vp, vp, i64, i64, ci, ci, f64, f32, ci, ci, ci, vp, vp, vp],
             "o_epilogue": [vp, i64, i64, vp, vp, vp, ci, ci, vp, f32, vp],
             "o_absmax_tensor": [vp, i64, i64, vp, ci, vp],
             "o_ema_update": [vp, f32, f32, ci],
@@ -180,6 +181,23 @@ def ssz(w, s=None, bits=8, max_iter=20, thr=1e-10, min_scale=1e-5, hist=False):
     if hist:
         out["hist"] = h
     return out
+
+
+def ssz_variant(w, s=None, bits=8, max_iter=20, thr=1e-10, min_scale=1e-5, conv_and=False, err_sum=False,
+                global_loop=False):
+    """Diagnostic only: the symmetric search under the alternative readings (both convergence tests required,
+    summed instead of mean error, rows iterating until all have converged).  Returns dict(S, iters, mse) with mse
+    the mean squared error of the final scale."""
+    w = _f32(w)
+    N, K = w.shape
+    s = None if s is None else _f32(s)
+    S = np.empty(N, dtype=np.float32)
+    it = np.empty(N, dtype=np.int32)
+    mse = np.empty(N, dtype=np.float64)
+    _check(_load().o_ssz_variant(w.ctypes.data, _p(s), N, K, int(bits), int(max_iter), float(thr), float(min_scale),
+                                 int(bool(conv_and)), int(bool(err_sum)), int(bool(global_loop)), S.ctypes.data,
+                                 it.ctypes.data, mse.ctypes.data), "ssz_variant")
+    return dict(S=S, iters=it, mse=mse)
 
 
 def quant_row_asym(r, S, Z):

@@ -287,6 +287,99 @@ int o_ssz(const float* w, const float* s, int64_t N, int64_t K, int bits, int ma
 }
 
 /* ---------------------------------------------------------------------------
+ * Diagnostic: the symmetric SSZ search under the other readings of the
+ * silent points, to measure how much each reading matters (never used for
+ * parity; o_ssz above is the reading the kernels follow).
+ *   conv_and    -- a row converges only when BOTH the relative and the
+ *                  absolute change are under the threshold ([SSZ] lists the
+ *                  two tests without saying how they combine).
+ *   err_sum     -- the error is the channel's SUM of squared differences
+ *                  instead of its mean (the relative test is unchanged, the
+ *                  absolute one sees K times larger changes).
+ *   global_loop -- rows do not stop on their own: every row keeps taking
+ *                  steps until all rows have converged at least once, or the
+ *                  iteration limit ("exit when all channels have converged").
+ * Each candidate is still kept only if strictly better.  Outputs S[N],
+ * iters[N] (steps whose candidate the row evaluated) and mse[N] (the mean
+ * squared error of the final scale, whatever the reading; may be NULL).
+ * ------------------------------------------------------------------------- */
+int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits, int max_iter, double thr,
+                  float min_scale, int conv_and, int err_sum, int global_loop, float* S, int32_t* iters,
+                  double* mse) {
+  if (!w || !S || !iters || N < 0 || K <= 0) return O_EARG;
+  if (bits != 8 && bits != 4) return O_EARG;
+  if (max_iter < 0 || !(thr >= 0.0) || !(min_scale > 0.0f)) return O_EARG;
+  if (!all_finite(w, N * K)) return O_ENONFINITE;
+  const int qmax = bits == 8 ? 127 : 7;
+  const double scale = err_sum ? (double)K : 1.0;  /* mean -> sum */
+  float* wh = (float*)malloc(sizeof(float) * (size_t)(N * K));
+  int8_t* q = (int8_t*)malloc((size_t)K);
+  double* best = (double*)malloc(sizeof(double) * (size_t)N);
+  double* A = (double*)malloc(sizeof(double) * (size_t)N);
+  int64_t* B = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+  char* done = (char*)malloc((size_t)N);
+  if (!wh || !q || !best || !A || !B || !done) {
+    free(wh); free(q); free(best); free(A); free(B); free(done);
+    return O_EARG;
+  }
+  o_fold_weight(w, s, N, K, wh);
+  for (int64_t n = 0; n < N; ++n) {
+    const float* r = wh + n * K;
+    float m = 0.0f;
+    for (int64_t k = 0; k < K; ++k) m = fabsf(r[k]) > m ? fabsf(r[k]) : m;
+    float S0 = m / (float)qmax;
+    S[n] = S0 < min_scale ? min_scale : S0;
+    o_quant_row(r, K, S[n], qmax, q);
+    best[n] = o_mse_row(r, q, K, S[n]) * scale;
+    A[n] = 0.0;
+    B[n] = 0;
+    for (int64_t k = 0; k < K; ++k) {
+      A[n] += (double)r[k] * (double)q[k];
+      B[n] += (int64_t)q[k] * (int64_t)q[k];
+    }
+    iters[n] = 0;
+    done[n] = 0;
+  }
+  for (int i = 1; i <= max_iter; ++i) {
+    int64_t active = 0;
+    for (int64_t n = 0; n < N; ++n) {
+      if (!global_loop && done[n]) continue;
+      const float* r = wh + n * K;
+      if (B[n] == 0) {  /* nothing to fit: the row is converged and never changes */
+        if (!done[n]) iters[n] = i;
+        done[n] = 1;
+        continue;
+      }
+      float Sc = (float)(A[n] / (double)B[n]);
+      if (Sc < min_scale) Sc = min_scale;
+      o_quant_row(r, K, Sc, qmax, q);
+      const double cur = o_mse_row(r, q, K, Sc) * scale;
+      const double d = best[n] - cur;
+      const int rel = best[n] == 0.0 || d / best[n] < thr, ab = fabs(d) < thr;
+      const int conv = best[n] == 0.0 || (conv_and ? (rel && ab) : (rel || ab));
+      iters[n] = i;
+      if (cur < best[n]) {
+        S[n] = Sc;
+        best[n] = cur;
+        A[n] = 0.0;
+        B[n] = 0;
+        for (int64_t k = 0; k < K; ++k) {
+          A[n] += (double)r[k] * (double)q[k];
+          B[n] += (int64_t)q[k] * (int64_t)q[k];
+        }
+      }
+      if (conv) done[n] = 1;
+    }
+    for (int64_t n = 0; n < N; ++n) active += !done[n];
+    if (active == 0) break;
+  }
+  if (mse)
+    for (int64_t n = 0; n < N; ++n) mse[n] = best[n] / scale;
+  free(wh); free(q); free(best); free(A); free(B); free(done);
+  return O_OK;
+}
+
+/* ---------------------------------------------------------------------------
  * Asymmetric linear quantization, int8.  [INT8] 2.1: Q = round(R/S) + Z with
  * saturation; the SSZ document's asymmetric mode lets the offset move
  * ([SSZ] iteration stage; "symmetric: false" in the option table) and

@@ -666,3 +666,54 @@ def test_granularity_error_ordering_on_outlier_layer():
     print(f"\nW8A8 output error: per-tensor {ea:.3e}, per-channel MinMax {eb:.3e}, per-channel SSZ {ec:.3e}, "
           f"+ smoothing {ed:.3e}")
     assert ea > eb and ec <= eb * 1.05 and ed < ec
+
+
+def _reading_rows(seed, N=96, K=256):
+    """Rows of mixed size with a few heavy entries, plus the special rows: all-zero, exact grid, one element."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((N, K)) * 0.02 * np.exp(rng.uniform(np.log(0.02), 0, N))[:, None]
+    w[rng.random((N, K)) < 0.004] *= 20
+    w[0] = 0.0
+    w[1] = 2.0 ** -9 * rng.integers(-127, 128, K)
+    w[2] = 0.0
+    w[2, 5] = 0.3
+    return w.astype(np.float32)
+
+
+def test_ssz_reading_variants_default_is_the_oracle():
+    """The diagnostic search with the used readings (OR, mean, per row) reproduces o_ssz exactly, int8 and int4."""
+    w = _reading_rows(71)
+    s = np.exp(np.random.default_rng(72).uniform(-0.5, 0.5, w.shape[1])).astype(np.float32)
+    for bits in (8, 4):
+        for ss in (None, s):
+            ref = oracle.ssz(w, ss, bits)
+            v = oracle.ssz_variant(w, ss, bits)
+            np.testing.assert_array_equal(v["S"], ref["S"])
+            np.testing.assert_array_equal(v["iters"], ref["iters"])
+            np.testing.assert_array_equal(v["mse"], ref["mse"])
+
+
+def test_ssz_reading_variants_properties():
+    """AND stops no earlier than OR and follows the same steps until OR stops; rows iterating until all
+    have converged all take the same number of steps, and a row whose own search ended on a rejected
+    candidate (a fixed point) keeps its scale; the summed error only weakens the absolute test."""
+    w = _reading_rows(73)
+    ref = oracle.ssz(w, None, 8, hist=True)
+    a = oracle.ssz_variant(w, None, 8, conv_and=True)
+    assert np.all(a["iters"] >= ref["iters"])
+    same = a["iters"] == ref["iters"]
+    np.testing.assert_array_equal(a["S"][same], ref["S"][same])
+    assert np.all(a["mse"] <= ref["mse"])  # it only ever keeps improvements
+
+    g = oracle.ssz_variant(w, None, 8, global_loop=True)
+    assert g["iters"][0] == 1  # the all-zero row has nothing to fit
+    assert np.all(g["iters"][1:] == g["iters"].max())
+    h = ref["hist"]
+    it = ref["iters"]
+    rejected_last = np.array([it[n] > 0 and h[n, it[n]] == h[n, it[n] - 1] for n in range(w.shape[0])])
+    assert rejected_last.sum() >= 3
+    np.testing.assert_array_equal(g["S"][rejected_last], ref["S"][rejected_last])
+
+    m = oracle.ssz_variant(w, None, 8, err_sum=True)
+    assert np.mean(m["iters"] >= ref["iters"]) >= 0.99
+    assert m["iters"].mean() > ref["iters"].mean()
