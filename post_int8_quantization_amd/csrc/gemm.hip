@@ -20,7 +20,9 @@
 //                     ST-deep LDS ring with direct HBM->LDS 16-byte loads;
 //                     each wave owns a TM x TN sub-tile of MFMA fragments.
 //                     One barrier per K step.  The epilogue dequantizes from
-//                     registers with the tile's scales staged in LDS.
+//                     registers with the tile's scales staged in LDS and
+//                     writes the converted tile back through the idle ring,
+//                     so that stores leave as whole-row 16-byte pieces.
 //  * k_gemm_dec    -- decode (M <= 64 tokens): HBM-bound weight streaming.
 //                     A block owns 16*NT output channels and its waves split
 //                     K into 128-byte slabs.  Each wave loads a slab with
