@@ -82,9 +82,11 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)
 // use the gfx950 row swaps (v_permlane16_swap / v_permlane32_swap), which
 // hand every lane the same lane of the paired row or half.  All are VALU
 // moves: no LDS round trip.
+// (every lane of these patterns reads a valid source lane, so no lane keeps the destination's old value:
+// the move form without an `old` operand spares the compiler a zeroing move per DPP move)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
