@@ -39,7 +39,7 @@ the int8 GEMM with dequantization.  The int8 weight is rotated over three
 copies so that it is read from HBM, not from the 256 MB last-level cache.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--alpha 0.5] [--no-cpu-baseline]
-                  [--workload opt67b|decode]
+                  [--workload opt67b|gpt345m|decode|ssz_scale|mlp_static]
 """
 from __future__ import annotations
 
@@ -71,7 +71,7 @@ def parse():
     p.add_argument("--calib-batches", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle GEMM time of the CPU baseline")
-    p.add_argument("--workload", choices=("opt67b", "decode", "ssz_scale", "mlp_static"), default="opt67b")
+    p.add_argument("--workload", choices=("opt67b", "gpt345m", "decode", "ssz_scale", "mlp_static"), default="opt67b")
     p.add_argument("--momentum", type=float, default=0.9, help="mlp_static: moving-average momentum")
     p.add_argument("--layers", type=int, default=32, help="ssz_scale workload: number of 4-matrix layers")
     p.add_argument("--copy-ref", action="store_true",
@@ -207,7 +207,8 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    cases = synth.cases("opt67b")
+    wl = args.workload  # opt67b (the default line) or gpt345m: the same step over the configuration's layers
+    cases = synth.cases(wl)
     B = args.calib_batches
 
     def up(a):
@@ -319,18 +320,22 @@ def main():
         roof = {"kernel": "k_quant_tok", "bound": "hbm", "achieved": quant_bytes / sec("quant") / 1e9,
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = load_counters(roof["kernel"], "opt67b")
+    rec = load_counters(roof["kernel"], wl)
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = tot[dom][0] * 1e3 / tot[dom][1]
+    if wl == "opt67b":
+        desc = ("opt67b-prefill hidden 4096: fc1 X[4096,4096] W[16384,4096], fc2 X[4096,16384] W[4096,16384], bf16, "
+                "1 percent outlier channels x60")
+    else:
+        desc = (f"{wl}: " + ", ".join(f"{c.name.split('/')[-1]} X[{c.T},{c.K}] W[{c.N},{c.K}]" for c in cases) +
+                ", bf16, 1 percent outlier channels x40")
 
     out = {
         "metric": METRIC, "value": gemm_tops, "unit": "TOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "opt67b-prefill hidden 4096: fc1 X[4096,4096] W[16384,4096], fc2 X[4096,16384] "
-                               f"W[4096,16384], bf16, 1 percent outlier channels x60, {B} calibration batches, "
-                               f"alpha {args.alpha:g}, int8 SSZ",
-                   "tokens": 4096, "hidden": 4096, "calib_batches": B, "alpha": args.alpha, "bits": 8,
+        "config": {"workload": f"{desc}, {B} calibration batches, alpha {args.alpha:g}, int8 SSZ",
+                   "tokens": cases[0].T, "hidden": cases[0].K, "calib_batches": B, "alpha": args.alpha, "bits": 8,
                    "parallelism": "single GPU"},
         "gpu_ms_per_step": gpu_ms, "step_tops": gemm_ops / (ms_per_step / 1e3) / 1e12,
         "graph_ms_per_step": graph_ms,

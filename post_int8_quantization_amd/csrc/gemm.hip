@@ -664,6 +664,10 @@ hipError_t dispatch_gemm(const int8_t* xq, const int8_t* wq, const float* ts, co
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 200) return launch_tiled<256, 256, 128, 2, 4, 2, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
   // smaller tiles: three 48 KB stages in flight instead of two 64 KB ones
+  const int64_t t_rect = M >= N ? ((M + 255) / 256) * ((N + 127) / 128) : ((M + 127) / 128) * ((N + 255) / 256);
+  // under half the CUs busy with those: 128x128 tiles (8 waves of 64x32) double the blocks (measured on
+  // the hidden-1024 shapes: 2048x1024 outputs 12 -> 9 us at K = 1024, 29 -> 20 us at K = 4096)
+  if (t_rect < 128) return launch_tiled<128, 128, 128, 2, 4, 3, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
   if (M >= N) return launch_tiled<256, 128, 128, 4, 2, 3, 32, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
   return launch_tiled<128, 256, 128, 2, 4, 3, 32, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
 }

@@ -202,7 +202,8 @@ def test_ssz_asym_scale_only(pq):
 @pytest.mark.parametrize("M,N,K", [
     (16, 128, 64), (1, 1, 16), (7, 33, 48), (16, 1000, 8192), (5, 1000, 8208), (20, 700, 272), (31, 4000, 4112),
     (33, 77, 160), (64, 300, 4096), (64, 16448, 1040), (65, 130, 1040),
-    (300, 520, 1040), (257, 259, 4096), (512, 768, 2048), (256, 256, 16), (1024, 1024, 4096)])
+    (300, 520, 1040), (257, 259, 4096), (512, 768, 2048), (256, 256, 16), (1024, 1024, 4096),
+    (1900, 3100, 1040), (3100, 1900, 1040)])
 def test_gemm_dequant(pq, M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     a = rng.integers(-127, 128, (M, K)).astype(np.int8)
@@ -251,7 +252,8 @@ def test_gemm_deterministic(pq):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 1000, 8192), (65, 130, 1040), (300, 520, 1040), (257, 259, 4096),
-                                   (1024, 1024, 4096), (512, 4352, 1024), (4352, 4096, 64), (4300, 4100, 80)])
+                                   (1024, 1024, 4096), (512, 4352, 1024), (4352, 4096, 64), (4300, 4100, 80),
+                                   (1900, 3104, 1040), (3100, 1904, 1040)])
 @pytest.mark.parametrize("out", ["f32", "bf16", "i8"])
 def test_gemm_plain_epilogue(pq, M, N, K, out):
     """No bias, no activation, no int32 copy: the prefill kernel's separate plain-dequantization loop,
