@@ -276,6 +276,191 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// Short rows (K <= 512, at most 32 chunks of 16): one wave holds R = 64 / G rows, G lanes each
+// (G = the chunk count rounded up to a power of two, 1 to 32), one 16-element chunk per lane -- the
+// same pass length per lane as the one-wave row kernel, which at these K leaves half its lanes or
+// more idle.  Each group
+// of G lanes carries its own row's state, reduces inside the group only (DPP moves within the 16-lane
+// row, plus the 16-lane swap for G = 32), and stops updating when its row converges, while the wave
+// runs until all its rows have; a pass never takes longer than in the row kernel, and R rows share it.
+// Same formulas and decisions per row as k_ssz.
+
+// sums and maximum over aligned groups of G lanes (G a power of two up to 32); every lane of a group
+// ends with the group's total, bit-identical across the group (each step adds the same two operands)
+template <int G>
+__device__ __forceinline__ double group_sum(double v) {
+  if constexpr (G >= 2) v += dpp_f64<kDppXor1>(v);
+  if constexpr (G >= 4) v += dpp_f64<kDppXor2>(v);
+  if constexpr (G >= 8) v += dpp_f64<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f64<kDppMirror>(v);
+  if constexpr (G == 32) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = join_f64(lo[0], hi[0]) + join_f64(lo[1], hi[1]);
+  }
+  return v;
+}
+
+template <int G, typename Op>
+__device__ __forceinline__ uint32_t group_reduce_u32(uint32_t v, Op op) {
+  if constexpr (G >= 2) v = op(v, dpp_u32<kDppXor1>(v));
+  if constexpr (G >= 4) v = op(v, dpp_u32<kDppXor2>(v));
+  if constexpr (G >= 8) v = op(v, dpp_u32<kDppHalfMirror>(v));
+  if constexpr (G >= 16) v = op(v, dpp_u32<kDppMirror>(v));
+  if constexpr (G == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(r[0], r[1]);
+  }
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ int group_sum(int v) {
+  return (int)group_reduce_u32<G>((uint32_t)v, [](uint32_t a, uint32_t b) { return (uint32_t)((int)a + (int)b); });
+}
+
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  return __uint_as_float(group_reduce_u32<G>(
+      __float_as_uint(v), [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); }));
+}
+
+template <int DT, bool HAS_S, int BITS, int G>
+__global__ __launch_bounds__(kWave) void k_ssz_rows(const void* __restrict__ w, int64_t N, int64_t K,
+                                                    const float* __restrict__ s, int max_iter, double thr,
+                                                    float min_scale, float* __restrict__ scale,
+                                                    void* __restrict__ wq, int32_t* __restrict__ iters,
+                                                    double* __restrict__ mse) {
+  static_assert(G >= 1 && G <= 32 && (G & (G - 1)) == 0, "1 to 32 lanes per row, a power of two");
+  constexpr int R = kWave / G;  // rows per wave
+  constexpr int CPT = 1;        // chunks of 16 per lane
+  constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
+  const int lane = threadIdx.x;
+  const int gl = lane % G;  // lane in the row's group
+  const int64_t nchunk = K / 16;
+  const DivK per_elem = make_divk(K);
+
+  // every lane runs the same number of row groups (uniform loop); rows past N compute on zeros, unwritten
+  for (int64_t n0 = (int64_t)blockIdx.x * R; n0 < N; n0 += (int64_t)gridDim.x * R) {
+    const int64_t n = n0 + lane / G;
+    const bool live = n < N;
+    float wh[CPT][16];
+    double wd[1][16];
+    load_row<DT, HAS_S, G, CPT, false>(w, live ? n : n0, K, s, gl, wh, wd);
+    if (!live) {
+#pragma unroll
+      for (int c8 = 0; c8 < CPT; ++c8)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
+    }
+    float m = 0.0f;
+    double w2 = 0.0;
+#pragma unroll
+    for (int c8 = 0; c8 < CPT; ++c8) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        m = fmaxf(m, fabsf(wh[c8][e]));
+        const double x = (double)wh[c8][e];
+        w2 = __builtin_fma(x, x, w2);
+      }
+    }
+    m = group_max<G>(m);
+    w2 = group_sum<G>(w2);
+
+    // one pass over the group's row for the scale S of that row: A = sum w_hat q (fp64), B = sum q^2
+    auto pass = [&](float Sx, double& A, int& B) {
+      const float inv = 1.0f / Sx;
+      double a = 0.0;
+      float bq = 0.0f;
+#pragma unroll
+      for (int c8 = 0; c8 < CPT; ++c8) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float q = code_f(wh[c8][e], inv, QMAX);
+          a = __builtin_fma((double)wh[c8][e], (double)q, a);
+          bq = __builtin_fmaf(q, q, bq);
+        }
+      }
+      A = group_sum<G>(a);
+      B = group_sum<G>((int)bq);
+    };
+
+    // MinMax init
+    float S = m / QMAX;
+    S = S < min_scale ? min_scale : S;
+    double A;
+    int B;
+    pass(S, A, B);
+    double best = per_elem(sq_err(w2, S, PassSums{A, B}));
+
+    // least-squares refits, greedy, per-row convergence; a row's state stays fixed once it stops
+    int it = 0;
+    bool active = live;  // rows past N take no step
+    for (int i = 1; i <= max_iter; ++i) {
+      if (!__builtin_amdgcn_ballot_w64(active)) break;
+      if (active) it = i;
+      const bool fit = active && B != 0;
+      if (active && B == 0) active = false;
+      float Sc = fit ? (float)(A / (double)B) : S;
+      Sc = Sc < min_scale ? min_scale : Sc;
+      double Ap;
+      int Bp;
+      pass(Sc, Ap, Bp);
+      const double c = per_elem(sq_err(w2, Sc, PassSums{Ap, Bp}));
+      const double d = best - c;
+      const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+      if (fit && c < best) {
+        S = Sc;
+        best = c;
+        A = Ap;
+        B = Bp;
+      }
+      if (fit && conv) active = false;
+    }
+
+    // codes of the kept scale, and its error summed directly
+    double e_dir = 0.0;
+    if (wq || mse) {
+      const float inv = 1.0f / S;
+      const double Sd = (double)S;
+#pragma unroll
+      for (int c8 = 0; c8 < CPT; ++c8) {
+        const int64_t c = gl + (int64_t)G * c8;
+        float q[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          q[e] = code_f(wh[c8][e], inv, QMAX);
+          const double dd = __builtin_fma(-Sd, (double)q[e], (double)wh[c8][e]);  // S*q is exact in fp64
+          e_dir = __builtin_fma(dd, dd, e_dir);
+        }
+        if (wq && live && c < nchunk) {
+          if constexpr (BITS == 8) {
+            uint4 o;
+            o.x = pack4_i8(q[0], q[1], q[2], q[3]);
+            o.y = pack4_i8(q[4], q[5], q[6], q[7]);
+            o.z = pack4_i8(q[8], q[9], q[10], q[11]);
+            o.w = pack4_i8(q[12], q[13], q[14], q[15]);
+            *reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(wq) + n * K + c * 16) = o;
+          } else {
+            uint2 o;
+            o.x = pack8_i4(q);
+            o.y = pack8_i4(q + 8);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(wq) + n * (K / 2) + c * 8) = o;
+          }
+        }
+      }
+      if (mse) e_dir = group_sum<G>(e_dir);
+    }
+    if (live && gl == 0) {
+      scale[n] = S;
+      if (iters) iters[n] = it;
+      if (mse) mse[n] = per_elem(e_dir);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Asymmetric int8 ([SSZ] asymmetric mode: scale and offset fitted together;
 // [INT8] 2.1 Q = round(R/S) + Z with saturation).  Codes
 //   q = clamp(rne(fl32(w_hat * inv S)) + Z, -128, 127),  dequantized S (q - Z).
@@ -533,7 +718,19 @@ template <int DT, bool HAS_S, int BITS>
 hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max_iter, double thr, float min_scale,
                     float* scale, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
   const int64_t nchunk = K / 16;
-  // about 64 elements per thread; one wave per row up to K = 4096
+  // short rows: several rows per wave, one chunk per lane
+  if (nchunk <= 32) {
+#define PTQ_SR(G_)                                                                                        \
+  if (nchunk <= G_) {                                                                                     \
+    constexpr int64_t R_ = kWave / G_;                                                                    \
+    k_ssz_rows<DT, HAS_S, BITS, G_><<<(unsigned)((N + R_ - 1) / R_), kWave, 0, stream>>>(                 \
+        w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse);                                     \
+    return hipGetLastError();                                                                             \
+  }
+    PTQ_SR(1) PTQ_SR(2) PTQ_SR(4) PTQ_SR(8) PTQ_SR(16) PTQ_SR(32)
+#undef PTQ_SR
+  }
+  // longer rows: about 64 elements per thread; one wave per row up to K = 4096
   int tpr = 64;
   while (tpr < 1024 && (nchunk + tpr - 1) / tpr > 4) tpr *= 2;
   const int64_t cpt = (nchunk + tpr - 1) / tpr;

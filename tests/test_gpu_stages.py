@@ -112,7 +112,13 @@ def _edge_rows(K, qmax):
     (96, 4096, synth.BF16, 4, True, 0.0), (40, 16384, synth.BF16, 8, True, 0.001),
     (40, 16384, synth.BF16, 4, False, 0.001), (23, 8192, synth.BF16, 8, True, 0.0),
     (17, 2064, synth.F32, 4, True, 0.002), (6, 36864, synth.BF16, 8, False, 0.001),
-    (3, 131072, synth.BF16, 8, True, 0.001), (3, 131072, synth.BF16, 4, False, 0.001)])
+    (3, 131072, synth.BF16, 8, True, 0.001), (3, 131072, synth.BF16, 4, False, 0.001),
+    # short rows, several per wave: 1, 2, 4, 8, 16 and 32 lanes per row (row counts that leave the
+    # last wave partly empty), and the widths just past them on the one-wave row kernel
+    (13, 16, synth.F32, 8, True, 0.0), (130, 32, synth.BF16, 4, True, 0.001),
+    (67, 48, synth.F32, 4, False, 0.0), (301, 112, synth.BF16, 8, True, 0.001),
+    (257, 256, synth.F32, 4, True, 0.002), (1023, 512, synth.BF16, 8, False, 0.001),
+    (45, 528, synth.BF16, 4, True, 0.001), (99, 1024, synth.F32, 8, True, 0.0)])
 def test_ssz(pq, N, K, dtype, bits, smooth, tail):
     w = _w(f"ssz/{N}x{K}", N, K, dtype, tail)
     wf = synth.widen(w).copy()
