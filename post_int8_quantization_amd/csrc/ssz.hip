@@ -131,6 +131,18 @@ __device__ __forceinline__ DivK make_divk(int64_t K) {
   return d;
 }
 
+// The relative convergence test fl64(d / best) < thr, for best > 0 and thr >= 0, with the division
+// taken only where its rounding can decide.  d <= 0 gives a quotient <= 0, below any thr > 0.
+// d >= 2 fl64(thr * best) means d > thr * best exactly (one rounding, or an underflow below the
+// smallest positive d, cannot halve the product), so the quotient exceeds thr and rounds to >= thr.
+// On these weights the division then runs only for improvements within a factor of two of the
+// threshold; it was 15 of the ~95 per-pass instructions of a row's wave.
+__device__ __forceinline__ bool rel_below(double d, double best, double thr) {
+  if (thr > 0.0 && d <= 0.0) return true;
+  if (d >= 2.0 * (thr * best)) return false;
+  return d / best < thr;
+}
+
 // K * mse(S) from the pass sums: W2 - 2 S A + S^2 B, never below 0
 __device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) {
   const double Sd = (double)S;
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
       par ^= 1;
       const double c = per_elem(sq_err(w2, Sc, p));
       const double d = best - c;
-      const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+      const bool conv = (best == 0.0) || (fabs(d) < thr) || rel_below(d, best, thr);
       if (c < best) {
         S = Sc;
         best = c;
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(kWave) void k_ssz_rows(const void* __restrict__ w, 
       pass(Sc, Ap, Bp);
       const double c = per_elem(sq_err(w2, Sc, PassSums{Ap, Bp}));
       const double d = best - c;
-      const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+      const bool conv = (best == 0.0) || (fabs(d) < thr) || rel_below(d, best, thr);
       if (fit && c < best) {
         S = Sc;
         best = c;
@@ -636,7 +648,7 @@ __global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, in
       par ^= 1;
       const double c = per_elem(sq_err_asym(w2, w1, Kd, Sc, Zc, p));
       const double d = best - c;
-      const bool conv = (best == 0.0) || (d / best < thr) || (fabs(d) < thr);
+      const bool conv = (best == 0.0) || (fabs(d) < thr) || rel_below(d, best, thr);
       if (c < best) {
         S = Sc;
         Z = Zc;

@@ -151,6 +151,31 @@ def test_ssz_outputs_optional(pq):
     np.testing.assert_array_equal(host(S), ref["S"])
 
 
+# Thresholds that make the relative convergence test decide: on weights scaled to mean errors above 1,
+# a threshold of 1e-3 leaves accepted improvements d > 0 with |d| >= thr and d / best near thr (the
+# kernels take the fp64 quotient only there); threshold 0 leaves only d < 0 (a rejected step) to stop
+# a row early.
+@pytest.mark.parametrize("N,K,bits,mag,thr", [
+    (64, 4096, 8, 1e4, 1e-3), (64, 4096, 4, 1e3, 1e-3), (256, 256, 8, 1e4, 1e-3), (256, 256, 4, 1e4, 1e-3),
+    (16, 16384, 8, 1e4, 1e-3), (64, 1024, 8, 1.0, 0.0), (256, 128, 4, 1.0, 0.0)])
+def test_ssz_thresholds(pq, N, K, bits, mag, thr):
+    w = (synth.widen(_w(f"ssz/thr/{N}x{K}", N, K, synth.F32, 0.001)) * np.float32(mag)).astype(np.float32)
+    ref = oracle.ssz(w, None, bits, thr=thr)
+    announce(f"ssz_weight_qparams N={N} K={K} bits={bits} magnitude={mag:g} threshold={thr:g}")
+    S, wq, it, mse = pq.ssz_weight_qparams(dev(w), None, bits=bits, threshold=thr)
+    codes = host(wq) if bits == 8 else unpack_int4(host(wq))
+    compare_ssz(host(S), codes, host(it), host(mse), ref, f"ssz thr={thr:g} {N}x{K} int{bits}")
+
+
+@pytest.mark.parametrize("N,K,mag,thr", [(64, 4096, 1e4, 1e-3), (48, 512, 1e3, 1e-3), (32, 2048, 1.0, 0.0)])
+def test_ssz_asym_thresholds(pq, N, K, mag, thr):
+    w = (synth.widen(_w(f"ssza/thr/{N}x{K}", N, K, synth.F32, 0.001)) * np.float32(mag)).astype(np.float32)
+    ref = oracle.ssz_asym(w, None, thr=thr)
+    announce(f"ssz_weight_qparams_asym N={N} K={K} magnitude={mag:g} threshold={thr:g}")
+    S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w), None, threshold=thr)
+    compare_ssz_asym(host(S), host(Z), host(wq), host(it), host(mse), ref, f"asym thr={thr:g} {N}x{K}")
+
+
 # ------------------------------------------------------------------ asymmetric SSZ
 
 def _edge_rows_asym(K):
