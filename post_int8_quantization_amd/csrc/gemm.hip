@@ -672,11 +672,13 @@ hipError_t dispatch_gemm(const int8_t* xq, const int8_t* wq, const float* ts, co
   // the largest tile that still gives about one tile per CU (256 CUs)
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 200) return launch_tiled<256, 256, 128, 2, 4, 2, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
-  // smaller tiles: three 48 KB stages in flight instead of two 64 KB ones
-  const int64_t t_rect = M >= N ? ((M + 255) / 256) * ((N + 127) / 128) : ((M + 127) / 128) * ((N + 255) / 256);
-  // under half the CUs busy with those: 128x128 tiles (8 waves of 64x32) double the blocks (measured on
-  // the hidden-1024 shapes: 2048x1024 outputs 12 -> 9 us at K = 1024, 29 -> 20 us at K = 4096)
-  if (t_rect < 128) return launch_tiled<128, 128, 128, 2, 4, 3, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  // small grids, by the count of 128x128 tiles (measured on 256- to 2048-row outputs, K 1024 to 16384):
+  // up to half a tile per CU, 64x64 tiles of 4 waves (four 16 KB stages) spread the work over 4x the
+  // blocks (10-25% faster than 128x128 there); up to one per CU, 128x128 tiles (2048x2048 outputs: 12.8
+  // -> 9.9 us against the rectangular tiles); beyond, 256x128 / 128x256 with three 48 KB stages
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t128 <= 128) return launch_tiled<64, 64, 128, 2, 2, 4, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  if (t128 <= 256) return launch_tiled<128, 128, 128, 2, 4, 3, 16, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
   if (M >= N) return launch_tiled<256, 128, 128, 4, 2, 3, 32, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
   return launch_tiled<128, 256, 128, 2, 4, 3, 32, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
 }
