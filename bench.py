@@ -136,6 +136,34 @@ class _NoTimer:
         fn()
 
 
+class _OnlyStage:
+    """Stage runner that runs one named stage and skips the others (for per-stage graph capture)."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def stage(self, name, fn):
+        if name == self.name:
+            fn()
+
+
+def graph_stage_ms(torch, step, names, steps, repeat=8):
+    """Per-stage time from a graph that holds only that stage's launches (all layers, `repeat` times over,
+    so that a replay is long next to the host's cost of launching it), replayed `steps` times: the kernels'
+    own time without the host's launch gaps, which dominate eager timings of short kernels."""
+    out = {}
+    for nm in names:
+        only = _OnlyStage(nm)
+
+        def rep(_tm, only=only):
+            for _ in range(repeat):
+                step(only)
+
+        ms = graph_step_ms(torch, rep, steps)
+        out[nm] = None if ms is None else ms / repeat
+    return out
+
+
 def graph_step_ms(torch, step, steps):
     """The same step captured once in a HIP graph and replayed `steps` times: the step's time without
     per-launch host overhead (stage events are not captured).  None if capture is not possible."""
@@ -262,6 +290,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tot = tm.totals()
     graph_ms = graph_step_ms(torch, step, args.steps)
+    graph_stage = graph_stage_ms(torch, step, ("calib_x", "calib_w", "smooth", "ssz", "quant", "gemm"), args.steps)
 
     # algorithmic work per step
     it_mean = {}
@@ -301,6 +330,10 @@ def main():
                   "frac_hbm": quant_bytes / sec("quant") / PEAK_HBM},
         "gemm": {"ms": gemm_s * 1e3, "TOPS": gemm_tops, "frac_i8": gemm_ops / gemm_s / PEAK_I8},
     }
+    for nm, g in graph_stage.items():
+        stages[nm]["graph_ms"] = g
+    if graph_stage.get("gemm"):
+        stages["gemm"]["graph_TOPS"] = gemm_ops / (graph_stage["gemm"] / 1e3) / 1e12
     gpu_ms = sum(v[0] for v in tot.values()) / K
 
     # dominant kernel: the stage with the largest share of the step
