@@ -133,13 +133,14 @@ def test_ssz(pq, N, K, dtype, bits, smooth, tail):
     compare_ssz(host(S), codes, host(it), host(mse), ref, f"ssz {N}x{K} int{bits}")
 
 
+@pytest.mark.parametrize("K", [1024, 256])
 @pytest.mark.parametrize("max_iter", [0, 1, 3])
-def test_ssz_max_iter(pq, max_iter):
-    w = _w("ssz/iter", 64, 1024, synth.BF16, 0.001)
+def test_ssz_max_iter(pq, max_iter, K):
+    w = _w(f"ssz/iter/{K}", 64, K, synth.BF16, 0.001)
     ref = oracle.ssz(synth.widen(w), None, 4, max_iter=max_iter)
-    announce(f"ssz_weight_qparams max_iter={max_iter}")
+    announce(f"ssz_weight_qparams K={K} max_iter={max_iter}")
     S, wq, it, mse = pq.ssz_weight_qparams(dev(w), None, bits=4, max_iter=max_iter)
-    compare_ssz(host(S), unpack_int4(host(wq)), host(it), host(mse), ref, f"max_iter={max_iter}")
+    compare_ssz(host(S), unpack_int4(host(wq)), host(it), host(mse), ref, f"K={K} max_iter={max_iter}")
 
 
 def test_ssz_outputs_optional(pq):
