@@ -36,6 +36,8 @@ _CONFIG = None
 def pytest_sessionstart(session):
     global _CONFIG
     _CONFIG = session.config
+    import parity_util
+    parity_util.set_writer(say)
 
 
 def say(msg):
@@ -43,8 +45,15 @@ def say(msg):
     GPU step belongs to is on record even if the process dies during the step."""
     tr = _CONFIG.pluginmanager.getplugin("terminalreporter") if _CONFIG else None
     if tr is not None:
-        tr.write_line(msg)
-        tr._tw.flush() if hasattr(tr, "_tw") else None
+        # inside a test, output capture is on: suspend it around the write (as pytest's live logging does)
+        capman = _CONFIG.pluginmanager.getplugin("capturemanager")
+        if capman is not None:
+            with capman.global_and_fixture_disabled():
+                tr.write_line(msg)
+                tr._tw.flush() if hasattr(tr, "_tw") else None
+        else:
+            tr.write_line(msg)
+            tr._tw.flush() if hasattr(tr, "_tw") else None
     else:
         sys.__stderr__.write(msg + "\n")
         sys.__stderr__.flush()

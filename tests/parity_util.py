@@ -15,10 +15,24 @@ Y_TOL = 1e-3          # max |y_gpu - y_ref| / max |y_ref|
 MSE_RTOL = 1e-9       # fp64 quantization error, summed in a different order
 
 
+# line writer to the real terminal, installed by the test session (conftest): test modules import this
+# module by name, but pytest loads conftest under its own module object, so it hands its writer over
+_SAY = None
+
+
+def set_writer(fn):
+    global _SAY
+    _SAY = fn
+
+
 def announce(msg: str):
-    """Name the case on the terminal before a GPU step (bypasses pytest capture)."""
-    from conftest import say
-    say(f"[gpu-case] {msg}")
+    """Name the case on the terminal before a GPU step (bypasses pytest capture, so the line is on record
+    even if the process dies during the step)."""
+    line = f"[gpu-case] {msg}"
+    if _SAY is not None:
+        _SAY(line)
+    else:
+        print(line, flush=True)
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
