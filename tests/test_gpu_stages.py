@@ -271,6 +271,25 @@ def test_gemm_max_k_extremes(pq):
     np.testing.assert_array_equal(host(acc2), ref2)
 
 
+@pytest.mark.parametrize("M,N", [(4096, 4096), (2048, 3072), (3072, 2048), (2048, 2048)])
+def test_gemm_max_k_tiles(pq, M, N):
+    """K = 133136 on the prefill tile shapes (256x256, 128x256, 256x128, 128x128 grids): rows of all +127 or all
+    -127 codes make every int32 sum +-127^2 K, the largest magnitude the bound admits (closed form)."""
+    K = 133136
+    sa = torch.where(torch.arange(M, device="cuda:0") % 3 == 0, -1, 1).to(torch.int8)
+    sb = torch.where(torch.arange(N, device="cuda:0") % 5 == 0, -1, 1).to(torch.int8)
+    a = (sa[:, None] * torch.full((M, K), 127, dtype=torch.int8, device="cuda:0")).contiguous()
+    b = (sb[:, None] * torch.full((N, K), 127, dtype=torch.int8, device="cuda:0")).contiguous()
+    ones_m = torch.ones(M, dtype=torch.float32, device="cuda:0")
+    ones_n = torch.ones(N, dtype=torch.float32, device="cuda:0")
+    announce(f"w8a8_gemm_dequant K=133136 extremes M={M} N={N}")
+    y, acc = pq.w8a8_gemm_dequant(a, b, ones_m, ones_n, want_acc=True)
+    del a, b
+    expect = np.outer(host(sa).astype(np.int64), host(sb).astype(np.int64)) * (127 * 127 * K)
+    np.testing.assert_array_equal(host(acc).astype(np.int64), expect)
+    np.testing.assert_array_equal(host(y), expect.astype(np.float32))
+
+
 def test_gemm_deterministic(pq):
     rng = np.random.default_rng(5)
     a = dev(rng.integers(-127, 128, (700, 1024)).astype(np.int8))
