@@ -123,6 +123,39 @@ def test_ssz_scale(pq, layer, bits):
         compare_ssz(host(S)[rows], codes[rows], host(it)[rows], host(mse)[rows], ref, case.name)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_ssz_scale_all_rows_properties(pq, bits):
+    """Every row of a model-scale layer (its 4 matrices, 36864 rows) at full size, by properties that hold at any
+    size ([SSZ] 算法流程, 收敛判断, 算法参数): scales at or above the 1e-5 floor, 1 to 20 steps, the codes are the
+    quantizer's codes for the returned scale, the reported error is those codes' error, and no row ends worse than
+    its MinMax start."""
+    qmax = 127 if bits == 8 else 7
+    floor = np.float32(1e-5)
+    for case in synth.cases("ssz_scale")[:4]:
+        w_host = case.w()
+        announce(f"{case.name}: ssz_weight_qparams int{bits} N={case.N} K={case.K}, every row")
+        S, wq, it, mse = pq.ssz_weight_qparams(dev(w_host), None, bits=bits)
+        S, it, mse = host(S), host(it), host(mse)
+        codes = host(wq) if bits == 8 else unpack_int4(host(wq))
+        assert S.min() >= floor and it.min() >= 1 and it.max() <= 20, case.name
+        w = synth.widen(w_host)
+        for r0 in range(0, case.N, 1024):
+            r1 = min(r0 + 1024, case.N)
+            wr, Sr, cr = w[r0:r1], S[r0:r1], codes[r0:r1]
+            inv = (np.float32(1.0) / Sr).astype(np.float32)
+            q = np.clip(np.rint((wr * inv[:, None]).astype(np.float32)), -qmax, qmax)
+            np.testing.assert_array_equal(q, cr, err_msg=f"{case.name} rows {r0}..{r1}: codes of the returned scale")
+            e = ((wr.astype(np.float64) - Sr.astype(np.float64)[:, None] * cr) ** 2).mean(axis=1)
+            rel = np.abs(mse[r0:r1] - e) / np.maximum(e, 1e-300)
+            rel[e == 0] = np.abs(mse[r0:r1][e == 0])
+            assert rel.max() <= 1e-9, f"{case.name} rows {r0}..{r1}: reported error {rel.max():.2e} off"
+            S0 = np.maximum((np.abs(wr).max(axis=1) / np.float32(qmax)).astype(np.float32), floor)
+            inv0 = (np.float32(1.0) / S0).astype(np.float32)
+            q0 = np.clip(np.rint((wr * inv0[:, None]).astype(np.float32)), -qmax, qmax)
+            e0 = ((wr.astype(np.float64) - S0.astype(np.float64)[:, None] * q0) ** 2).mean(axis=1)
+            assert np.all(mse[r0:r1] <= e0 * (1 + 1e-9)), f"{case.name} rows {r0}..{r1}: worse than MinMax"
+
+
 @pytest.mark.parametrize("layer", [0, 31])
 def test_ssz_scale_asym(pq, layer):
     """Asymmetric int8 SSZ at full size on the 4 matrices of a layer (sampled rows on the oracle)."""
