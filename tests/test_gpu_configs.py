@@ -81,9 +81,24 @@ def run_case(pq, case, alpha, bits=8, w_sample=None, x_sample=None):
     y_ref = oracle.dequant(acc_ref, d_ref, ref_w["S"])
     announce(f"{tag}: w8a8_gemm_dequant M={case.T} N={case.N} K={case.K}")
     y, acc = pq.w8a8_gemm_dequant(xq, wq, d, S, want_acc=True)
-    acc_h = host(acc)[np.ix_(toks, rows)]
+    acc_full = host(acc)
+    acc_h = acc_full[np.ix_(toks, rows)]
     np.testing.assert_array_equal(acc_h, acc_ref, err_msg=tag + " acc")
     err = assert_y(host(y)[np.ix_(toks, rows)], y_ref, tag + " y")
+    # every output, by properties that hold at any size: the int32 sums pass Freivalds' test (C v = A (B^T v)
+    # exactly in int64, three random integer vectors; a wrong sum escapes one draw with probability ~1/2001), and
+    # y is the epilogue fl32(acc) * fl32(ts * cs) of those sums, element for element
+    a64 = acc_full.astype(np.int64)
+    xq64 = host(xq).astype(np.int64)
+    wq64 = host(wq).astype(np.int64)
+    rng = np.random.default_rng(41)
+    for _ in range(3):
+        v = rng.integers(-1000, 1001, case.N).astype(np.int64)
+        assert np.array_equal(a64 @ v, xq64 @ (wq64.T @ v)), tag + ": int32 sums fail Freivalds' test"
+    del xq64, wq64
+    y_all = acc_full.astype(np.float32) * (host(d)[:, None] * host(S)[None, :])
+    np.testing.assert_array_equal(host(y), y_all, err_msg=tag + " y (every element) from acc")
+    del a64, y_all
     # accuracy of the whole W8A8 layer against the unquantized product (reported; parity unpinned)
     full = synth.widen(x_eval)[toks].astype(np.float64) @ w_f[rows].astype(np.float64).T
     rel = np.max(np.abs(host(y)[np.ix_(toks, rows)] - full)) / np.max(np.abs(full))
