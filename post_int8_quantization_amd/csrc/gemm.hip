@@ -125,6 +125,8 @@ __device__ __forceinline__ u32x4 panel_rsrc(const void* base, uint32_t bytes) {
 
 constexpr uint32_t OFF_OUT = 0x80000000u;  // an offset past every panel (panels stay below 2^31 bytes)
 
+// One 16-byte load per lane from the panel into 64 consecutive LDS slots at lds_byte_addr.  M0 is set inside
+// the block and declared clobbered; the generated code of these kernels reads M0 nowhere else.
 __device__ __forceinline__ void dma16_lds(u32x4 rsrc, uint32_t voff, uint32_t lds_byte_addr) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
