@@ -119,12 +119,20 @@ KERNEL_SOURCES = {"k_ssz": "ssz.hip", "k_ssz_asym": "ssz.hip", "k_gemm_pipe": "g
                   "k_absmax_cols": "calib.hip", "k_tensor_scale": "calib.hip", "k_quant_tok": "quant.hip"}
 
 
+def _code_only(text):
+    """Source text without comments and blank space (the sources hold no // or /* inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha(kernel_tag):
-    """Hash of the source a kernel is built from: its .hip file and the shared device header."""
+    """Hash of the code a kernel is built from (its .hip file and the shared device header, comments and
+    layout ignored), so a traffic record stays valid across comment edits and no longer once the code changes."""
     src = os.path.join(ROOT, "post_int8_quantization_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[kernel_tag], "ptq_dev.hpp"):
-        h.update(open(os.path.join(src, f), "rb").read())
+        h.update(_code_only(open(os.path.join(src, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
