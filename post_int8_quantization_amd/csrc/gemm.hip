@@ -189,24 +189,37 @@ struct EpiOut<EPI_I8> {
   static constexpr int kBytes = 1;
 };
 
+// Epilogue modes, fixed per compiled loop: the plain dequantization (no bias, no activation), bias only, bias and
+// ReLU (the bias added when present), or the activation read at run time (GELU, and the decode kernel's small
+// epilogue).  The ReLU loop carries no GELU code: with the activation chosen per element, the GELU code in the
+// loop cost the ReLU epilogue of a 4096x16384 output ~30 us (measured).  A loop compiled for GELU alone needed
+// more registers than the run-time one (spills on the int8-output tile), so GELU stays on the run-time loop.
+enum { EM_PLAIN = 0, EM_BIAS = 1, EM_RELU = 2, EM_RUNTIME = 3 };
+
+__device__ __forceinline__ int epi_mode(const Epi& epi) {
+  if (epi.act == ACT_RELU) return EM_RELU;
+  if (epi.act != ACT_NONE) return EM_RUNTIME;
+  return epi.bias ? EM_BIAS : EM_PLAIN;
+}
+
 // v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent).
-// GEN = false is the plain dequantization (no bias, no activation): the per-element tests drop out.
-template <int OUT, bool GEN>
+template <int OUT, int EM>
 __device__ __forceinline__ typename EpiOut<OUT>::T epi_value(float v, float bn, float nrn, float inv_out,
                                                              const Epi& epi) {
-  if constexpr (GEN) {
+  if constexpr (EM != EM_PLAIN) {
     if (epi.bias) v = v + bn;
-    v = epi_act(v, epi.act);
+    if constexpr (EM == EM_RELU) v = epi_act(v, ACT_RELU);
+    else if constexpr (EM == EM_RUNTIME) v = epi_act(v, epi.act);
   }
   if constexpr (OUT == EPI_F32) return v;
   else if constexpr (OUT == EPI_BF16) return bf16_rne(v);
   else return (int8_t)(int)code_f(v * nrn, inv_out, 127.0f);  // nrn is exactly 1 without next_s, and v * 1 = v
 }
 
-template <int OUT, bool NTS = true, bool GEN = true>
+template <int OUT, bool NTS = true, int EM = EM_RUNTIME>
 __device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
                                           float inv_out, const Epi& epi) {
-  const typename EpiOut<OUT>::T o = epi_value<OUT, GEN>(v, bn, nrn, inv_out, epi);
+  const typename EpiOut<OUT>::T o = epi_value<OUT, EM>(v, bn, nrn, inv_out, epi);
   typename EpiOut<OUT>::T* y = reinterpret_cast<typename EpiOut<OUT>::T*>(Y) + idx;
   if constexpr (OUT == EPI_F32 && NTS) __builtin_nontemporal_store(o, y);  // written once, not re-read
   else *y = o;
@@ -384,8 +397,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   const bool full = m0 + BM <= M && n0 + BN <= N;
   const float inv_out = OUT == EPI_I8 ? 1.0f / epi.out_scale[0] : 0.0f;
   constexpr int NG = NR / 4;
-  auto epilogue = [&](auto gen) {
-    constexpr bool GEN = decltype(gen)::value;
+  auto epilogue = [&](auto mode) {
+    constexpr int EM = decltype(mode)::value;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
@@ -405,8 +418,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
             const int m = m0 + rl0 + q;
             const int a = acc[i][j][g * 4 + q];
             if (full || (m < M && n < N)) {
-              epi_store<OUT, true, GEN>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
-              if constexpr (GEN)
+              epi_store<OUT, true, EM>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
+              if constexpr (EM != EM_PLAIN)
                 if (ACC) ACC[(int64_t)m * N + n] = a;
             }
           }
@@ -430,8 +443,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   static_assert(LPR <= 64 && 64 % LPR == 0, "whole rows per wave store");
   constexpr int RPI = 64 / LPR;              // tile rows per wave store
   static_assert(RPP % (RPI * NW) == 0, "passes split evenly over the waves");
-  auto staged = [&](auto gen) {
-    constexpr bool GEN = decltype(gen)::value;
+  auto staged = [&](auto mode) {
+    constexpr int EM = decltype(mode)::value;
     typedef typename EpiOut<OUT>::T OT;
     uint8_t* tl = reinterpret_cast<uint8_t*>(sm);
     __syncthreads();  // every wave is done with the stage buffers
@@ -454,7 +467,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               *reinterpret_cast<OT*>(tl + (wm * BAND + ro + q) * PITCH + cl * E) =
-                  epi_value<OUT, GEN>((float)acc[i][j][g * 4 + q] * (tsv[q] * csn), bn, nrn, inv_out, epi);
+                  epi_value<OUT, EM>((float)acc[i][j][g * 4 + q] * (tsv[q] * csn), bn, nrn, inv_out, epi);
           }
         }
       }
@@ -474,17 +487,24 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
       if (p + 1 < NPASS) __syncthreads();  // the pass's pieces are read before the next pass writes
     }
   };
-  const bool gen = epi.bias || epi.act != ACT_NONE;
+  // one mode per tile, a loop compiled for it (the int32 copy goes with the non-plain loops)
+  const int em = epi_mode(epi);
   // measured: the staging pays for int8 and bf16 outputs everywhere and for fp32 on 256x256 tiles; fp32 on the
   // smaller tiles (one pass of a 128-row tile at 1 KB a row) was 8% slower than the per-element stores
   constexpr bool kStage = OUT != EPI_F32 || (BM == 256 && BN == 256);
   if (kStage && ACC == nullptr && ((int64_t)N * E) % 16 == 0) {
-    if (gen) staged(std::true_type{});
-    else staged(std::false_type{});
-  } else if (gen || ACC) {
-    epilogue(std::true_type{});
+    if (em == EM_RELU) staged(std::integral_constant<int, EM_RELU>{});
+    else if (em == EM_RUNTIME) staged(std::integral_constant<int, EM_RUNTIME>{});
+    else if (em == EM_BIAS) staged(std::integral_constant<int, EM_BIAS>{});
+    else staged(std::integral_constant<int, EM_PLAIN>{});
+  } else if (em == EM_RELU) {
+    epilogue(std::integral_constant<int, EM_RELU>{});
+  } else if (em == EM_RUNTIME) {
+    epilogue(std::integral_constant<int, EM_RUNTIME>{});
+  } else if (em == EM_BIAS || ACC) {
+    epilogue(std::integral_constant<int, EM_BIAS>{});
   } else {
-    epilogue(std::false_type{});
+    epilogue(std::integral_constant<int, EM_PLAIN>{});
   }
 }
 
