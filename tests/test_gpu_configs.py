@@ -362,3 +362,46 @@ def test_accuracy_report(pq, config, alpha):
     announce(f"accuracy report, {config} alpha {alpha}: relative error vs fp64 (max-normalised / Frobenius)")
     for layer, err in rows:
         announce(f"  {layer:16s} " + "  ".join(f"{n}: {err[n][0]:.2e} / {err[n][1]:.2e}" for n in names))
+
+
+def _random_shapes(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.choice([1, 5, 16, 17, 33, 64, 65, 100, 257, 700]))
+        K = 16 * int(rng.integers(1, 130))
+        N = int(rng.integers(1, 900))
+        dt = synth.BF16 if rng.random() < 0.7 else synth.F32
+        out.append((i, T, K, N, dt, bool(rng.random() < 0.7), float(rng.choice([0.0, 0.5, 0.8, 1.0]))))
+    return out
+
+
+@pytest.mark.parametrize("i,T,K,N,dtype,smooth,alpha", _random_shapes())
+def test_random_shapes_whole_path(pq, i, T, K, N, dtype, smooth, alpha):
+    """The whole path on seeded random shapes (ragged tokens, widths of 16 to ~2 K, any channel count, both input
+    types, with and without smoothing), every output against the oracle: codes, scales, iteration counts, int32
+    sums bit for bit, y within the tolerance."""
+    tag = f"random {i}: T={T} K={K} N={N} dtype={dtype} smooth={smooth} alpha={alpha}"
+    x_h = synth.activation(f"random/{i}/x", T, K, dtype, synth.pick_channels(f"random/{i}/ch", K, max(1, K // 50)),
+                           40.0)
+    w_h = synth.weight(f"random/{i}/w", N, K, dtype, 0.02, 0.1, 1.0)
+    xf, wf = synth.widen(x_h), synth.widen(w_h)
+    announce(tag)
+    xd, wd = dev(x_h), dev(w_h)
+    if smooth:
+        s_ref = oracle.smooth_factors(oracle.absmax_cols(xf), oracle.absmax_cols(wf), alpha)
+        s = pq.sq_smooth_factors(pq.sq_absmax_calib(xd), pq.sq_absmax_calib(wd), alpha)
+        np.testing.assert_array_equal(host(s), s_ref, err_msg=tag + " s")
+    else:
+        s_ref, s = None, None
+    ref = oracle.ssz(wf, s_ref, 8)
+    S, wq, it, mse = pq.ssz_weight_qparams(wd, s, bits=8)
+    compare_ssz(host(S), host(wq), host(it), host(mse), ref, tag)
+    xq_ref, d_ref = oracle.quant_per_token(xf, s_ref)
+    xq, d = pq.quant_per_token_i8(xd, s)
+    np.testing.assert_array_equal(host(xq), xq_ref, err_msg=tag + " xq")
+    np.testing.assert_array_equal(host(d), d_ref, err_msg=tag + " tok_scale")
+    acc_ref = oracle.gemm_i8(xq_ref, ref["q"])
+    y, acc = pq.w8a8_gemm_dequant(xq, wq, d, S, want_acc=True)
+    np.testing.assert_array_equal(host(acc), acc_ref, err_msg=tag + " acc")
+    assert_y(host(y), oracle.dequant(acc_ref, d_ref, ref["S"]), tag + " y")
