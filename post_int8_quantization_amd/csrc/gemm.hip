@@ -155,13 +155,35 @@ struct Epi {
   int act;
 };
 
+// GELU(v) = 0.5 v (1 + erf(v / sqrt 2)), each operation rounded in fp32 as the epilogue defines it.  erf comes
+// from the complementary function by the Chebyshev fit of Numerical Recipes (2nd ed., section 6.2, erfcc):
+// erfc(z) = t exp(-z^2 + c(t)), t = 1 / (1 + z/2), c a polynomial of degree 9, relative error below 1.2e-7 for
+// every z >= 0 -- a relative bound, so 1 + erf(v / sqrt 2) = erfc(|v| / sqrt 2) stays accurate where it is small
+// (an absolute-error fit flips bf16 codes there).  The rounding error of z^2 is folded back into the exponent.
+// Branch-free; erf is odd.
+__device__ __forceinline__ float gelu_fast(float v) {
+  const float z = fabsf(v) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+  float c = __builtin_fmaf(0.17087277f, t, -0.82215223f);
+  c = __builtin_fmaf(c, t, 1.48851587f);
+  c = __builtin_fmaf(c, t, -1.13520398f);
+  c = __builtin_fmaf(c, t, 0.27886807f);
+  c = __builtin_fmaf(c, t, -0.18628806f);
+  c = __builtin_fmaf(c, t, 0.09678418f);
+  c = __builtin_fmaf(c, t, 0.37409196f);
+  c = __builtin_fmaf(c, t, 1.00002368f);
+  c = __builtin_fmaf(c, t, -1.26551223f);
+  const float z2 = z * z;
+  const float z2_lo = __builtin_fmaf(z, z, -z2);  // z*z - z2, exact
+  const float arg = (c - z2) - z2_lo;
+  const float erfc = t * __builtin_amdgcn_exp2f(arg * 1.44269504088896341f);
+  const float e = v < 0.0f ? erfc - 1.0f : 1.0f - erfc;  // erf(v / sqrt 2)
+  return (0.5f * v) * (1.0f + e);
+}
+
 __device__ __forceinline__ float epi_act(float v, int act) {
   if (act == ACT_RELU) return v > 0.0f ? v : 0.0f;
-  if (act == ACT_GELU) {
-    const float e = erff(v * 0.70710678118654752440f);
-    const float h = 0.5f * v;
-    return h * (1.0f + e);
-  }
+  if (act == ACT_GELU) return gelu_fast(v);
   return v;
 }
 
@@ -190,15 +212,14 @@ struct EpiOut<EPI_I8> {
 };
 
 // Epilogue modes, fixed per compiled loop: the plain dequantization (no bias, no activation), bias only, bias and
-// ReLU (the bias added when present), or the activation read at run time (GELU, and the decode kernel's small
-// epilogue).  The ReLU loop carries no GELU code: with the activation chosen per element, the GELU code in the
-// loop cost the ReLU epilogue of a 4096x16384 output ~30 us (measured).  A loop compiled for GELU alone needed
-// more registers than the run-time one (spills on the int8-output tile), so GELU stays on the run-time loop.
-enum { EM_PLAIN = 0, EM_BIAS = 1, EM_RELU = 2, EM_RUNTIME = 3 };
+// ReLU, bias and GELU (the bias added when present), or the activation read at run time (the decode kernel's small
+// epilogue).  A loop compiled for one activation carries no code of the other: with the activation chosen per
+// element, the GELU code in the loop cost the ReLU epilogue of a 4096x16384 output ~30 us (measured).
+enum { EM_PLAIN = 0, EM_BIAS = 1, EM_RELU = 2, EM_GELU = 3, EM_RUNTIME = 4 };
 
 __device__ __forceinline__ int epi_mode(const Epi& epi) {
   if (epi.act == ACT_RELU) return EM_RELU;
-  if (epi.act != ACT_NONE) return EM_RUNTIME;
+  if (epi.act == ACT_GELU) return EM_GELU;
   return epi.bias ? EM_BIAS : EM_PLAIN;
 }
 
@@ -209,6 +230,7 @@ __device__ __forceinline__ typename EpiOut<OUT>::T epi_value(float v, float bn, 
   if constexpr (EM != EM_PLAIN) {
     if (epi.bias) v = v + bn;
     if constexpr (EM == EM_RELU) v = epi_act(v, ACT_RELU);
+    else if constexpr (EM == EM_GELU) v = epi_act(v, ACT_GELU);
     else if constexpr (EM == EM_RUNTIME) v = epi_act(v, epi.act);
   }
   if constexpr (OUT == EPI_F32) return v;
@@ -494,13 +516,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   constexpr bool kStage = OUT != EPI_F32 || (BM == 256 && BN == 256);
   if (kStage && ACC == nullptr && ((int64_t)N * E) % 16 == 0) {
     if (em == EM_RELU) staged(std::integral_constant<int, EM_RELU>{});
-    else if (em == EM_RUNTIME) staged(std::integral_constant<int, EM_RUNTIME>{});
+    else if (em == EM_GELU) staged(std::integral_constant<int, EM_GELU>{});
     else if (em == EM_BIAS) staged(std::integral_constant<int, EM_BIAS>{});
     else staged(std::integral_constant<int, EM_PLAIN>{});
   } else if (em == EM_RELU) {
     epilogue(std::integral_constant<int, EM_RELU>{});
-  } else if (em == EM_RUNTIME) {
-    epilogue(std::integral_constant<int, EM_RUNTIME>{});
+  } else if (em == EM_GELU) {
+    epilogue(std::integral_constant<int, EM_GELU>{});
   } else if (em == EM_BIAS || ACC) {
     epilogue(std::integral_constant<int, EM_BIAS>{});
   } else {

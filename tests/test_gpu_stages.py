@@ -371,9 +371,9 @@ def test_gemm_fused(pq, M, N, K, act, out, want_acc):
     if act != "gelu":
         np.testing.assert_array_equal(got, ref)  # exact: the same fp32 operations in the same order
         return
-    # GELU: the device erff and the host erff may differ in the last bit.  For negative inputs
-    # 1 + erf(v / sqrt 2) cancels, so that bit is a small absolute (not relative) difference; bf16 rounding
-    # can turn a tiny fp32 difference into one bf16 step.
+    # GELU: the device's erf (from a published erfc fit, relative error below 1.2e-7) and the oracle's erf may
+    # differ in the last bit.  For negative inputs 1 + erf(v / sqrt 2) cancels, so that bit is a small absolute
+    # (not relative) difference; bf16 rounding can turn a tiny fp32 difference into one bf16 step.
     den = max(1.0, float(np.max(np.abs(y32))))
     if out == "f32":
         assert np.max(np.abs(got.astype(np.float64) - ref)) <= 4e-7 * den
