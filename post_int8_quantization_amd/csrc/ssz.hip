@@ -1,5 +1,6 @@
 // ssz.hip -- MinMax + SSZ per-output-channel weight quantization (gfx950):
-// symmetric int8/int4 (k_ssz) and asymmetric int8 (k_ssz_asym, further down).
+// symmetric int8/int4 (k_ssz; k_ssz_rows for rows of at most 512 elements,
+// several rows per wave) and asymmetric int8 (k_ssz_asym, further down).
 //
 // [SSZ] flow: MinMax initial scale, then least-squares refits of the scale for
 // the current codes, a refit kept only when it lowers the quantization error,
