@@ -338,10 +338,17 @@ def main():
                   "frac_hbm": quant_bytes / sec("quant") / PEAK_HBM},
         "gemm": {"ms": gemm_s * 1e3, "TOPS": gemm_tops, "frac_i8": gemm_ops / gemm_s / PEAK_I8},
     }
+    stage_bytes = {"calib_x": calib_x_bytes, "calib_w": calib_w_bytes, "quant": quant_bytes}
     for nm, g in graph_stage.items():
         stages[nm]["graph_ms"] = g
+        if g and nm in stage_bytes:
+            stages[nm]["graph_GB/s"] = stage_bytes[nm] / (g / 1e3) / 1e9
+            stages[nm]["graph_frac_hbm"] = stage_bytes[nm] / (g / 1e3) / PEAK_HBM
     if graph_stage.get("gemm"):
         stages["gemm"]["graph_TOPS"] = gemm_ops / (graph_stage["gemm"] / 1e3) / 1e12
+        stages["gemm"]["graph_frac_i8"] = gemm_ops / (graph_stage["gemm"] / 1e3) / PEAK_I8
+    if graph_stage.get("ssz"):
+        stages["ssz"]["graph_frac_alu"] = SSZ_OPS_PER_ELEM_PASS * elem_passes / (graph_stage["ssz"] / 1e3) / PEAK_ALU
     gpu_ms = sum(v[0] for v in tot.values()) / K
 
     # dominant kernel: the stage with the largest share of the step
