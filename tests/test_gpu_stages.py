@@ -106,6 +106,12 @@ def _edge_rows(K, qmax):
     return rows
 
 
+def _bf16_bits(a):
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even; finite inputs (test input preparation)."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 @pytest.mark.parametrize("N,K,dtype,bits,smooth,tail", [
     (128, 64, synth.F32, 8, True, 0.0), (300, 1040, synth.BF16, 8, True, 0.001),
     (300, 1040, synth.BF16, 4, False, 0.001), (96, 4096, synth.BF16, 8, False, 0.001),
@@ -122,9 +128,14 @@ def _edge_rows(K, qmax):
 def test_ssz(pq, N, K, dtype, bits, smooth, tail):
     w = _w(f"ssz/{N}x{K}", N, K, dtype, tail)
     wf = synth.widen(w).copy()
+    edge = _edge_rows(K, 127 if bits == 8 else 7)[:min(4, N)]
     if dtype == synth.F32:
-        wf[:4] = _edge_rows(K, 127 if bits == 8 else 7)
+        wf[:len(edge)] = edge
         w = wf
+    else:
+        w = w.copy()
+        w[:len(edge)] = _bf16_bits(edge)
+        wf = synth.widen(w).copy()
     s = np.exp(np.random.default_rng(N + K).uniform(-1, 1, K)).astype(np.float32) if smooth else None
     ref = oracle.ssz(wf, s, bits)
     announce(f"ssz_weight_qparams N={N} K={K} dtype={dtype} bits={bits} smooth={smooth}")
