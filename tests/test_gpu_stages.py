@@ -210,10 +210,14 @@ def _edge_rows_asym(K):
 def test_ssz_asym(pq, N, K, dtype, smooth, tail, shift):
     w = _w(f"ssza/{N}x{K}", N, K, dtype, tail)
     wf = synth.widen(w).copy()
+    wf[::2] += np.float32(shift)
+    edge = _edge_rows_asym(K)[:min(6, N)]
+    wf[:len(edge)] = edge
     if dtype == synth.F32:
-        wf[::2] += np.float32(shift)
-        wf[:6] = _edge_rows_asym(K)
         w = wf
+    else:
+        w = _bf16_bits(wf)
+        wf = synth.widen(w).copy()
     s = np.exp(np.random.default_rng(N * 3 + K).uniform(-1, 1, K)).astype(np.float32) if smooth else None
     ref = oracle.ssz_asym(wf, s)
     announce(f"ssz_weight_qparams_asym N={N} K={K} dtype={dtype} smooth={smooth}")
