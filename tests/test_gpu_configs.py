@@ -8,6 +8,8 @@ rows from the same seeded inputs: calibration is checked in full (it is
 cheap), the weight quantization on sampled output channels, the activation
 quantization on sampled tokens, and the GEMM on the sampled tokens x channels.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -364,27 +366,36 @@ def test_accuracy_report(pq, config, alpha):
         announce(f"  {layer:16s} " + "  ".join(f"{n}: {err[n][0]:.2e} / {err[n][1]:.2e}" for n in names))
 
 
-def _random_shapes(n=24, seed=2024):
+# case count and seed of the random-shape sweep; larger sweeps: PTQ_RANDOM_CASES=5000 PTQ_RANDOM_SEED=11
+_RANDOM_CASES = int(os.environ.get("PTQ_RANDOM_CASES", "64"))
+_RANDOM_SEED = int(os.environ.get("PTQ_RANDOM_SEED", "2024"))
+
+
+def _random_shapes(n=_RANDOM_CASES, seed=_RANDOM_SEED):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        T = int(rng.choice([1, 5, 16, 17, 33, 64, 65, 100, 257, 700]))
-        K = 16 * int(rng.integers(1, 130))
-        N = int(rng.integers(1, 900))
+        T = int(rng.choice([1, 3, 5, 16, 17, 31, 33, 64, 65, 100, 257, 512, 700]))
+        K = 16 * int(rng.integers(1, 260))
+        N = int(rng.integers(1, 1200))
         dt = synth.BF16 if rng.random() < 0.7 else synth.F32
-        out.append((i, T, K, N, dt, bool(rng.random() < 0.7), float(rng.choice([0.0, 0.5, 0.8, 1.0]))))
+        smooth = bool(rng.random() < 0.7)
+        alpha = float(rng.choice([0.0, 0.3, 0.5, 0.8, 1.0]))
+        std = float(rng.choice([0.002, 0.02, 0.5]))
+        out.append((seed, i, T, K, N, dt, smooth, alpha, std))
     return out
 
 
-@pytest.mark.parametrize("i,T,K,N,dtype,smooth,alpha", _random_shapes())
-def test_random_shapes_whole_path(pq, i, T, K, N, dtype, smooth, alpha):
-    """The whole path on seeded random shapes (ragged tokens, widths of 16 to ~2 K, any channel count, both input
-    types, with and without smoothing), every output against the oracle: codes, scales, iteration counts, int32
-    sums bit for bit, y within the tolerance."""
-    tag = f"random {i}: T={T} K={K} N={N} dtype={dtype} smooth={smooth} alpha={alpha}"
-    x_h = synth.activation(f"random/{i}/x", T, K, dtype, synth.pick_channels(f"random/{i}/ch", K, max(1, K // 50)),
-                           40.0)
-    w_h = synth.weight(f"random/{i}/w", N, K, dtype, 0.02, 0.1, 1.0)
+@pytest.mark.parametrize("seed,i,T,K,N,dtype,smooth,alpha,std", _random_shapes())
+def test_random_shapes_whole_path(pq, seed, i, T, K, N, dtype, smooth, alpha, std):
+    """The whole path on seeded random shapes (ragged tokens, widths of 16 to ~4 K, any channel count, both input
+    types, three weight spreads with heavy-tailed entries, with and without smoothing), every output against the
+    oracle: codes, scales, iteration counts, int32 sums bit for bit, y within the tolerance; and on the same
+    weights the int4 and the asymmetric int8 SSZ."""
+    tag = f"random {seed}/{i}: T={T} K={K} N={N} dtype={dtype} smooth={smooth} alpha={alpha} std={std}"
+    x_h = synth.activation(f"random/{seed}/{i}/x", T, K, dtype,
+                           synth.pick_channels(f"random/{seed}/{i}/ch", K, max(1, K // 50)), 40.0)
+    w_h = synth.weight(f"random/{seed}/{i}/w", N, K, dtype, std, 0.05, 1.0, 0.001, 20.0)
     xf, wf = synth.widen(x_h), synth.widen(w_h)
     announce(tag)
     xd, wd = dev(x_h), dev(w_h)
@@ -405,3 +416,9 @@ def test_random_shapes_whole_path(pq, i, T, K, N, dtype, smooth, alpha):
     y, acc = pq.w8a8_gemm_dequant(xq, wq, d, S, want_acc=True)
     np.testing.assert_array_equal(host(acc), acc_ref, err_msg=tag + " acc")
     assert_y(host(y), oracle.dequant(acc_ref, d_ref, ref["S"]), tag + " y")
+    r4 = oracle.ssz(wf, s_ref, 4)
+    S4, q4, it4, m4 = pq.ssz_weight_qparams(wd, s, bits=4)
+    compare_ssz(host(S4), unpack_int4(host(q4)), host(it4), host(m4), r4, tag + " int4")
+    ra = oracle.ssz_asym(wf, s_ref)
+    Sa, Za, qa, ita, ma = pq.ssz_weight_qparams_asym(wd, s)
+    compare_ssz_asym(host(Sa), host(Za), host(qa), host(ita), host(ma), ra, tag + " asym")
