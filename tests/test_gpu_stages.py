@@ -3,6 +3,8 @@ seeded inputs, over shapes that span several tiles and a ragged tail, plus the
 degenerate cases of the method.  Integers are compared bit for bit; floats to
 the tolerances in parity_util.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -334,6 +336,8 @@ def test_gemm_plain_epilogue(pq, M, N, K, out):
     code = {"f32": oracle.OUT_F32, "bf16": oracle.OUT_BF16, "i8": oracle.OUT_I8}[out]
     y32 = oracle.epilogue(acc_ref, ts, cs, None, oracle.ACT_NONE)
     osc = np.float32(np.max(np.abs(y32)) / 100.0) if out == "i8" else 1.0
+    if out == "i8" and not osc > 0:  # an all-zero output (tiny shapes): any positive scale will do
+        osc = np.float32(1.0)
     ref = oracle.epilogue(acc_ref, ts, cs, None, oracle.ACT_NONE, code, ns, osc)
     announce(f"w8a8_gemm_fused plain M={M} N={N} K={K} out={out} next_s={ns is not None}")
     y = pq.w8a8_gemm_fused(dev(a), dev(b), dev(ts), dev(cs), None, "none", out, None if ns is None else dev(ns),
@@ -356,7 +360,37 @@ def test_gemm_plain_epilogue(pq, M, N, K, out):
 def test_gemm_fused(pq, M, N, K, act, out, want_acc):
     """With the int32 copy the prefill kernel stores element by element; without it (and 16-byte output
     rows) its epilogue goes through LDS as whole-row pieces: both against the oracle."""
-    rng = np.random.default_rng(M * 11 + N * 5 + K + len(act) + len(out))
+    _fused_case(pq, M, N, K, act, out, want_acc, M * 11 + N * 5 + K + len(act) + len(out))
+
+
+# case count and seed of the random-shape sweep; larger sweeps: PTQ_RANDOM_CASES=2000 PTQ_RANDOM_SEED=11
+_RANDOM_CASES = int(os.environ.get("PTQ_RANDOM_CASES", "64"))
+_RANDOM_SEED = int(os.environ.get("PTQ_RANDOM_SEED", "2024"))
+
+
+def _random_fused(n=_RANDOM_CASES, seed=_RANDOM_SEED):
+    rng = np.random.default_rng(seed + 1)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([1, 2, 7, 16, 17, 32, 33, 63, 64, 65, 100, 255, 256, 300, 513, 1024, 1100]))
+        N = int(rng.integers(1, 2300))
+        K = 16 * int(rng.integers(1, 400))
+        if M * N * K > 2_000_000_000:  # keeps the oracle's GEMM to a second or two
+            continue
+        out.append((seed, len(out), M, N, K, str(rng.choice(["none", "relu", "gelu"])),
+                    str(rng.choice(["f32", "bf16", "i8"])), bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("seed,i,M,N,K,act,out,want_acc", _random_fused())
+def test_gemm_fused_random_shapes(pq, seed, i, M, N, K, act, out, want_acc):
+    """The fused epilogue on seeded random shapes: every GEMM kernel the dispatch picks (decode kernel, 64x64 to
+    256x256 tiles, ragged edges on all three sides), every activation and output type, against the oracle."""
+    _fused_case(pq, M, N, K, act, out, want_acc, seed * 100_003 + i)
+
+
+def _fused_case(pq, M, N, K, act, out, want_acc, seed):
+    rng = np.random.default_rng(seed)
     a = rng.integers(-127, 128, (M, K)).astype(np.int8)
     b = rng.integers(-127, 128, (N, K)).astype(np.int8)
     ts = rng.uniform(0.002, 0.02, M).astype(np.float32)
@@ -388,7 +422,8 @@ def test_gemm_fused(pq, M, N, K, act, out, want_acc):
         return
     # GELU: the device's erf (from a published erfc fit, relative error below 1.2e-7) and the oracle's erf may
     # differ in the last bit.  For negative inputs 1 + erf(v / sqrt 2) cancels, so that bit is a small absolute
-    # (not relative) difference; bf16 rounding can turn a tiny fp32 difference into one bf16 step.
+    # (not relative) difference; bf16 rounding can turn a tiny fp32 difference into one bf16 step.  Such
+    # boundary cases are rare (~1e-5 of the elements), so at most max(2, 1e-3 n) elements may differ.
     den = max(1.0, float(np.max(np.abs(y32))))
     if out == "f32":
         assert np.max(np.abs(got.astype(np.float64) - ref)) <= 4e-7 * den
@@ -396,10 +431,10 @@ def test_gemm_fused(pq, M, N, K, act, out, want_acc):
         g = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         r = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         assert np.all(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 4e-7 * den)
-        assert np.mean(got != ref) < 1e-3
+        assert np.sum(got != ref) <= max(2, 1e-3 * got.size)
     else:
         diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
-        assert diff.max() <= 1 and np.mean(diff) < 1e-3
+        assert diff.max() <= 1 and np.sum(diff) <= max(2, 1e-3 * diff.size)
 
 
 # ------------------------------------------------------------------ static per-tensor scales
