@@ -490,6 +490,42 @@ def test_quant_static(pq, R, C, dtype, fold):
     assert np.any(np.abs(ref) == 127)
 
 
+def _random_quant(n=_RANDOM_CASES, seed=_RANDOM_SEED):
+    rng = np.random.default_rng(seed + 2)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 16, 31, 64, 100, 257, 600, 2048]))
+        C = 16 * int(rng.integers(1, 1300))
+        out.append((seed, i, R, C, synth.BF16 if rng.random() < 0.7 else synth.F32,
+                    [None, "div", "mul"][int(rng.integers(0, 3))]))
+    return out
+
+
+@pytest.mark.parametrize("seed,i,R,C,dtype,fold", _random_quant())
+def test_quantizers_random_shapes(pq, seed, i, R, C, dtype, fold):
+    """Per-token, per-tensor weight and static quantization on seeded random shapes (1 to 2048 rows, widths of 16
+    to ~21 K, both input types, each fold), bit for bit against the oracle."""
+    x = _x(f"rq/{seed}/{i}", R, C, dtype)
+    s = np.exp(np.random.default_rng(seed * 7 + i).uniform(-1, 1, C)).astype(np.float32) if fold else None
+    xf = synth.widen(x)
+    sd = None if s is None else dev(s)
+    announce(f"random quantizers {seed}/{i}: R={R} C={C} dtype={dtype} fold={fold}")
+    xd = dev(x)
+    if fold != "mul":  # per-token quantization folds by division or not at all
+        xq_ref, d_ref = oracle.quant_per_token(xf, s)
+        xq, d = pq.quant_per_token_i8(xd, sd)
+        np.testing.assert_array_equal(host(xq), xq_ref)
+        np.testing.assert_array_equal(host(d), d_ref)
+    fcode = {"div": oracle.FOLD_DIV, "mul": oracle.FOLD_MUL, None: oracle.FOLD_NONE}[fold]
+    a = oracle.absmax_tensor(xf, s, fcode)
+    if fold != "div":  # the per-tensor weight scale folds by multiplication or not at all
+        sc, _ = pq.weight_scale_per_tensor(pq.sq_absmax_calib(xd), sd)
+        assert host(sc)[0] == oracle.weight_scale_per_tensor(a)
+    S = np.float32(a / 150.0) if a > 0 else np.float32(1.0)
+    q, _ = pq.quant_static_i8(xd, dev(np.array([S], np.float32)), sd, fold or "div")
+    np.testing.assert_array_equal(host(q), oracle.quant_static(xf, S, s, fcode))
+
+
 # ------------------------------------------------------------------ streams, graphs, determinism
 
 def test_repeatable_bit_for_bit(pq):
