@@ -63,7 +63,7 @@ def _load():
             "o_minmax_per_tensor": [vp, i64, i64, ci, f32, vp, vp],
             "o_quant_row_asym": [vp, i64, f32, ci, vp],
             "o_mse_row_asym": [vp, vp, i64, f32, ci],
-            "o_lsq_affine": [vp, vp, i64, vp, vp],
+            "o_lsq_affine": [vp, vp, i64, ci, vp, vp],
             "o_ssz_asym": [vp, vp, i64, i64, ci, f64, f32, vp, vp, vp, vp, vp, vp],
             "o_ssz_variant": [vp, vp, i64, i64, ci, ci, f64, f32, ci, ci, ci, vp, vp, vp],
             "o_epilogue": [vp, i64, i64, vp, vp, vp, ci, ci, vp, f32, vp],
@@ -214,13 +214,14 @@ def mse_row_asym(wh, q, S, Z):
     return float(_load().o_mse_row_asym(wh.ctypes.data, q.ctypes.data, wh.size, float(S), int(Z)))
 
 
-def lsq_affine(wh, q):
-    """(a, b) of the least-squares line wh ~ a q + b, or None when all codes are equal."""
+def lsq_affine(wh, q, Z=0):
+    """(a, b) of the least-squares line wh ~ a (q - Z) + b, or None when all codes are equal."""
     wh = _f32(wh).ravel()
     q = np.ascontiguousarray(q, dtype=np.int8).ravel()
     a = ctypes.c_double()
     b = ctypes.c_double()
-    ok = _load().o_lsq_affine(wh.ctypes.data, q.ctypes.data, wh.size, ctypes.addressof(a), ctypes.addressof(b))
+    ok = _load().o_lsq_affine(wh.ctypes.data, q.ctypes.data, wh.size, int(Z), ctypes.addressof(a),
+                              ctypes.addressof(b))
     return (a.value, b.value) if ok else None
 
 

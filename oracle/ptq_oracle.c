@@ -27,12 +27,19 @@
  *   - fl32(.) is IEEE binary32 round-to-nearest-even.  This file is compiled
  *     with -O2 -fno-fast-math -ffp-contract=off so no product is fused into a
  *     following add and float expressions stay in float.
- *   - R / S is evaluated as fl32(R * fl32(1/S)): the scale's reciprocal is
- *     rounded to fp32 once, then multiplied.
+ *   - R / S is the IEEE binary32 quotient fl32(R / S), the plain reading of
+ *     [INT8] 2.1's Q = round(R/S) + Z; the activation fold X / s_j is the
+ *     quotient fl32(X / s_j) likewise.
  *   - round() is round-half-to-even (nearbyintf under the default rounding
  *     mode), then saturation to [-qmax, qmax], qmax = 127 (int8) or 7 (int4);
  *     symmetric, so the zero point Z is 0.
- *   - sums of squares and cross products are fp64, k ascending.
+ *   - the SSZ sums -- the quantization error sum (w_hat - S q)^2 and the
+ *     least-squares sums sum w_hat q, sum w_hat -- are the exact real sums
+ *     rounded once to fp64 (accumulated in binary128, whose 113-bit
+ *     significand holds every product exactly; the fp64 result can differ from
+ *     the correctly rounded exact sum only when that sum lies within about
+ *     K * 2^-113 of it, relatively, of an fp64 rounding boundary).  The value
+ *     is therefore independent of any summation order.
  *
  * Every function takes host pointers to row-major, K-contiguous arrays and
  * returns 0 on success, a negative value on a bad argument or a non-finite
@@ -105,7 +112,7 @@ int o_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, f
  * are divided by s_j and the weights of input channel j multiplied by s_j, so
  * (X diag(s)^-1)(diag(s) W^T) = X W^T.
  *   w_hat[n,j] = fl32(W[n,j] * s_j)
- *   x_hat[t,j] = fl32(X[t,j] * fl32(1/s_j))
+ *   x_hat[t,j] = fl32(X[t,j] / s_j)
  * With s == NULL both are the identity.
  * ------------------------------------------------------------------------- */
 int o_fold_weight(const float* w, const float* s, int64_t N, int64_t K, float* wh) {
@@ -120,8 +127,7 @@ int o_fold_act(const float* x, const float* s, int64_t T, int64_t K, float* xh) 
   for (int64_t t = 0; t < T; ++t)
     for (int64_t j = 0; j < K; ++j) {
       if (s) {
-        float r = 1.0f / s[j];
-        xh[t * K + j] = x[t * K + j] * r;
+        xh[t * K + j] = x[t * K + j] / s[j];
       } else {
         xh[t * K + j] = x[t * K + j];
       }
@@ -133,10 +139,10 @@ int o_fold_act(const float* x, const float* s, int64_t T, int64_t K, float* xh) 
  * Linear quantization, symmetric.  [INT8] 2.1: Q = round(R/S) + Z followed by
  * saturation to the representable range; Z = 0 for symmetric quantization
  * ([SSZ] iteration stage: symmetric keeps the offset at 0).
- *   code = clamp(rne(fl32(R * fl32(1/S))), -qmax, qmax)
+ *   code = clamp(rne(fl32(R / S)), -qmax, qmax)
  * ------------------------------------------------------------------------- */
-static int code_of(float r, float inv_s, int qmax) {
-  float t = r * inv_s;
+static int code_of(float r, float S, int qmax) {
+  float t = r / S;
   float q = nearbyintf(t);
   if (q > (float)qmax) q = (float)qmax;
   if (q < (float)-qmax) q = (float)-qmax;
@@ -145,34 +151,50 @@ static int code_of(float r, float inv_s, int qmax) {
 
 int o_quant_row(const float* r, int64_t K, float S, int qmax, int8_t* q) {
   if (!r || !q || K <= 0 || !(S > 0.0f) || qmax <= 0 || qmax > 127) return O_EARG;
-  float inv = 1.0f / S;
-  for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_of(r[k], inv, qmax);
+  for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_of(r[k], S, qmax);
   return O_OK;
 }
 
-/* Quantization error of one channel: mean of (w_hat - S*q)^2 over its K
- * elements, fp64, k ascending.  ([SSZ] compares "quantization error"; the
- * mean is this oracle's reading.) */
-double o_mse_row(const float* wh, const int8_t* q, int64_t K, float S) {
-  double acc = 0.0;
+/* Exact sums, rounded once to fp64 (binary128 accumulation; see the header).
+ *   sq_err_exact: sum_k (w_hat_k - S (q_k - z))^2
+ *   dot_exact:    sum_k w_hat_k (q_k - z)
+ *   sum_exact:    sum_k w_hat_k */
+static double sq_err_exact(const float* wh, const int8_t* q, int64_t K, float S, int z) {
+  __float128 acc = 0;
   for (int64_t k = 0; k < K; ++k) {
-    double d = (double)wh[k] - (double)S * (double)q[k];
+    __float128 d = (__float128)wh[k] - (__float128)S * (__float128)((int)q[k] - z);
     acc += d * d;
   }
-  return acc / (double)K;
+  return (double)acc;
+}
+
+static double dot_exact(const float* wh, const int8_t* q, int64_t K, int z) {
+  __float128 acc = 0;
+  for (int64_t k = 0; k < K; ++k) acc += (__float128)wh[k] * (__float128)((int)q[k] - z);
+  return (double)acc;
+}
+
+static double sum_exact(const float* wh, int64_t K) {
+  __float128 acc = 0;
+  for (int64_t k = 0; k < K; ++k) acc += (__float128)wh[k];
+  return (double)acc;
+}
+
+/* Quantization error of one channel: the mean of (w_hat - S*q)^2 over its K
+ * elements -- the exact sum rounded to fp64, then divided by K in fp64.
+ * ([SSZ] compares "quantization error"; the mean is this oracle's reading.) */
+double o_mse_row(const float* wh, const int8_t* q, int64_t K, float S) {
+  return sq_err_exact(wh, q, K, S, 0) / (double)K;
 }
 
 /* Least-squares scale for fixed codes: argmin_S sum (w_hat - S q)^2 =
- * sum(w_hat q) / sum(q^2).  Returns the fp64 quotient, or 0 when sum(q^2)=0.
+ * sum(w_hat q) / sum(q^2), the numerator the exact sum rounded to fp64.
+ * Returns the fp64 quotient, or 0 when sum(q^2)=0.
  * ([SSZ] each iteration fits the scale by least squares.) */
 double o_lsq_scale(const float* wh, const int8_t* q, int64_t K) {
-  double A = 0.0;
   int64_t B = 0;
-  for (int64_t k = 0; k < K; ++k) {
-    A += (double)wh[k] * (double)q[k];
-    B += (int64_t)q[k] * (int64_t)q[k];
-  }
-  return B == 0 ? 0.0 : A / (double)B;
+  for (int64_t k = 0; k < K; ++k) B += (int64_t)q[k] * (int64_t)q[k];
+  return B == 0 ? 0.0 : dot_exact(wh, q, K, 0) / (double)B;
 }
 
 /* ---------------------------------------------------------------------------
@@ -188,8 +210,10 @@ double o_lsq_scale(const float* wh, const int8_t* q, int64_t K) {
  * Readings taken where the document is silent:
  *   - MinMax init: S0 = max(fl32(max_k |w_hat_k| / qmax), fl32(min_scale)).
  *   - each least-squares step refits S for the codes of the current S:
- *     S' = max(fl32(A/B), fl32(min_scale)), A = sum w_hat q (fp64),
- *     B = sum q^2 (exact); B == 0 leaves nothing to fit and ends the row.
+ *     S' = max(fl32(A/B), fl32(min_scale)), A = sum w_hat q (the exact sum
+ *     rounded to fp64), B = sum q^2 (exact); B == 0 leaves nothing to fit
+ *     and ends the row.
+ *   - errors are o_mse_row's (exact sums, rounded once).
  *   - a candidate is kept only if strictly better (cur < best).
  *   - either convergence test ends the row; d = best - cur is signed, so a
  *     rejected candidate (d <= 0) also ends it (the next step would rebuild
@@ -214,12 +238,9 @@ static void ssz_one_row(const float* wh, int64_t K, int qmax, int max_iter, doub
   double best = o_mse_row(wh, q, K, S);
   if (hist) hist[0] = best;
 
-  double A = 0.0;
+  double A = dot_exact(wh, q, K, 0);
   int64_t B = 0;
-  for (int64_t k = 0; k < K; ++k) {
-    A += (double)wh[k] * (double)q[k];
-    B += (int64_t)q[k] * (int64_t)q[k];
-  }
+  for (int64_t k = 0; k < K; ++k) B += (int64_t)q[k] * (int64_t)q[k];
 
   int it = 0;
   for (int i = 1; i <= max_iter; ++i) {
@@ -235,12 +256,9 @@ static void ssz_one_row(const float* wh, int64_t K, int qmax, int max_iter, doub
       S = Sc;
       best = cur;
       memcpy(q, qc, (size_t)K);
-      A = 0.0;
+      A = dot_exact(wh, q, K, 0);
       B = 0;
-      for (int64_t k = 0; k < K; ++k) {
-        A += (double)wh[k] * (double)q[k];
-        B += (int64_t)q[k] * (int64_t)q[k];
-      }
+      for (int64_t k = 0; k < K; ++k) B += (int64_t)q[k] * (int64_t)q[k];
     }
     if (hist) hist[i] = best;
     if (conv) break;
@@ -331,12 +349,9 @@ int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits
     S[n] = S0 < min_scale ? min_scale : S0;
     o_quant_row(r, K, S[n], qmax, q);
     best[n] = o_mse_row(r, q, K, S[n]) * scale;
-    A[n] = 0.0;
+    A[n] = dot_exact(r, q, K, 0);
     B[n] = 0;
-    for (int64_t k = 0; k < K; ++k) {
-      A[n] += (double)r[k] * (double)q[k];
-      B[n] += (int64_t)q[k] * (int64_t)q[k];
-    }
+    for (int64_t k = 0; k < K; ++k) B[n] += (int64_t)q[k] * (int64_t)q[k];
     iters[n] = 0;
     done[n] = 0;
   }
@@ -361,12 +376,9 @@ int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits
       if (cur < best[n]) {
         S[n] = Sc;
         best[n] = cur;
-        A[n] = 0.0;
+        A[n] = dot_exact(r, q, K, 0);
         B[n] = 0;
-        for (int64_t k = 0; k < K; ++k) {
-          A[n] += (double)r[k] * (double)q[k];
-          B[n] += (int64_t)q[k] * (int64_t)q[k];
-        }
+        for (int64_t k = 0; k < K; ++k) B[n] += (int64_t)q[k] * (int64_t)q[k];
       }
       if (conv) done[n] = 1;
     }
@@ -384,7 +396,7 @@ int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits
  * saturation; the SSZ document's asymmetric mode lets the offset move
  * ([SSZ] iteration stage; "symmetric: false" in the option table) and
  * supports it for int8 only ([SSZ] limits: no int4 asymmetric).
- *   code = clamp(rne(fl32(R * fl32(1/S))) + Z, -128, 127),  Z an integer,
+ *   code = clamp(rne(fl32(R / S)) + Z, -128, 127),  Z an integer,
  *   dequantized value S * (code - Z).
  * Readings: the full two's-complement range [-128, 127] (256 levels); Z is
  * an integer in that range.
@@ -392,8 +404,8 @@ int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits
 #define O_QMIN_ASYM (-128)
 #define O_QMAX_ASYM 127
 
-static int code_asym(float r, float inv_s, int z) {
-  float t = r * inv_s;
+static int code_asym(float r, float S, int z) {
+  float t = r / S;
   int q = (int)nearbyintf(t);
   /* saturate before adding Z so that a huge |t| cannot overflow the int */
   if (q > 1000) q = 1000;
@@ -406,43 +418,41 @@ static int code_asym(float r, float inv_s, int z) {
 
 int o_quant_row_asym(const float* r, int64_t K, float S, int Z, int8_t* q) {
   if (!r || !q || K <= 0 || !(S > 0.0f) || Z < O_QMIN_ASYM || Z > O_QMAX_ASYM) return O_EARG;
-  float inv = 1.0f / S;
-  for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_asym(r[k], inv, Z);
+  for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_asym(r[k], S, Z);
   return O_OK;
 }
 
-/* mean of (w_hat - S*(q - Z))^2, fp64, k ascending */
+/* mean of (w_hat - S*(q - Z))^2: the exact sum rounded to fp64, divided by K in fp64 */
 double o_mse_row_asym(const float* wh, const int8_t* q, int64_t K, float S, int Z) {
-  double acc = 0.0;
-  for (int64_t k = 0; k < K; ++k) {
-    double d = (double)wh[k] - (double)S * (double)((int)q[k] - Z);
-    acc += d * d;
-  }
-  return acc / (double)K;
+  return sq_err_exact(wh, q, K, S, Z) / (double)K;
 }
 
-/* Least squares over scale and offset for fixed codes: the line w ~ a*q + b
- * that minimises sum (w_hat - a q - b)^2, from its 2x2 normal equations
- *   [sum q^2  sum q] [a]   [sum w q]
- *   [sum q    K    ] [b] = [sum w  ]
- * solved as a = (K sum wq - sum w sum q) / det, b = (sum w - a sum q) / K,
- * det = K sum q^2 - (sum q)^2 (exact integers; fp64 for the w sums).
+/* Least squares over scale and offset for fixed codes.  The dequantized weight
+ * is S (q - Z), so the fit is taken in the offset-relative codes r = q - Z:
+ * the line w ~ a*r + b that minimises sum (w_hat - a r - b)^2, from its 2x2
+ * normal equations
+ *   [sum r^2  sum r] [a]   [sum w r]
+ *   [sum r    K    ] [b] = [sum w  ]
+ * solved as a = (K sum wr - sum w sum r) / det, b = (sum w - a sum r) / K,
+ * det = K sum r^2 - (sum r)^2 (exact integers; sum w r and sum w are the
+ * exact sums rounded to fp64; each fp64 operation in the order written).
+ * a is the scale of the fitted line and b its intercept, so the refit
+ * parameters are S' = a and Z' = Z - b/a (rounded; see ssz_asym_one_row).
  * ([SSZ] asymmetric mode fits scale and offset together by least squares.)
  * Returns 1 and a, b when det > 0; 0 when all codes are equal (nothing to fit). */
-int o_lsq_affine(const float* wh, const int8_t* q, int64_t K, double* a, double* b) {
-  double sw = 0.0, swq = 0.0;
-  int64_t sq = 0, sqq = 0;
+int o_lsq_affine(const float* wh, const int8_t* q, int64_t K, int Z, double* a, double* b) {
+  int64_t sr = 0, srr = 0;
   for (int64_t k = 0; k < K; ++k) {
-    sw += (double)wh[k];
-    swq += (double)wh[k] * (double)q[k];
-    sq += q[k];
-    sqq += (int64_t)q[k] * q[k];
+    int64_t r = (int64_t)q[k] - Z;
+    sr += r;
+    srr += r * r;
   }
-  int64_t det = K * sqq - sq * sq;
+  int64_t det = K * srr - sr * sr;
   if (det <= 0) return 0;
-  double aa = ((double)K * swq - sw * (double)sq) / (double)det;
+  double sw = sum_exact(wh, K), swr = dot_exact(wh, q, K, Z);
+  double aa = ((double)K * swr - sw * (double)sr) / (double)det;
   *a = aa;
-  *b = (sw - aa * (double)sq) / (double)K;
+  *b = (sw - aa * (double)sr) / (double)K;
   return 1;
 }
 
@@ -455,14 +465,15 @@ int o_lsq_affine(const float* wh, const int8_t* q, int64_t K, double* a, double*
  * Readings taken where the document is silent:
  *   - MinMax init from the channel's min lo and max hi:
  *       S0 = max(fl32(fl32(hi - lo) / 255), fl32(min_scale)),
- *       Z0 = clamp(-128 - rne(fl32(lo * fl32(1/S0))), -128, 127),
+ *       Z0 = clamp(-128 - rne(fl32(lo / S0)), -128, 127),
  *     which maps lo to -128 and hi to (about) 127.
- *   - each least-squares step fits the line w ~ a q + b to the codes q of
- *     the current (S, Z) (o_lsq_affine) and converts it to parameters:
+ *   - each least-squares step fits the line w ~ a r + b to the offset-relative
+ *     codes r = q - Z of the current (S, Z) (o_lsq_affine) and converts it to
+ *     parameters:
  *       S' = max(fl32(a), fl32(min_scale)),
- *       Z' = clamp(rne(-b / a), -128, 127)   (fp64 quotient, ties to even),
- *     since S (q - Z) = S q - S Z.  All codes equal (det = 0) leaves nothing
- *     to fit and ends the row.
+ *       Z' = clamp(Z - rne(b / a), -128, 127)   (fp64 quotient, ties to even),
+ *     since a r + b = a (q - (Z - b/a)).  All codes equal (det = 0) leaves
+ *     nothing to fit and ends the row.
  *   - the candidate's error is computed with its own codes; kept only if
  *     strictly better; iters, convergence and hist as in the symmetric case.
  * ------------------------------------------------------------------------- */
@@ -477,8 +488,7 @@ static void ssz_asym_one_row(const float* wh, int64_t K, int max_iter, double th
   float range = hi - lo;
   float S = range / 255.0f;
   if (S < min_scale) S = min_scale;
-  float inv0 = 1.0f / S;
-  int Z = O_QMIN_ASYM - (int)nearbyintf(lo * inv0);
+  int Z = O_QMIN_ASYM - (int)nearbyintf(lo / S);
   if (Z < O_QMIN_ASYM) Z = O_QMIN_ASYM;
   if (Z > O_QMAX_ASYM) Z = O_QMAX_ASYM;
   o_quant_row_asym(wh, K, S, Z, q);
@@ -489,10 +499,10 @@ static void ssz_asym_one_row(const float* wh, int64_t K, int max_iter, double th
   for (int i = 1; i <= max_iter; ++i) {
     it = i;
     double a, b;
-    if (!o_lsq_affine(wh, q, K, &a, &b)) break;
+    if (!o_lsq_affine(wh, q, K, Z, &a, &b)) break;
     float Sc = (float)a;
     if (Sc < min_scale) Sc = min_scale;
-    double zr = nearbyint(-b / a);
+    double zr = (double)Z - nearbyint(b / a);
     int Zc = zr < (double)O_QMIN_ASYM ? O_QMIN_ASYM : (zr > (double)O_QMAX_ASYM ? O_QMAX_ASYM : (int)zr);
     o_quant_row_asym(wh, K, Sc, Zc, qc);
     double cur = o_mse_row_asym(wh, qc, K, Sc, Zc);
@@ -582,7 +592,7 @@ int o_pack_int4(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
  * token row computed from that row at run time; the smoothing fold X/s is
  * applied first.
  *   a_t = max_j |x_hat[t,j]|,  delta_t = a_t > 0 ? fl32(a_t / 127) : 1,
- *   Xq[t,j] = clamp(rne(fl32(x_hat[t,j] * fl32(1/delta_t))), -127, 127).
+ *   Xq[t,j] = clamp(rne(fl32(x_hat[t,j] / delta_t)), -127, 127).
  * ([SQ] per-channel activation scales do not fit integer GEMM kernels, which
  * is why the activation scale varies per token and the channel variation is
  * moved into the weights; [INT8] 2.1 for the formula; section 6 closes on
@@ -608,8 +618,7 @@ int o_quant_per_token(const float* x, const float* s, int64_t T, int64_t K, int8
           if (v > a) a = v;
         }
         float d = a > 0.0f ? a / 127.0f : 1.0f;
-        float inv = 1.0f / d;
-        for (int64_t j = 0; j < K; ++j) xq[t * K + j] = (int8_t)code_of(xh[j], inv, 127);
+        for (int64_t j = 0; j < K; ++j) xq[t * K + j] = (int8_t)code_of(xh[j], d, 127);
         delta[t] = d;
       }
     }
@@ -662,8 +671,8 @@ int o_dequant(const int64_t* acc, const float* delta, const float* S, int64_t M,
  *       relu: v > 0 ? v : +0;   gelu: fl32(0.5 v (1 + erf(v / sqrt 2))) (fp32 erff)
  *   - output f32: v;  bf16: v rounded to nearest-even bf16;  int8: the next
  *     layer's static per-tensor quantization of v, with its smoothing fold
- *     x_hat = fl32(v * fl32(1/next_s[n])) when next_s is given, then
- *     clamp(rne(fl32(x_hat * fl32(1/out_scale))), -127, 127).
+ *     x_hat = fl32(v / next_s[n]) when next_s is given, then
+ *     clamp(rne(fl32(x_hat / out_scale)), -127, 127).
  *   - the q_sigmoid snippet of [INT8] 3.3 is an integer sigmoid for a
  *     convolutional network; the linear layers here use ReLU (OPT) or GELU
  *     (GPT) instead.
@@ -696,7 +705,6 @@ int o_epilogue(const int64_t* acc, int64_t M, int64_t N, const float* tok_scale,
   if (!acc || !tok_scale || !ch_scale || !out || M < 0 || N < 0) return O_EARG;
   if (act < O_ACT_NONE || act > O_ACT_GELU || out_type < O_OUT_F32 || out_type > O_OUT_I8) return O_EARG;
   if (out_type == O_OUT_I8 && !(out_scale > 0.0f)) return O_EARG;
-  const float inv_out = out_type == O_OUT_I8 ? 1.0f / out_scale : 0.0f;
   for (int64_t t = 0; t < M; ++t) {
     for (int64_t n = 0; n < N; ++n) {
       int64_t a = acc[t * N + n];
@@ -711,8 +719,8 @@ int o_epilogue(const int64_t* acc, int64_t M, int64_t N, const float* tok_scale,
       } else if (out_type == O_OUT_BF16) {
         ((uint16_t*)out)[t * N + n] = o_bf16_rne(v);
       } else {
-        float xh = next_s ? v * (1.0f / next_s[n]) : v;
-        ((int8_t*)out)[t * N + n] = (int8_t)code_of(xh, inv_out, 127);
+        float xh = next_s ? v / next_s[n] : v;
+        ((int8_t*)out)[t * N + n] = (int8_t)code_of(xh, out_scale, 127);
       }
     }
   }
@@ -728,7 +736,7 @@ int o_epilogue(const int64_t* acc, int64_t M, int64_t N, const float* tok_scale,
  *
  * Readings:
  *   - the tracked range is per tensor: a = max over the batch of |x_hat|,
- *     x_hat the smoothed activation fl32(x * fl32(1/s_j)) (s may be NULL);
+ *     x_hat the smoothed activation fl32(x / s_j) (s may be NULL);
  *   - moving average: the first batch sets the state, later batches update
  *     state = fl32(fl32(m * state) + fl32(fl32(1 - m) * a)) with momentum m in
  *     [0, 1) -- the pages give no momentum; it is a labelled parameter
@@ -737,16 +745,17 @@ int o_epilogue(const int64_t* acc, int64_t M, int64_t N, const float* tok_scale,
  *   - per-tensor weight scale = max(fl32(max|w_hat| / 127), fl32(min_scale)),
  *     w_hat = fl32(w * s_j) (the MinMax rule of the per-channel path on the
  *     whole tensor; the SSZ search itself is per-channel only, [SSZ] 使用限制).
- * Both are computed from column maxima: for a positive constant r and RNE,
- * max_t |fl32(x_tj * r)| = fl32(max_t |x_tj| * r) (rounding is monotone).
+ * Both can be computed from column maxima: for a positive constant c and RNE,
+ * max_t |fl32(x_tj / c)| = fl32(max_t |x_tj| / c) and likewise for x_tj * c
+ * (rounding is monotone).
  * ========================================================================= */
 #define O_FOLD_NONE 0
-#define O_FOLD_DIV 1 /* activation side: x * fl32(1/s_j) */
+#define O_FOLD_DIV 1 /* activation side: x / s_j */
 #define O_FOLD_MUL 2 /* weight side: w * s_j */
 
 static float fold_one(float x, const float* s, int64_t j, int fold) {
   if (!s || fold == O_FOLD_NONE) return x;
-  return fold == O_FOLD_DIV ? x * (1.0f / s[j]) : x * s[j];
+  return fold == O_FOLD_DIV ? x / s[j] : x * s[j];
 }
 
 /* max over the whole [rows, cols] tensor of |fold(x)| (element by element, no shortcut) */
@@ -783,12 +792,11 @@ float o_weight_scale_per_tensor(float amax, float min_scale) {
   return S < min_scale ? min_scale : S;
 }
 
-/* codes of a whole tensor with one static scale S: clamp(rne(fl32(fold(x) * fl32(1/S))), -127, 127) */
+/* codes of a whole tensor with one static scale S: clamp(rne(fl32(fold(x) / S)), -127, 127) */
 int o_quant_static(const float* x, int64_t rows, int64_t cols, const float* s, int fold, float S, int8_t* q) {
   if (!x || !q || rows < 0 || cols <= 0 || !(S > 0.0f) || fold < O_FOLD_NONE || fold > O_FOLD_MUL) return O_EARG;
   if (!all_finite(x, rows * cols)) return O_ENONFINITE;
-  float inv = 1.0f / S;
   for (int64_t r = 0; r < rows; ++r)
-    for (int64_t j = 0; j < cols; ++j) q[r * cols + j] = (int8_t)code_of(fold_one(x[r * cols + j], s, j, fold), inv, 127);
+    for (int64_t j = 0; j < cols; ++j) q[r * cols + j] = (int8_t)code_of(fold_one(x[r * cols + j], s, j, fold), S, 127);
   return O_OK;
 }

@@ -159,16 +159,14 @@ def test_ssz_scale_all_rows_properties(pq, bits):
         for r0 in range(0, case.N, 1024):
             r1 = min(r0 + 1024, case.N)
             wr, Sr, cr = w[r0:r1], S[r0:r1], codes[r0:r1]
-            inv = (np.float32(1.0) / Sr).astype(np.float32)
-            q = np.clip(np.rint((wr * inv[:, None]).astype(np.float32)), -qmax, qmax)
+            q = np.clip(np.rint(wr / Sr[:, None]), -qmax, qmax)
             np.testing.assert_array_equal(q, cr, err_msg=f"{case.name} rows {r0}..{r1}: codes of the returned scale")
             e = ((wr.astype(np.float64) - Sr.astype(np.float64)[:, None] * cr) ** 2).mean(axis=1)
             rel = np.abs(mse[r0:r1] - e) / np.maximum(e, 1e-300)
             rel[e == 0] = np.abs(mse[r0:r1][e == 0])
             assert rel.max() <= 1e-9, f"{case.name} rows {r0}..{r1}: reported error {rel.max():.2e} off"
             S0 = np.maximum((np.abs(wr).max(axis=1) / np.float32(qmax)).astype(np.float32), floor)
-            inv0 = (np.float32(1.0) / S0).astype(np.float32)
-            q0 = np.clip(np.rint((wr * inv0[:, None]).astype(np.float32)), -qmax, qmax)
+            q0 = np.clip(np.rint(wr / S0[:, None]), -qmax, qmax)
             e0 = ((wr.astype(np.float64) - S0.astype(np.float64)[:, None] * q0) ** 2).mean(axis=1)
             assert np.all(mse[r0:r1] <= e0 * (1 + 1e-9)), f"{case.name} rows {r0}..{r1}: worse than MinMax"
 

@@ -42,15 +42,46 @@ def test_rounding_power_of_two_scale():
         np.testing.assert_array_equal(oracle.quant_row(r, S, 127), want)
 
 
-def test_rounding_matches_rint_of_rounded_product():
-    """General S: the code is numpy's rint (ties-to-even) of the fp32 product with the fp32 reciprocal."""
+def _boundary_values(rng, S, reach=4):
+    """fp32 values within `reach` ulps of every half-integer multiple (k + 1/2) S, k = -128..127 -- where a
+    quotient rounded in another order (for instance through the fp32 reciprocal) lands on the other code --
+    plus normal values."""
+    mids = ((np.arange(-128, 128) + 0.5) * np.float64(S)).astype(np.float32)
+    out, up, down = [mids], mids, mids
+    for _ in range(reach):
+        up = np.nextafter(up, np.float32(np.inf)).astype(np.float32)
+        down = np.nextafter(down, np.float32(-np.inf)).astype(np.float32)
+        out += [up, down]
+    return np.concatenate(out + [(rng.standard_normal(4000) * 50 * S).astype(np.float32)])
+
+
+def test_rounding_is_rint_of_fp32_quotient():
+    """General S: the code is numpy's rint (ties to even) of numpy's IEEE float32 quotient R / S, clipped
+    ([INT8] 2.1 Q = round(R/S)).  The values sit next to every rounding boundary, where the product with the
+    rounded reciprocal fl32(R fl32(1/S)) gives another code: the test asserts that such values are present."""
     rng = np.random.default_rng(2)
-    for _ in range(20):
+    differs = 0
+    for _ in range(200):
         S = np.float32(rng.uniform(1e-4, 1.0))
-        r = (rng.standard_normal(5000) * 50 * S).astype(np.float32)
-        inv = np.float32(1.0) / S
-        want = np.clip(np.rint(r * inv), -127, 127).astype(np.int8)
+        r = _boundary_values(rng, S)
+        want = np.clip(np.rint(r / S), -127, 127).astype(np.int8)
         np.testing.assert_array_equal(oracle.quant_row(r, S, 127), want)
+        via_recip = np.clip(np.rint(r * (np.float32(1.0) / S)), -127, 127).astype(np.int8)
+        differs += int(np.count_nonzero(via_recip != want))
+    assert differs > 0, "no value separates the quotient from the reciprocal product"
+
+
+def test_fold_act_is_fp32_quotient():
+    """x_hat = fl32(X / s_j) ([SQ] X diag(s)^-1): numpy's float32 division, column by column, on values that
+    include cases where the product with fl32(1/s_j) differs."""
+    rng = np.random.default_rng(3)
+    T, K = 64, 512
+    x = (rng.standard_normal((T, K)) * 3).astype(np.float32)
+    s = np.exp(rng.uniform(-4, 4, K)).astype(np.float32)
+    want = x / s[None, :]
+    got = oracle.fold_act(x, s)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.count_nonzero(x * (np.float32(1.0) / s)[None, :] != want) > 0
 
 
 # ---------------------------------------------------------------- smoothing (pins 2, 4)
@@ -227,6 +258,54 @@ def test_mse_closed_form():
     assert oracle.mse_row(w2, q, S) == (2.0 ** -12) ** 2 / 8
 
 
+def _exact_sum(terms):
+    """The exact real sum of float terms (each a Fraction-exact product), rounded once to fp64."""
+    from fractions import Fraction
+    return float(sum((Fraction(t) for t in terms), Fraction(0)))
+
+
+def test_mse_is_the_exact_sum_rounded_once():
+    """mse = fl64(exact sum of (w - S q)^2) / K: python's exact rationals on rows whose terms span many binary
+    orders, and a row where the fp64 running sum in index order gives another double (1 + 3 * 2^-54 -> the
+    exact sum rounds up; the running sum never moves off 1)."""
+    from fractions import Fraction
+    w = np.array([1.0, 2.0 ** -27, 2.0 ** -27, 2.0 ** -27], dtype=np.float32)
+    q = np.zeros(4, dtype=np.int8)
+    want = float(1 + 3 * Fraction(2) ** -54) / 4
+    assert want == (1 + 2.0 ** -52) / 4
+    assert oracle.mse_row(w, q, 1.0) == want
+    run = 0.0
+    for v in w.astype(np.float64):
+        run += v * v
+    assert run / 4 != want
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        K = int(rng.integers(1, 48))
+        S = np.float32(np.exp(rng.uniform(-12, 0)))
+        w = (rng.standard_normal(K) * np.exp(rng.uniform(-20, 3, K)) * S * 40).astype(np.float32)
+        q = oracle.quant_row(w, S, 127)
+        terms = [(Fraction(float(a)) - Fraction(float(S)) * int(b)) ** 2 for a, b in zip(w, q)]
+        assert oracle.mse_row(w, q, S) == float(sum(terms, Fraction(0))) / K
+
+
+def test_lsq_numerator_is_the_exact_sum_rounded_once():
+    """S' = fl64(exact sum w q) / sum q^2: exact rationals, and a row where the running fp64 sum cancels to 0."""
+    from fractions import Fraction
+    w = np.array([1.0, 2.0 ** -60, -1.0], dtype=np.float32)
+    q = np.array([1, 1, 1], dtype=np.int8)
+    assert oracle.lsq_scale(w, q) == 2.0 ** -60 / 3
+    rng = np.random.default_rng(13)
+    for _ in range(300):
+        K = int(rng.integers(1, 48))
+        w = (rng.standard_normal(K) * np.exp(rng.uniform(-30, 3, K))).astype(np.float32)
+        q = rng.integers(-127, 128, K).astype(np.int8)
+        B = int(np.sum(q.astype(np.int64) ** 2))
+        if B == 0:
+            continue
+        A = float(sum((Fraction(float(a)) * int(b) for a, b in zip(w, q)), Fraction(0)))
+        assert oracle.lsq_scale(w, q) == A / B
+
+
 @pytest.mark.parametrize("bits,qmax", [(8, 127), (4, 7)])
 def test_ssz_exact_grid_row(bits, qmax):
     """Row = c * integers with max |k| = qmax, c = 2^-k: lossless, S = c, one step, error 0."""
@@ -304,22 +383,46 @@ def test_asym_code_table():
 
 
 def test_asym_lsq_brute_force():
-    """For fixed codes, sum(w - a q - b)^2 is minimised at the normal-equation solution: grid search."""
+    """For fixed codes and offset Z, sum(w - a (q - Z) - b)^2 is minimised at the normal-equation solution:
+    grid search."""
     rng = np.random.default_rng(31)
     for _ in range(60):
         K = int(rng.integers(2, 9))
         w = rng.standard_normal(K).astype(np.float32)
         q = rng.integers(-128, 128, K).astype(np.int8)
+        Z = int(rng.integers(-128, 128))
         if np.all(q == q[0]):
             q[0] = q[0] ^ 1
-        a, b = oracle.lsq_affine(w, q)
-        wd, qd = w.astype(np.float64), q.astype(np.float64)
+        a, b = oracle.lsq_affine(w, q, Z)
+        wd, qd = w.astype(np.float64), q.astype(np.float64) - Z
         ga = np.linspace(a - 2e-3, a + 2e-3, 401)
         gb = np.linspace(b - 0.05, b + 0.05, 401)
         err = ((wd[None, None, :] - ga[:, None, None] * qd[None, None, :] - gb[None, :, None]) ** 2).sum(-1)
         i, j = np.unravel_index(np.argmin(err), err.shape)
         assert abs(ga[i] - a) <= 1.01 * (ga[1] - ga[0]) and abs(gb[j] - b) <= 1.01 * (gb[1] - gb[0])
     assert oracle.lsq_affine(np.ones(5, np.float32), np.full(5, 7, np.int8)) is None
+
+
+def test_asym_lsq_sums_are_exact():
+    """The fit's sums (sum w r, sum w) are the exact sums rounded once, then the normal equations in fp64 in
+    the written order: python's exact rationals and IEEE doubles reproduce (a, b) bit for bit."""
+    from fractions import Fraction
+    rng = np.random.default_rng(35)
+    for _ in range(200):
+        K = int(rng.integers(2, 40))
+        w = (rng.standard_normal(K) * np.exp(rng.uniform(-25, 2, K))).astype(np.float32)
+        q = rng.integers(-128, 128, K).astype(np.int8)
+        Z = int(rng.integers(-128, 128))
+        r = [int(v) - Z for v in q]
+        sr, srr = sum(r), sum(v * v for v in r)
+        det = K * srr - sr * sr
+        if det <= 0:
+            continue
+        swr = float(sum((Fraction(float(a)) * b for a, b in zip(w, r)), Fraction(0)))
+        sw = float(sum((Fraction(float(a)) for a in w), Fraction(0)))
+        a = (float(K) * swr - sw * float(sr)) / float(det)
+        b = (sw - a * float(sr)) / float(K)
+        assert oracle.lsq_affine(w, q, Z) == (a, b)
 
 
 def test_asym_exact_grid_row():
@@ -386,9 +489,9 @@ def test_asym_monotone_consistent_and_fixed_point():
         if 1 <= it < 20 and r["mse"][n] > 0:
             if seq[-1] == seq[-2]:
                 # the last candidate was rejected: it is rebuilt from the kept codes and is again no better
-                a, b = oracle.lsq_affine(w[n], r["q"][n])
+                a, b = oracle.lsq_affine(w[n], r["q"][n], int(r["Z"][n]))
                 Sn = max(np.float32(a), fmin)
-                Zn = int(min(127, max(-128, np.rint(-b / a))))
+                Zn = int(min(127, max(-128, int(r["Z"][n]) - np.rint(b / a))))
                 cur = oracle.mse_row_asym(w[n], oracle.quant_row_asym(w[n], Sn, Zn), Sn, Zn)
                 assert cur >= r["mse"][n]
             else:
