@@ -29,9 +29,10 @@
  *     ptq_last_error() returns a message for the calling thread.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified results.
  *   - Rounding: fl32 denotes IEEE binary32 round-to-nearest-even.  A division
- *     R/S by a scale is evaluated as fl32(R * fl32(1/S)); round() is
- *     round-half-to-even; codes saturate symmetrically to [-qmax, qmax]
- *     (qmax = 127 for int8, 7 for int4), so the zero point is 0.
+ *     R/S by a scale (or by a smoothing factor) is the IEEE quotient
+ *     fl32(R / S); round() is round-half-to-even; symmetric codes saturate to
+ *     [-qmax, qmax] (qmax = 127 for int8, 7 for int4), so the zero point is 0.
+ *   - Folded values (x / s_j, w * s_j) must be finite as well.
  *
  * Sources, cited by page title and section:
  *   [PTQ]  tutorial chapter "4. 训练后量化（PTQ）" -- the four-step PTQ flow
@@ -71,9 +72,10 @@ extern "C" {
 #define PTQ_SSZ_THRESHOLD 1e-10
 #define PTQ_SSZ_MIN_SCALE 1e-5f
 
-/* Largest K for which no int8 x int8 dot product can overflow int32:
- * floor((2^31 - 1) / 127^2).  ([INT8] 5.1 overflow.) */
-#define PTQ_GEMM_MAX_K 133144
+/* Largest K (a multiple of 16) for which no int8 x int8 dot product can
+ * overflow int32, whatever the codes -- (-128) * (-128) = 2^14 per term:
+ * 2^14 K <= 2^31 - 1.  ([INT8] 5.1 overflow.) */
+#define PTQ_GEMM_MAX_K 131056
 
 /* Every K must be a multiple of this (16-byte vector rows, [INT8] 3.1). */
 #define PTQ_K_MULTIPLE 16
@@ -148,12 +150,14 @@ PTQ_API ptq_status sq_smooth_factors(const float* act_amax, const float* w_amax,
  *   S = max(fl32(max_k |w_hat[k]| / qmax), min_scale);  q = quant(S);  best = mse(S)
  *   repeat up to max_iter times (the row stops on its own):
  *     if sum q^2 == 0: stop
- *     S' = max(fl32(sum(w_hat q) / sum(q^2)), min_scale);  cur = mse(S')
+ *     S' = max(fl32(A / sum(q^2)), min_scale);  cur = mse(S')
  *     converged = best == 0 || (best - cur)/best < threshold || |best - cur| < threshold
  *     if cur < best: S = S', q = quant(S'), best = cur
  *     if converged: stop
- * quant(S)[k] = clamp(rne(fl32(w_hat[k] * fl32(1/S))), -qmax, qmax);
- * mse(S) = mean_k (w_hat[k] - S q[k])^2 in fp64.
+ * quant(S)[k] = clamp(rne(fl32(w_hat[k] / S)), -qmax, qmax);
+ * A = sum_k w_hat[k] q[k], and mse(S) = E / K with E = sum_k (w_hat[k] - S q[k])^2,
+ * where A and E are the exact sums rounded once to fp64 (the division by K in
+ * fp64); every comparison and quotient above is fp64.
  *
  *   w          [N, K] of `dtype`, 16-B aligned;  N >= 1;  K multiple of 16, <= 131072
  *   s          [K] fp32 smoothing factors, or NULL for no smoothing
@@ -181,17 +185,20 @@ PTQ_API ptq_status ssz_weight_qparams(const void* w, int dtype, int64_t N, int64
  * saturation.
  *
  * For each row n, with w_hat as above:
- *   quant(S, Z)[k] = clamp(rne(fl32(w_hat[k] * fl32(1/S))) + Z, -128, 127)
- *   mse(S, Z)      = mean_k (w_hat[k] - S (q[k] - Z))^2 in fp64
+ *   quant(S, Z)[k] = clamp(rne(fl32(w_hat[k] / S)) + Z, -128, 127)
+ *   mse(S, Z)      = mean_k (w_hat[k] - S (q[k] - Z))^2 (the exact sum rounded
+ *                    once to fp64, divided by K in fp64)
  *   init: lo = min_k w_hat[k], hi = max_k w_hat[k];
  *         S = max(fl32(fl32(hi - lo) / 255), min_scale);
- *         Z = clamp(-128 - rne(fl32(lo * fl32(1/S))), -128, 127)
- *   step: for the codes q of the current (S, Z), the least-squares line
- *         w_hat ~ a q + b (2x2 normal equations; det = K sum q^2 - (sum q)^2,
- *         det == 0 stops the row);  S' = max(fl32(a), min_scale),
- *         Z' = clamp(rne(-b / a), -128, 127) (fp64 quotient);  kept only if
- *         mse(S', Z') < best;  convergence, iteration limit and per-row stop
- *         exactly as in ssz_weight_qparams.
+ *         Z = clamp(-128 - rne(fl32(lo / S)), -128, 127)
+ *   step: for the offset-relative codes r = q - Z of the current (S, Z), the
+ *         least-squares line w_hat ~ a r + b (2x2 normal equations;
+ *         det = K sum r^2 - (sum r)^2, det == 0 stops the row; sum w_hat r and
+ *         sum w_hat the exact sums rounded once to fp64;
+ *         a = (K sum w_hat r - sum w_hat sum r) / det, b = (sum w_hat - a sum r) / K);
+ *         S' = max(fl32(a), min_scale), Z' = clamp(Z - rne(b / a), -128, 127)
+ *         (fp64 quotient);  kept only if mse(S', Z') < best;  convergence,
+ *         iteration limit and per-row stop exactly as in ssz_weight_qparams.
  * Dequantized weight: S (q - Z).
  *
  *   w, s, N, K, max_iter, threshold, min_scale   as for ssz_weight_qparams
@@ -210,10 +217,10 @@ PTQ_API ptq_status ssz_weight_qparams_asym(const void* w, int dtype, int64_t N, 
  * [SQ] the activation side of the fold (X diag(s)^-1) and the reason the
  * activation scale varies per token rather than per channel; [INT8] 2.1.
  *
- * For each token row t, with x_hat[j] = fl32(x[t,j] * fl32(1/s[j])) (x_hat = x
+ * For each token row t, with x_hat[j] = fl32(x[t,j] / s[j]) (x_hat = x
  * when s is NULL):
  *   a = max_j |x_hat[j]|;  tok_scale[t] = a > 0 ? fl32(a / 127) : 1
- *   xq[t,j] = clamp(rne(fl32(x_hat[j] * fl32(1/tok_scale[t]))), -127, 127)
+ *   xq[t,j] = clamp(rne(fl32(x_hat[j] / tok_scale[t])), -127, 127)
  *
  *   x          [T, K] of `dtype`, 16-B aligned;  T >= 1;  K multiple of 16, <= 131072
  *   s          [K] fp32 smoothing factors, or NULL
@@ -251,11 +258,13 @@ PTQ_API ptq_status w8a8_gemm_dequant(const int8_t* xq, const int8_t* wq, const f
  *   v = fl32(acc) * fl32(tok_scale[t] * ch_scale[n])      (as w8a8_gemm_dequant)
  *   v = v + bias[n]                                       (bias may be NULL)
  *   act PTQ_ACT_RELU: v = v > 0 ? v : +0
- *       PTQ_ACT_GELU: v = 0.5 v (1 + erf(v / sqrt 2))     (device erff)
+ *       PTQ_ACT_GELU: v = 0.5 v (1 + erf(v / sqrt 2))     (erf from the erfc fit of
+ *                     Numerical Recipes 2nd ed. section 6.2, relative error < 1.2e-7:
+ *                     within about an ulp of the correctly rounded erf)
  *   out_type PTQ_OUT_F32:  out[t,n] = v                     float  [M, N]
  *            PTQ_OUT_BF16: out[t,n] = bf16 RNE of v         uint16 [M, N]
- *            PTQ_OUT_I8:   x = next_s ? fl32(v * fl32(1/next_s[n])) : v;
- *                          out[t,n] = clamp(rne(fl32(x * fl32(1/out_scale[0]))), -127, 127)   int8 [M, N]
+ *            PTQ_OUT_I8:   x = next_s ? fl32(v / next_s[n]) : v;
+ *                          out[t,n] = clamp(rne(fl32(x / out_scale[0])), -127, 127)   int8 [M, N]
  *              -- the next layer's static per-tensor activation quantization
  *              (see sq_act_scale_ema) with its smoothing fold; its token
  *              scales are then out_scale[0] for every row.
@@ -280,7 +289,7 @@ PTQ_API ptq_status w8a8_gemm_fused(const int8_t* xq, const int8_t* wq, const flo
  *
  * Per calibration batch: col_amax = sq_absmax_calib of the batch (not
  * accumulated), then this call:
- *   a     = max_j fl32(col_amax[j] * fl32(1/s[j]))      (max |x_hat| of the batch; s may be NULL)
+ *   a     = max_j fl32(col_amax[j] / s[j])      (max |x_hat| of the batch; s may be NULL)
  *   state = first ? a : fl32(fl32(momentum * state) + fl32(fl32(1 - momentum) * a))
  *   scale = state > 0 ? fl32(state / 127) : 1
  * The pages give no momentum: it is the caller's parameter, in [0, 1).
@@ -305,10 +314,10 @@ PTQ_API ptq_status weight_scale_per_tensor(const float* col_amax, const float* s
 /*
  * Int8 codes of a whole [rows, cols] tensor with one static scale (scale[0],
  * device): the static per-tensor activation quantization (fold =
- * PTQ_FOLD_DIV: x_hat = fl32(x * fl32(1/s_j))) or the per-tensor weight
+ * PTQ_FOLD_DIV: x_hat = fl32(x / s_j)) or the per-tensor weight
  * quantization (fold = PTQ_FOLD_MUL: w_hat = fl32(w * s_j)); s may be NULL
  * (no fold, fold ignored).  [INT8] 2.1.
- *   q[r, j] = clamp(rne(fl32(x_hat[r, j] * fl32(1/scale[0]))), -127, 127)
+ *   q[r, j] = clamp(rne(fl32(x_hat[r, j] / scale[0])), -127, 127)
  *   row_scale [rows] fp32 output filled with scale[0] (the GEMM's token scales), or NULL
  * Shapes, dtypes and alignment as quant_per_token_i8.
  */

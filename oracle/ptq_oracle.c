@@ -405,12 +405,12 @@ int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits
 #define O_QMAX_ASYM 127
 
 static int code_asym(float r, float S, int z) {
-  float t = r / S;
-  int q = (int)nearbyintf(t);
-  /* saturate before adding Z so that a huge |t| cannot overflow the int */
-  if (q > 1000) q = 1000;
-  if (q < -1000) q = -1000;
-  q += z;
+  float t = nearbyintf(r / S);
+  /* saturate (in floating point) before converting and adding Z, so that a quotient beyond the int range
+   * still lands on its own end of the code range */
+  if (t > 1000.0f) t = 1000.0f;
+  if (t < -1000.0f) t = -1000.0f;
+  int q = (int)t + z;
   if (q > O_QMAX_ASYM) q = O_QMAX_ASYM;
   if (q < O_QMIN_ASYM) q = O_QMIN_ASYM;
   return q;
@@ -488,9 +488,10 @@ static void ssz_asym_one_row(const float* wh, int64_t K, int max_iter, double th
   float range = hi - lo;
   float S = range / 255.0f;
   if (S < min_scale) S = min_scale;
-  int Z = O_QMIN_ASYM - (int)nearbyintf(lo / S);
-  if (Z < O_QMIN_ASYM) Z = O_QMIN_ASYM;
-  if (Z > O_QMAX_ASYM) Z = O_QMAX_ASYM;
+  double zd = (double)O_QMIN_ASYM - (double)nearbyintf(lo / S); /* saturated before the int conversion */
+  if (zd < O_QMIN_ASYM) zd = O_QMIN_ASYM;
+  if (zd > O_QMAX_ASYM) zd = O_QMAX_ASYM;
+  int Z = (int)zd;
   o_quant_row_asym(wh, K, S, Z, q);
   double best = o_mse_row_asym(wh, q, K, S, Z);
   if (hist) hist[0] = best;

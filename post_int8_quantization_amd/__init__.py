@@ -32,7 +32,7 @@ PTQ_F32, PTQ_BF16 = 0, 1
 SSZ_MAX_ITER = 20
 SSZ_THRESHOLD = 1e-10
 SSZ_MIN_SCALE = 1e-5
-GEMM_MAX_K = 133144
+GEMM_MAX_K = 131056
 
 STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE", 4: "PTQ_ERR_UNSUPPORTED",
           5: "PTQ_ERR_ARG", 6: "PTQ_ERR_ALIGN", 7: "PTQ_ERR_HIP"}
@@ -96,14 +96,35 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t, name, dtypes=None):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _dev(t, name, dtypes=None, numel=None, ndim=None, device=None):
+    """Checks a tensor argument: type, dtype, dimensions, size, layout, and the device it shares with the call's
+    other tensors.  The kernels read and write exactly these sizes, so a short buffer is an error here rather
+    than an out-of-bounds access on the device."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if dtypes is not None and t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     return t
+
+
+def _gpu(*ts):
+    """Every tensor argument lives on the GPU (checked after all sizes and types)."""
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensor arguments must be GPU tensors")
+
+
+def _opt(t, name, dtype, numel, device):
+    """An optional argument (None passes through)."""
+    return None if t is None else _dev(t, name, (dtype,), numel=numel, device=device)
 
 
 def _dtype_code(t):
@@ -114,12 +135,13 @@ _FLOATS = (torch.float32, torch.bfloat16)
 
 
 def sq_absmax_calib(x, amax=None, accumulate=False, stream=None):
-    _dev(x, "x", _FLOATS)
+    _dev(x, "x", _FLOATS, ndim=2)
     rows, cols = x.shape
     if amax is None:
         amax = torch.empty(cols, dtype=torch.float32, device=x.device)
         accumulate = False
-    _dev(amax, "amax", (torch.float32,))
+    _dev(amax, "amax", (torch.float32,), numel=cols, device=x.device)
+    _gpu(x, amax)
     _check(lib.sq_absmax_calib(_ptr(x), _dtype_code(x), rows, cols, _ptr(amax), int(bool(accumulate)),
                                _stream(stream)))
     return amax
@@ -127,12 +149,12 @@ def sq_absmax_calib(x, amax=None, accumulate=False, stream=None):
 
 def sq_smooth_factors(act_amax, w_amax, alpha, s=None, stream=None):
     _dev(act_amax, "act_amax", (torch.float32,))
-    _dev(w_amax, "w_amax", (torch.float32,))
     K = act_amax.numel()
-    if w_amax.numel() != K:
-        raise ValueError("act_amax and w_amax differ in length")
+    _dev(w_amax, "w_amax", (torch.float32,), numel=K, device=act_amax.device)
     if s is None:
         s = torch.empty(K, dtype=torch.float32, device=act_amax.device)
+    _dev(s, "s", (torch.float32,), numel=K, device=act_amax.device)
+    _gpu(act_amax, w_amax, s)
     _check(lib.sq_smooth_factors(_ptr(act_amax), _ptr(w_amax), K, float(alpha), _ptr(s), _stream(stream)))
     return s
 
@@ -142,11 +164,10 @@ def ssz_weight_qparams(w, s=None, bits=8, symmetric=True, max_iter=SSZ_MAX_ITER,
                        mse=None, stream=None):
     """Returns (scale[N] fp32, wq (int8 [N,K] or uint8 [N,K/2] for int4) or None, iters or None, mse or None).
     Output tensors may be passed in preallocated."""
-    _dev(w, "w", _FLOATS)
+    _dev(w, "w", _FLOATS, ndim=2)
     N, K = w.shape
     dev = w.device
-    if s is not None:
-        _dev(s, "s", (torch.float32,))
+    _opt(s, "s", torch.float32, K, dev)
     if scale is None:
         scale = torch.empty(N, dtype=torch.float32, device=dev)
     if wq is None and want_codes:
@@ -155,9 +176,12 @@ def ssz_weight_qparams(w, s=None, bits=8, symmetric=True, max_iter=SSZ_MAX_ITER,
     if want_stats:
         iters = torch.empty(N, dtype=torch.int32, device=dev) if iters is None else iters
         mse = torch.empty(N, dtype=torch.float64, device=dev) if mse is None else mse
-    for t, nm in ((scale, "scale"), (wq, "wq"), (iters, "iters"), (mse, "mse")):
-        if t is not None:
-            _dev(t, nm)
+    _dev(scale, "scale", (torch.float32,), numel=N, device=dev)
+    if wq is not None:
+        _dev(wq, "wq", (torch.int8, torch.uint8), numel=N * K if bits == 8 else N * (K // 2), device=dev)
+    _opt(iters, "iters", torch.int32, N, dev)
+    _opt(mse, "mse", torch.float64, N, dev)
+    _gpu(w, s, scale, wq, iters, mse)
     _check(lib.ssz_weight_qparams(_ptr(w), _dtype_code(w), N, K, _ptr(s), int(bits), int(bool(symmetric)),
                                   int(max_iter), float(threshold), float(min_scale), _ptr(scale), _ptr(wq),
                                   _ptr(iters), _ptr(mse), _stream(stream)))
@@ -169,11 +193,10 @@ def ssz_weight_qparams_asym(w, s=None, max_iter=SSZ_MAX_ITER, threshold=SSZ_THRE
                             mse=None, stream=None):
     """Asymmetric int8.  Returns (scale[N] fp32, zero_point[N] int32, wq int8 [N,K] or None, iters or None,
     mse or None).  Output tensors may be passed in preallocated."""
-    _dev(w, "w", _FLOATS)
+    _dev(w, "w", _FLOATS, ndim=2)
     N, K = w.shape
     dev = w.device
-    if s is not None:
-        _dev(s, "s", (torch.float32,))
+    _opt(s, "s", torch.float32, K, dev)
     if scale is None:
         scale = torch.empty(N, dtype=torch.float32, device=dev)
     if zero_point is None:
@@ -183,9 +206,12 @@ def ssz_weight_qparams_asym(w, s=None, max_iter=SSZ_MAX_ITER, threshold=SSZ_THRE
     if want_stats:
         iters = torch.empty(N, dtype=torch.int32, device=dev) if iters is None else iters
         mse = torch.empty(N, dtype=torch.float64, device=dev) if mse is None else mse
-    for t, nm in ((scale, "scale"), (zero_point, "zero_point"), (wq, "wq"), (iters, "iters"), (mse, "mse")):
-        if t is not None:
-            _dev(t, nm)
+    _dev(scale, "scale", (torch.float32,), numel=N, device=dev)
+    _dev(zero_point, "zero_point", (torch.int32,), numel=N, device=dev)
+    _opt(wq, "wq", torch.int8, N * K, dev)
+    _opt(iters, "iters", torch.int32, N, dev)
+    _opt(mse, "mse", torch.float64, N, dev)
+    _gpu(w, s, scale, zero_point, wq, iters, mse)
     _check(lib.ssz_weight_qparams_asym(_ptr(w), _dtype_code(w), N, K, _ptr(s), int(max_iter), float(threshold),
                                        float(min_scale), _ptr(scale), _ptr(zero_point), _ptr(wq), _ptr(iters),
                                        _ptr(mse), _stream(stream)))
@@ -193,30 +219,35 @@ def ssz_weight_qparams_asym(w, s=None, max_iter=SSZ_MAX_ITER, threshold=SSZ_THRE
 
 
 def quant_per_token_i8(x, s=None, xq=None, tok_scale=None, stream=None):
-    _dev(x, "x", _FLOATS)
+    _dev(x, "x", _FLOATS, ndim=2)
     T, K = x.shape
-    if s is not None:
-        _dev(s, "s", (torch.float32,))
+    _opt(s, "s", torch.float32, K, x.device)
     if xq is None:
         xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
     if tok_scale is None:
         tok_scale = torch.empty(T, dtype=torch.float32, device=x.device)
+    _dev(xq, "xq", (torch.int8,), numel=T * K, device=x.device)
+    _dev(tok_scale, "tok_scale", (torch.float32,), numel=T, device=x.device)
+    _gpu(x, s, xq, tok_scale)
     _check(lib.quant_per_token_i8(_ptr(x), _dtype_code(x), T, K, _ptr(s), _ptr(xq), _ptr(tok_scale),
                                   _stream(stream)))
     return xq, tok_scale
 
 
 def w8a8_gemm_dequant(xq, wq, tok_scale, ch_scale, want_acc=False, y=None, stream=None):
-    _dev(xq, "xq", (torch.int8,))
-    _dev(wq, "wq", (torch.int8,))
-    _dev(tok_scale, "tok_scale", (torch.float32,))
-    _dev(ch_scale, "ch_scale", (torch.float32,))
+    _dev(xq, "xq", (torch.int8,), ndim=2)
     M, K = xq.shape
+    dev = xq.device
+    _dev(wq, "wq", (torch.int8,), ndim=2, device=dev)
     N, K2 = wq.shape
     if K2 != K:
         raise ValueError("xq and wq differ in K")
+    _dev(tok_scale, "tok_scale", (torch.float32,), numel=M, device=dev)
+    _dev(ch_scale, "ch_scale", (torch.float32,), numel=N, device=dev)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _dev(y, "y", (torch.float32,), numel=M * N, device=dev)
+    _gpu(xq, wq, tok_scale, ch_scale, y)
     acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
     _check(lib.w8a8_gemm_dequant(_ptr(xq), _ptr(wq), _ptr(tok_scale), _ptr(ch_scale), M, N, K, _ptr(y), _ptr(acc),
                                  _stream(stream)))
@@ -231,20 +262,25 @@ def w8a8_gemm_fused(xq, wq, tok_scale, ch_scale, bias=None, act="none", out="f32
                     want_acc=False, y=None, stream=None):
     """GEMM + dequant + bias + activation, output fp32, bf16 or int8 (the next layer's static quantization:
     next_s [N] its smoothing factors or None, out_scale a 1-element device tensor, its static scale)."""
-    _dev(xq, "xq", (torch.int8,))
-    _dev(wq, "wq", (torch.int8,))
-    _dev(tok_scale, "tok_scale", (torch.float32,))
-    _dev(ch_scale, "ch_scale", (torch.float32,))
-    for t, nm in ((bias, "bias"), (next_s, "next_s"), (out_scale, "out_scale")):
-        if t is not None:
-            _dev(t, nm, (torch.float32,))
+    _dev(xq, "xq", (torch.int8,), ndim=2)
     M, K = xq.shape
+    dev = xq.device
+    _dev(wq, "wq", (torch.int8,), ndim=2, device=dev)
     N, K2 = wq.shape
     if K2 != K:
         raise ValueError("xq and wq differ in K")
+    _dev(tok_scale, "tok_scale", (torch.float32,), numel=M, device=dev)
+    _dev(ch_scale, "ch_scale", (torch.float32,), numel=N, device=dev)
+    _opt(bias, "bias", torch.float32, N, dev)
+    _opt(next_s, "next_s", torch.float32, N, dev)
+    _opt(out_scale, "out_scale", torch.float32, 1, dev)
+    if act not in ACT or out not in OUT:
+        raise ValueError(f"act must be one of {tuple(ACT)} and out one of {tuple(OUT)}")
     code, dt = OUT[out]
     if y is None:
         y = torch.empty((M, N), dtype=dt, device=xq.device)
+    _dev(y, "y", (dt,), numel=M * N, device=dev)
+    _gpu(xq, wq, tok_scale, ch_scale, bias, next_s, out_scale, y)
     acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
     _check(lib.w8a8_gemm_fused(_ptr(xq), _ptr(wq), _ptr(tok_scale), _ptr(ch_scale), _ptr(bias), ACT[act], code,
                                _ptr(next_s), _ptr(out_scale), M, N, K, _ptr(y), _ptr(acc), _stream(stream)))
@@ -261,15 +297,19 @@ def sq_act_scale_ema(col_amax, s=None, momentum=0.9, first=False, state=None, sc
     _dev(col_amax, "col_amax", (torch.float32,))
     K = col_amax.numel()
     dev = col_amax.device
-    if s is not None:
-        _dev(s, "s", (torch.float32,))
+    _opt(s, "s", torch.float32, K, dev)
     if state is None:
         state = torch.zeros(1, dtype=torch.float32, device=dev)
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=dev)
     if row_scale is None and rows > 0:
         row_scale = torch.empty(rows, dtype=torch.float32, device=dev)
+    _dev(state, "state", (torch.float32,), numel=1, device=dev)
+    _dev(scale, "scale", (torch.float32,), numel=1, device=dev)
+    if row_scale is not None:
+        _dev(row_scale, "row_scale", (torch.float32,), device=dev)
     n = row_scale.numel() if row_scale is not None else 0
+    _gpu(col_amax, s, state, scale, row_scale)
     _check(lib.sq_act_scale_ema(_ptr(col_amax), _ptr(s), K, float(momentum), int(bool(first)), _ptr(state),
                                 _ptr(scale), _ptr(row_scale), n, _stream(stream)))
     return state, scale, row_scale
@@ -280,13 +320,16 @@ def weight_scale_per_tensor(col_amax, s=None, min_scale=SSZ_MIN_SCALE, n=0, scal
     _dev(col_amax, "col_amax", (torch.float32,))
     K = col_amax.numel()
     dev = col_amax.device
-    if s is not None:
-        _dev(s, "s", (torch.float32,))
+    _opt(s, "s", torch.float32, K, dev)
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=dev)
     if ch_scale is None and n > 0:
         ch_scale = torch.empty(n, dtype=torch.float32, device=dev)
+    _dev(scale, "scale", (torch.float32,), numel=1, device=dev)
+    if ch_scale is not None:
+        _dev(ch_scale, "ch_scale", (torch.float32,), device=dev)
     nn = ch_scale.numel() if ch_scale is not None else 0
+    _gpu(col_amax, s, scale, ch_scale)
     _check(lib.weight_scale_per_tensor(_ptr(col_amax), _ptr(s), K, float(min_scale), _ptr(scale), _ptr(ch_scale),
                                        nn, _stream(stream)))
     return scale, ch_scale
@@ -295,15 +338,20 @@ def weight_scale_per_tensor(col_amax, s=None, min_scale=SSZ_MIN_SCALE, n=0, scal
 def quant_static_i8(x, scale, s=None, fold="div", q=None, row_scale=None, want_row_scale=True, stream=None):
     """Int8 codes of x with one static scale (1-element device tensor); fold "div" (activations) or "mul"
     (weights) when s is given."""
-    _dev(x, "x", _FLOATS)
-    _dev(scale, "scale", (torch.float32,))
+    _dev(x, "x", _FLOATS, ndim=2)
     R, C = x.shape
-    if s is not None:
-        _dev(s, "s", (torch.float32,))
+    dev = x.device
+    _dev(scale, "scale", (torch.float32,), numel=1, device=dev)
+    _opt(s, "s", torch.float32, C, dev)
+    if fold not in FOLD:
+        raise ValueError(f"fold must be one of {tuple(FOLD)}")
     if q is None:
         q = torch.empty((R, C), dtype=torch.int8, device=x.device)
     if row_scale is None and want_row_scale:
         row_scale = torch.empty(R, dtype=torch.float32, device=x.device)
+    _dev(q, "q", (torch.int8,), numel=R * C, device=dev)
+    _opt(row_scale, "row_scale", torch.float32, R, dev)
+    _gpu(x, scale, s, q, row_scale)
     _check(lib.quant_static_i8(_ptr(x), _dtype_code(x), R, C, _ptr(s), FOLD[fold] if s is not None else 0,
                                _ptr(scale), _ptr(q), _ptr(row_scale), _stream(stream)))
     return q, row_scale

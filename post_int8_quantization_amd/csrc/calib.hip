@@ -121,10 +121,10 @@ __global__ void k_smooth(const float* __restrict__ ax, const float* __restrict__
   s[j] = (float)v;
 }
 
-// Static per-tensor scales from column maxima (one block).  For a positive constant r, rounding is
-// monotone, so max_t |fl32(x_tj * r)| = fl32(max_t |x_tj| * r): the maximum of the folded tensor is
-// the maximum over columns of the folded column maxima.
-//   mode 0 (activation, [INT8] 2.1 moving-average range): a = max_j fl32(colmax_j * fl32(1/s_j));
+// Static per-tensor scales from column maxima (one block).  For a positive constant c, rounding is
+// monotone, so max_t |fl32(x_tj / c)| = fl32(max_t |x_tj| / c) (and likewise for x_tj * c): the maximum of
+// the folded tensor is the maximum over columns of the folded column maxima.
+//   mode 0 (activation, [INT8] 2.1 moving-average range): a = max_j fl32(colmax_j / s_j);
 //          state = first ? a : fl32(fl32(m * state) + fl32(fl32(1 - m) * a));
 //          scale = state > 0 ? fl32(state / 127) : 1
 //   mode 1 (weight, per-tensor MinMax): a = max_j fl32(colmax_j * s_j);  scale = max(fl32(a / 127), min_scale)
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kScaleThreads) void k_tensor_scale(const float* __r
   float a = 0.0f;
   for (int64_t j = tid; j < K; j += kScaleThreads) {
     float c = colmax[j];
-    if (s) c = mode == 0 ? c * (1.0f / s[j]) : c * s[j];
+    if (s) c = mode == 0 ? c / s[j] : c * s[j];
     a = fmaxf(a, c);
   }
   a = wave_max(a);

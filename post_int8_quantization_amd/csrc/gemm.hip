@@ -143,8 +143,12 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // Fused epilogue ([INT8] 4.2: dequantize and activate inside the GEMM).  In fp32, each operation
 // rounded: v = fl32(acc) * fl32(ts[t] * cs[n]);  v += bias[n];  relu (v > 0 ? v : +0) or gelu
 // (0.5 v (1 + erf(v / sqrt 2)));  then one of three outputs: fp32; bf16 (round to nearest even);
-// int8 for the next layer: clamp(rne(fl32(fl32(v * fl32(1/next_s[n])) * fl32(1/out_scale))), -127, 127),
-// its static per-tensor quantization with its smoothing fold.
+// int8 for the next layer: clamp(rne(fl32(fl32(v / next_s[n]) / out_scale)), -127, 127), its static
+// per-tensor quantization with its smoothing fold ([INT8] 2.1 Q = round(R/S); [SQ] X diag(s)^-1).  Both
+// quotients are div_rn's corrected products with the IEEE reciprocals: the IEEE quotients for every dividend
+// of at least 2^-102 in magnitude; with next_s[n] in [2^-20, 2^100] and out_scale in [2^-60, 2^100] a smaller
+// v gives |v / next_s| < 2^-81 and the code 0 either way.  A tile whose next_s or out_scale leaves those ranges
+// takes a loop compiled with the IEEE division instead.
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_I8 = 2 };
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 
@@ -215,7 +219,12 @@ struct EpiOut<EPI_I8> {
 // ReLU, bias and GELU (the bias added when present), or the activation read at run time (the decode kernel's small
 // epilogue).  A loop compiled for one activation carries no code of the other: with the activation chosen per
 // element, the GELU code in the loop cost the ReLU epilogue of a 4096x16384 output ~30 us (measured).
-enum { EM_PLAIN = 0, EM_BIAS = 1, EM_RELU = 2, EM_GELU = 3, EM_RUNTIME = 4 };
+// EM_IEEE added to a mode selects the IEEE division for the int8 output's quotients.
+enum { EM_PLAIN = 0, EM_BIAS = 1, EM_RELU = 2, EM_GELU = 3, EM_RUNTIME = 4, EM_IEEE = 8 };
+
+// the int8 output's quotients are in div_rn's proven range (see the fused epilogue above)
+__device__ __forceinline__ bool next_s_ok(float ns) { return ns >= 0x1p-20f && ns <= 0x1p100f; }
+__device__ __forceinline__ bool out_scale_ok(float os) { return os >= 0x1p-60f && os <= 0x1p100f; }
 
 __device__ __forceinline__ int epi_mode(const Epi& epi) {
   if (epi.act == ACT_RELU) return EM_RELU;
@@ -223,10 +232,17 @@ __device__ __forceinline__ int epi_mode(const Epi& epi) {
   return epi.bias ? EM_BIAS : EM_PLAIN;
 }
 
-// v: the dequantized value; bn, nrn: the column's bias and fl32(1/next_s) (0 and 1 when absent).
-template <int OUT, int EM>
-__device__ __forceinline__ typename EpiOut<OUT>::T epi_value(float v, float bn, float nrn, float inv_out,
-                                                             const Epi& epi) {
+// The int8 output's per-column and per-tensor divisors: ns = next_s[n] and its IEEE reciprocal nr (1 and 1 when
+// absent: v / 1 = v), os = out_scale and its reciprocal or.
+struct EpiDiv {
+  float ns, nr, os, orc;
+};
+
+// v: the dequantized value; bn: the column's bias (0 when absent).
+template <int OUT, int EM_>
+__device__ __forceinline__ typename EpiOut<OUT>::T epi_value(float v, float bn, const EpiDiv& dv, const Epi& epi) {
+  constexpr int EM = EM_ & (EM_IEEE - 1);
+  constexpr bool IEEE = (EM_ & EM_IEEE) != 0;
   if constexpr (EM != EM_PLAIN) {
     if (epi.bias) v = v + bn;
     if constexpr (EM == EM_RELU) v = epi_act(v, ACT_RELU);
@@ -235,13 +251,14 @@ __device__ __forceinline__ typename EpiOut<OUT>::T epi_value(float v, float bn, 
   }
   if constexpr (OUT == EPI_F32) return v;
   else if constexpr (OUT == EPI_BF16) return bf16_rne(v);
-  else return (int8_t)(int)code_f(v * nrn, inv_out, 127.0f);  // nrn is exactly 1 without next_s, and v * 1 = v
+  else if constexpr (IEEE) return (int8_t)(int)code_f_ieee(v / dv.ns, dv.os, 127.0f);
+  else return (int8_t)(int)code_f(div_rn(v, dv.ns, dv.nr), dv.os, dv.orc, 127.0f);
 }
 
 template <int OUT, bool NTS = true, int EM = EM_RUNTIME>
-__device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, float nrn,
-                                          float inv_out, const Epi& epi) {
-  const typename EpiOut<OUT>::T o = epi_value<OUT, EM>(v, bn, nrn, inv_out, epi);
+__device__ __forceinline__ void epi_store(void* __restrict__ Y, int64_t idx, float v, float bn, const EpiDiv& dv,
+                                          const Epi& epi) {
+  const typename EpiOut<OUT>::T o = epi_value<OUT, EM>(v, bn, dv, epi);
   typename EpiOut<OUT>::T* y = reinterpret_cast<typename EpiOut<OUT>::T*>(Y) + idx;
   if constexpr (OUT == EPI_F32 && NTS) __builtin_nontemporal_store(o, y);  // written once, not re-read
   else *y = o;
@@ -279,7 +296,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   __shared__ __attribute__((aligned(16))) float s_ts[BM];  // the tile's token scales
   __shared__ float s_cs[BN];                               // and channel scales
   __shared__ float s_b[BN];                                // and bias (epilogue fusion)
-  __shared__ float s_nr[BN];                               // and 1/next_s (int8 output)
+  __shared__ float s_ns[BN];                               // and next_s (int8 output)
+  __shared__ float s_nr[BN];                               // and fl32(1/next_s)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -295,7 +313,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
     const bool in = n0 + t < N;
     s_cs[t] = in ? cs[n0 + t] : 0.0f;
     s_b[t] = (in && epi.bias) ? epi.bias[n0 + t] : 0.0f;
-    if constexpr (OUT == EPI_I8) s_nr[t] = (in && epi.next_s) ? 1.0f / epi.next_s[n0 + t] : 1.0f;
+    if constexpr (OUT == EPI_I8) {
+      const float ns = (in && epi.next_s) ? epi.next_s[n0 + t] : 1.0f;
+      s_ns[t] = ns;
+      s_nr[t] = 1.0f / ns;
+    }
   }
 
   // the tile's A and B panels (at most BM / BN rows of K bytes) and each lane's offsets into them
@@ -417,7 +439,14 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   // so the token scales of a group are one 16-byte LDS read.  The plain dequantization (no bias,
   // no activation, no int32 copy) is its own loop, free of per-element tests.
   const bool full = m0 + BM <= M && n0 + BN <= N;
-  const float inv_out = OUT == EPI_I8 ? 1.0f / epi.out_scale[0] : 0.0f;
+  const float osc = OUT == EPI_I8 ? epi.out_scale[0] : 1.0f;
+  const float orc = 1.0f / osc;
+  bool ieee = false;  // the int8 output's quotients need the IEEE division on this tile
+  if constexpr (OUT == EPI_I8) {
+    bool ok = true;
+    for (int t = tid; t < BN; t += NW * 64) ok = ok && next_s_ok(s_ns[t]);
+    ieee = !(__syncthreads_and(ok) && out_scale_ok(osc));
+  }
   constexpr int NG = NR / 4;
   auto epilogue = [&](auto mode) {
     constexpr int EM = decltype(mode)::value;
@@ -427,7 +456,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
       const int n = n0 + cl;
       const float csn = s_cs[cl];
       const float bn = s_b[cl];
-      const float nrn = OUT == EPI_I8 ? s_nr[cl] : 1.0f;
+      const EpiDiv dv{OUT == EPI_I8 ? s_ns[cl] : 1.0f, OUT == EPI_I8 ? s_nr[cl] : 1.0f, osc, orc};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -440,8 +469,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
             const int m = m0 + rl0 + q;
             const int a = acc[i][j][g * 4 + q];
             if (full || (m < M && n < N)) {
-              epi_store<OUT, true, EM>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, nrn, inv_out, epi);
-              if constexpr (EM != EM_PLAIN)
+              epi_store<OUT, true, EM>(Y, (int64_t)m * N + n, (float)a * (tsv[q] * csn), bn, dv, epi);
+              if constexpr ((EM & (EM_IEEE - 1)) != EM_PLAIN)
                 if (ACC) ACC[(int64_t)m * N + n] = a;
             }
           }
@@ -477,7 +506,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
         const int cl = wn * TN + j * MF + (MF == 32 ? (lane & 31) : lr);
         const float csn = s_cs[cl];
         const float bn = s_b[cl];
-        const float nrn = OUT == EPI_I8 ? s_nr[cl] : 1.0f;
+        const EpiDiv dv{OUT == EPI_I8 ? s_ns[cl] : 1.0f, OUT == EPI_I8 ? s_nr[cl] : 1.0f, osc, orc};
 #pragma unroll
         for (int ii = 0; ii < FPP; ++ii) {
           const int i = p * FPP + ii;
@@ -489,7 +518,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               *reinterpret_cast<OT*>(tl + (wm * BAND + ro + q) * PITCH + cl * E) =
-                  epi_value<OUT, EM>((float)acc[i][j][g * 4 + q] * (tsv[q] * csn), bn, nrn, inv_out, epi);
+                  epi_value<OUT, EM>((float)acc[i][j][g * 4 + q] * (tsv[q] * csn), bn, dv, epi);
           }
         }
       }
@@ -514,7 +543,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_pipe(const int8_t* __re
   // measured: the staging pays for int8 and bf16 outputs everywhere and for fp32 on 256x256 tiles; fp32 on the
   // smaller tiles (one pass of a 128-row tile at 1 KB a row) was 8% slower than the per-element stores
   constexpr bool kStage = OUT != EPI_F32 || (BM == 256 && BN == 256);
-  if (kStage && ACC == nullptr && ((int64_t)N * E) % 16 == 0) {
+  if (OUT == EPI_I8 && ieee) {
+    // rare: the IEEE division (per-element loop with the runtime activation)
+    epilogue(std::integral_constant<int, EM_RUNTIME + EM_IEEE>{});
+  } else if (kStage && ACC == nullptr && ((int64_t)N * E) % 16 == 0) {
     if (em == EM_RELU) staged(std::integral_constant<int, EM_RELU>{});
     else if (em == EM_GELU) staged(std::integral_constant<int, EM_GELU>{});
     else if (em == EM_BIAS) staged(std::integral_constant<int, EM_BIAS>{});
@@ -668,13 +700,17 @@ __global__ __launch_bounds__(KS * 64) void k_gemm_dec(const int8_t* __restrict__
     if (n < N) {
       const float csn = cs[n];
       const float bn = epi.bias ? epi.bias[n] : 0.0f;
-      const float nrn = (OUT == EPI_I8 && epi.next_s) ? 1.0f / epi.next_s[n] : 1.0f;
-      const float inv_out = OUT == EPI_I8 ? 1.0f / epi.out_scale[0] : 0.0f;
+      const float ns = (OUT == EPI_I8 && epi.next_s) ? epi.next_s[n] : 1.0f;
+      const float os = OUT == EPI_I8 ? epi.out_scale[0] : 1.0f;
+      const EpiDiv dv{ns, 1.0f / ns, os, 1.0f / os};
+      const bool ieee = OUT == EPI_I8 && !(next_s_ok(ns) && out_scale_ok(os));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = t * 16 + mg * 4 + r;
         if (m < M) {
-          epi_store<OUT, false>(Y, (int64_t)m * N + n, (float)s[r] * (ts[m] * csn), bn, nrn, inv_out, epi);
+          const float v = (float)s[r] * (ts[m] * csn);
+          if (OUT == EPI_I8 && ieee) epi_store<OUT, false, EM_RUNTIME + EM_IEEE>(Y, (int64_t)m * N + n, v, bn, dv, epi);
+          else epi_store<OUT, false>(Y, (int64_t)m * N + n, v, bn, dv, epi);
           if (ACC) ACC[(int64_t)m * N + n] = s[r];
         }
       }

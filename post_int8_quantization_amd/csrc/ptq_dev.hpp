@@ -154,10 +154,118 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Symmetric code of one value: clamp(rne(x * inv), -qmax, qmax), as fp32.
-__device__ __forceinline__ float code_f(float x, float inv, float qmax) {
-  const float t = x * inv;
-  return fminf(fmaxf(__builtin_rintf(t), -qmax), qmax);
+// The IEEE binary32 quotient fl32(x / s) from r = fl32(1 / s) (itself an IEEE quotient) by one residual
+// correction (Markstein; Muller et al., Handbook of Floating-Point Arithmetic, division chapter):
+//   q0 = fl32(x r),  e = x - q0 s  (exact, by the fused multiply-add),  q = fl32(q0 + e r).
+// q equals fl32(x / s) whenever |x| >= 2^-102 and 2^-126 <= |s| < 2^126 (so that r is a normal number) and the
+// quotient does not overflow: the residual then stays a normal number.  A host sweep over every fp32 mantissa
+// of x against thousands of divisor mantissas confirms it bit for bit.  Below |x| = 2^-102 the result is still
+// within a few units of the smallest subnormal of the quotient; every caller either proves that such x cannot
+// change its outputs or takes the IEEE division (`/`, correctly rounded in this build) instead.
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_fmaf(e, r, q0);
+}
+
+// The domain of div_rn for a divisor: r normal and x / s far from overflow for the callers' operands.
+__device__ __forceinline__ bool div_rn_divisor_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+
+// A value known to be the same in every lane, moved to scalar registers (frees vector registers in
+// register-bound kernels; the value is unchanged).
+__device__ __forceinline__ float uni(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(v)));
+}
+__device__ __forceinline__ double uni(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Symmetric code of one value: clamp(rne(fl32(x / s)), -qmax, qmax), as fp32; r = fl32(1 / s).
+__device__ __forceinline__ float code_f(float x, float s, float r, float qmax) {
+  return fminf(fmaxf(__builtin_rintf(div_rn(x, s, r)), -qmax), qmax);
+}
+
+// The same code through the IEEE division.
+__device__ __forceinline__ float code_f_ieee(float x, float s, float qmax) {
+  return fminf(fmaxf(__builtin_rintf(x / s), -qmax), qmax);
+}
+
+// ---------------------------------------------------------------------------
+// Double-double sums (Dekker, Knuth): a value hi + lo with |lo| <= ulp(hi) / 2, for sums that must come out as
+// the exact real sum rounded once to fp64.  Used only on rare fallback paths.
+struct DD {
+  double hi, lo;
+};
+
+// s + e = a + b exactly (Knuth's TwoSum)
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// x + y; the same bits whichever operand comes first (the rounding error of hi + hi is unique and the two lo
+// parts are added to each other first), so butterfly partners stay identical
+__device__ __forceinline__ DD dd_add(DD x, DD y) {
+  double s, e;
+  two_sum(x.hi, y.hi, s, e);
+  e += x.lo + y.lo;
+  DD r;
+  r.hi = s + e;
+  r.lo = e - (r.hi - s);
+  return r;
+}
+
+__device__ __forceinline__ DD dd_add_d(DD x, double y) { return dd_add(x, DD{y, 0.0}); }
+
+// the exact square of an fp64 value as a double-double (the product error by the fused multiply-add)
+__device__ __forceinline__ DD two_sqr(double d) {
+  DD r;
+  r.hi = d * d;
+  r.lo = __builtin_fma(d, d, -r.hi);
+  return r;
+}
+
+__device__ __forceinline__ DD dd_dpp_xor(DD v, int step) {
+  switch (step) {
+    case 0: return DD{dpp_f64<kDppXor1>(v.hi), dpp_f64<kDppXor1>(v.lo)};
+    case 1: return DD{dpp_f64<kDppXor2>(v.hi), dpp_f64<kDppXor2>(v.lo)};
+    case 2: return DD{dpp_f64<kDppHalfMirror>(v.hi), dpp_f64<kDppHalfMirror>(v.lo)};
+    default: return DD{dpp_f64<kDppMirror>(v.hi), dpp_f64<kDppMirror>(v.lo)};
+  }
+}
+
+__device__ __forceinline__ DD dd_swap16(DD v, bool second) {
+  const uint64_t bh = (uint64_t)__double_as_longlong(v.hi), bl = (uint64_t)__double_as_longlong(v.lo);
+  const auto h0 = __builtin_amdgcn_permlane16_swap((uint32_t)bh, (uint32_t)bh, false, false);
+  const auto h1 = __builtin_amdgcn_permlane16_swap((uint32_t)(bh >> 32), (uint32_t)(bh >> 32), false, false);
+  const auto l0 = __builtin_amdgcn_permlane16_swap((uint32_t)bl, (uint32_t)bl, false, false);
+  const auto l1 = __builtin_amdgcn_permlane16_swap((uint32_t)(bl >> 32), (uint32_t)(bl >> 32), false, false);
+  return second ? DD{join_f64(h0[1], h1[1]), join_f64(l0[1], l1[1])} : DD{join_f64(h0[0], h1[0]), join_f64(l0[0], l1[0])};
+}
+
+__device__ __forceinline__ DD dd_swap32(DD v, bool second) {
+  const uint64_t bh = (uint64_t)__double_as_longlong(v.hi), bl = (uint64_t)__double_as_longlong(v.lo);
+  const auto h0 = __builtin_amdgcn_permlane32_swap((uint32_t)bh, (uint32_t)bh, false, false);
+  const auto h1 = __builtin_amdgcn_permlane32_swap((uint32_t)(bh >> 32), (uint32_t)(bh >> 32), false, false);
+  const auto l0 = __builtin_amdgcn_permlane32_swap((uint32_t)bl, (uint32_t)bl, false, false);
+  const auto l1 = __builtin_amdgcn_permlane32_swap((uint32_t)(bl >> 32), (uint32_t)(bl >> 32), false, false);
+  return second ? DD{join_f64(h0[1], h1[1]), join_f64(l0[1], l1[1])} : DD{join_f64(h0[0], h1[0]), join_f64(l0[0], l1[0])};
+}
+
+// Sum over aligned groups of G lanes (G a power of two up to 64); every lane of a group ends with the same bits.
+template <int G>
+__device__ __forceinline__ DD group_sum_dd(DD v) {
+  if constexpr (G >= 2) v = dd_add(v, dd_dpp_xor(v, 0));
+  if constexpr (G >= 4) v = dd_add(v, dd_dpp_xor(v, 1));
+  if constexpr (G >= 8) v = dd_add(v, dd_dpp_xor(v, 2));
+  if constexpr (G >= 16) v = dd_add(v, dd_dpp_xor(v, 3));
+  if constexpr (G >= 32) v = dd_add(dd_swap16(v, false), dd_swap16(v, true));
+  if constexpr (G >= 64) v = dd_add(dd_swap32(v, false), dd_swap32(v, true));
+  return v;
 }
 
 // Four codes in [-128,127] packed into one dword, element 0 in the low byte.

@@ -10,18 +10,29 @@
 // so the 64 lanes of a wave read 1 KB of consecutive bytes per load
 // instruction (whole cache lines) and write E*64 consecutive code bytes per
 // store ([INT8] 3.1: 16-byte vectorised accesses).  The smoothing fold
-// x_hat = fl32(x * fl32(1/s_j)) ([SQ] X diag(s)^-1) uses per-column
-// reciprocals that each thread computes once (IEEE division) for its own
-// columns and keeps in registers across the rows it visits; the grid size
-// trades that reuse against rows in flight.
+// x_hat = fl32(x / s_j) ([SQ] X diag(s)^-1) is div_rn's corrected product
+// with the per-column reciprocals fl32(1 / s_j), which each thread computes
+// once (IEEE division) for its own columns and keeps in registers, beside
+// s_j, across the rows it visits; the grid size trades that reuse against
+// rows in flight.
 //
 // All row accesses are range-checked buffer loads and stores on a per-row
 // descriptor (zero bytes for a row past T), so no lane or row takes a branch
 // around a memory access and the loads of the rows in flight stay in flight.
 //
 // Per row: a = max|x_hat| (wave butterfly + LDS across waves),
-// delta = a > 0 ? fl32(a/127) : 1, inv = fl32(1/delta),
-// code = clamp(rne(fl32(x_hat * inv)), -127, 127)   ([INT8] 2.1).
+// delta = a > 0 ? fl32(a/127) : 1, code = clamp(rne(fl32(x_hat / delta)),
+// -127, 127) ([INT8] 2.1), the quotient again by div_rn.
+//
+// div_rn gives the IEEE quotient of every operand at least 2^-102 in
+// magnitude.  With every s_j in [2^-20, 2^100] (checked once per block) an x
+// under 2^-102 has |x_hat| < 2^-81, so a row whose computed maximum a lies in
+// [2^-60, 2^100] has the exact a and delta, and its small elements have the
+// code 0 either way: such rows take the fast path.  Any other row (a zero or
+// tiny row, a huge one), and every row when some s_j is outside that range,
+// is folded and quantized with the IEEE division instead.  The static mode
+// takes the fast path when its scale lies in [2^-60, 2^100] (and the s_j
+// check holds for the division fold).
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
 
@@ -79,9 +90,13 @@ __device__ __forceinline__ void unpack16(const uint4 (&raw)[Piece<DT>::P], float
 }
 
 // One row: fold, absmax (wave butterfly + LDS across waves), codes, store.  STATIC: the scale is
-// given (static_delta, its reciprocal static_inv) and no maximum is taken.
+// given (static_delta, its reciprocal static_inv) and no maximum is taken.  HAS_S folds by the per-column
+// factors sf: x * sf (fold_mul) or x / sf through their reciprocals rf.  cols_ok: every s_j of the block is in
+// div_rn's fold range (see the file header); the row takes the IEEE division when it is not, or when its
+// maximum (or the static scale) is out of range.
 template <int DT, bool HAS_S, int TPR, int CPT, bool STATIC>
-__device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P], const float (&r)[CPT][16], int64_t t,
+__device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P], const float (&sf)[CPT][16],
+                                          const float (&rf)[CPT][16], bool fold_mul, bool cols_ok, int64_t t,
                                           int64_t T, int64_t K, int tid, int8_t* __restrict__ xq,
                                           float* __restrict__ tok_scale, float (*red)[TPR / kWave], int parity,
                                           float static_delta, float static_inv) {
@@ -94,7 +109,7 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
     unpack16<DT>(raw[m], v[m]);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if constexpr (HAS_S) v[m][e] = v[m][e] * r[m][e];
+      if constexpr (HAS_S) v[m][e] = fold_mul ? v[m][e] * sf[m][e] : div_rn(v[m][e], sf[m][e], rf[m][e]);
       if constexpr (!STATIC) amax = fmaxf(amax, fabsf(v[m][e]));
     }
   }
@@ -111,6 +126,35 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
 #pragma unroll
       for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red[parity][w]);
     }
+  }
+  const bool fast = cols_ok && (STATIC ? (delta >= 0x1p-60f && delta <= 0x1p100f)
+                                       : (amax >= 0x1p-60f && amax <= 0x1p100f));
+  if (!fast) {
+    // the IEEE division throughout (uniform over the row)
+    amax = 0.0f;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      unpack16<DT>(raw[m], v[m]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if constexpr (HAS_S) v[m][e] = fold_mul ? v[m][e] * sf[m][e] : v[m][e] / sf[m][e];
+        if constexpr (!STATIC) amax = fmaxf(amax, fabsf(v[m][e]));
+      }
+    }
+    if constexpr (!STATIC) {
+      amax = wave_max(amax);
+      if constexpr (NW > 1) {
+        __syncthreads();
+        if ((tid & (kWave - 1)) == 0) red[parity ^ 1][tid / kWave] = amax;
+        __syncthreads();
+        amax = red[parity ^ 1][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red[parity ^ 1][w]);
+        __syncthreads();
+      }
+    }
+  }
+  if constexpr (!STATIC) {
     delta = amax > 0.0f ? amax / 127.0f : 1.0f;
     inv = 1.0f / delta;
   }
@@ -119,8 +163,13 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
     float q[16];
+    if (fast) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) q[e] = code_f(v[m][e], inv, 127.0f);
+      for (int e = 0; e < 16; ++e) q[e] = code_f(v[m][e], delta, inv, 127.0f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) q[e] = code_f_ieee(v[m][e], delta, 127.0f);
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint32_t c = (uint32_t)piece_col<DT, TPR>(m, p, tid);
@@ -146,7 +195,7 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
 // block walks whole rounds of D rows; the rows of a round past T are no-ops
 // (zero-length descriptors).
 // STATIC: one given scale (scale[0]) for every row, as a per-tensor static quantization; fold_mul
-// folds by s_j (the weight side) instead of by fl32(1/s_j) (the activation side).
+// folds by s_j (the weight side, fl32(x * s_j)) instead of fl32(x / s_j) (the activation side).
 template <int DT, bool HAS_S, int TPR, int CPT, int D, bool STATIC>
 __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, int64_t T, int64_t K,
                                                    const float* __restrict__ s, int8_t* __restrict__ xq,
@@ -174,7 +223,8 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 #pragma unroll
   for (int d = 0; d < D; ++d) load_raw<DT, TPR, CPT>(x, blockIdx.x + d * G, T, K, tid, ring[d]);
 
-  float r[CPT][16];
+  float sf[CPT][16], rf[CPT][16];
+  bool cols_ok = true;
   if constexpr (HAS_S) {
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
@@ -187,17 +237,20 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
           const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float sj = __uint_as_float(u[i]);
-            r[m][p * E + 4 * h + i] = in ? (fold_mul ? sj : 1.0f / sj) : 1.0f;
+            const float sj = in ? __uint_as_float(u[i]) : 1.0f;
+            sf[m][p * E + 4 * h + i] = sj;
+            rf[m][p * E + 4 * h + i] = fold_mul ? 1.0f : 1.0f / sj;
+            cols_ok = cols_ok && (fold_mul || (sj >= 0x1p-20f && sj <= 0x1p100f));
           }
         }
       }
     }
+    cols_ok = __syncthreads_and(cols_ok) != 0;
   } else {
 #pragma unroll
     for (int m = 0; m < CPT; ++m)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) r[m][e] = 1.0f;
+      for (int e = 0; e < 16; ++e) sf[m][e] = rf[m][e] = 1.0f;
   }
   float static_delta = 1.0f, static_inv = 1.0f;
   if constexpr (STATIC) {
@@ -209,8 +262,8 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int64_t t = base + d * G;
-      quant_row<DT, HAS_S, TPR, CPT, STATIC>(ring[d], r, t, T, K, tid, xq, tok_scale, red, parity, static_delta,
-                                             static_inv);
+      quant_row<DT, HAS_S, TPR, CPT, STATIC>(ring[d], sf, rf, fold_mul != 0, cols_ok, t, T, K, tid, xq, tok_scale,
+                                             red, parity, static_delta, static_inv);
       parity ^= 1;
       load_raw<DT, TPR, CPT>(x, t + D * G, T, K, tid, ring[d]);
     }

@@ -1,26 +1,56 @@
 // ssz.hip -- MinMax + SSZ per-output-channel weight quantization (gfx950):
-// symmetric int8/int4 (k_ssz; k_ssz_rows for rows of at most 512 elements,
-// several rows per wave) and asymmetric int8 (k_ssz_asym, further down).
+// symmetric int8/int4 and asymmetric int8 (k_ssz), short symmetric rows of at
+// most 512 elements, several rows per wave (k_ssz_rows), and the exact search
+// for the rows those two defer (k_ssz_exact).
 //
-// [SSZ] flow: MinMax initial scale, then least-squares refits of the scale for
-// the current codes, a refit kept only when it lowers the quantization error,
+// [SSZ] flow: MinMax initial parameters, then least-squares refits for the
+// current codes, a refit kept only when it lowers the quantization error,
 // until the relative or absolute change falls under the threshold or the
 // iteration limit is reached; symmetric quantization fixes the offset at 0.
 // [SQ] the weight side of the smoothing fold, w_hat = fl32(w * s_j).
+// [INT8] 2.1 the codes: clamp(rne(fl32(w_hat / S)) + Z).
 //
 // One block of TPR threads owns one row (output channel).  The row is read
-// from HBM once and stays in registers (CPT chunks of 16 elements per
-// thread, in fp32, widened to fp64 where a pass needs it) for every pass;
-// all passes are ALU work.  One pass over the row for a scale S computes, per
-// element, the code q = clamp(rne(w_hat * inv S)) and accumulates A =
-// sum(w_hat q) in fp64 and B = sum(q^2) exactly (fp32 per lane, integer
-// across lanes) -- the two sums the least-squares step needs.  The error of
-// the pass follows from the same sums and the row's sum of squares W2
-// (computed once): K * mse(S) = W2 - 2 S A + S^2 B, the expansion of
-// sum (w_hat - S q)^2, evaluated in fp64 and clamped at 0.  The sums are
-// reduced with xor butterflies (identical in every lane) and, for multi-wave
-// rows, through LDS in wave order, so every decision is uniform across the
-// row.
+// from HBM once and stays in registers (CPT chunks of 16 elements per thread)
+// for every pass; all passes are ALU work.  A pass for (S, Z) computes per
+// element the code q, its offset-relative value r = q - Z (r = q when
+// symmetric) and accumulates
+//   P = sum w_hat r (fp64),  R2 = sum r^2,  R1 = sum r (exact integers),
+// the sums the least-squares step needs.  The quotient w_hat / S is div_rn's
+// corrected product with the IEEE reciprocal: the IEEE quotient whenever
+// 2^-100 <= S <= 2^100 (an element under 2^-102 then has |w_hat / S| < 1/4 and
+// the code 0 either way).
+//
+// Every decision is the one the exact values give:
+//  * P is exact.  A non-zero r needs |w_hat / S| > 1/2, so every non-zero term
+//    w_hat r is a multiple of 2^(E-25) (E the binary exponent of S), and it is
+//    never negative (r has the sign of w_hat).  While the sum stays under
+//    2^(E+28) every partial sum is an integer multiple of 2^(E-25) below
+//    2^53 of them: no fp64 addition rounds, in any order.  A computed sum under
+//    2^(E+27) proves that (a sum that had rounded would be at least
+//    2^(E+28)(1 - 2^-40)).
+//  * The error of a pass comes from the expansion
+//      K mse = W2 - 2 S P + S^2 R2,  W2 = sum w_hat^2 (fp64, once per row),
+//    whose rounding is bounded by (h + 8) u (W2 + 2 S P + S^2 R2), u = 2^-53,
+//    h the longest chain of fp64 additions in the reduction of W2 (serial per
+//    lane, then the butterfly, then the waves).  Each error is therefore
+//    known as an interval holding the exact error (its exact sum rounded to
+//    fp64, divided by K), and a keep or convergence decision that the
+//    intervals settle is the exact decision.
+//  * A refit that returns the kept parameters exactly is the same candidate:
+//    its error equals the best one, so the step converges (threshold > 0)
+//    without a pass.
+// A row for which any of this fails -- a scale outside div_rn's range, a P
+// the certificate does not cover, a decision the intervals leave open (none
+// in 330,000 passes over the workloads' weights) -- is deferred: the kernel
+// writes a NaN scale and nothing else for it, and k_ssz_exact, launched next
+// on the same stream, searches those rows again with the IEEE division and
+// every sum in double-double, rounded once.  Its roundings of the exact sums
+// give the correctly rounded fp64 value unless an exact sum lies within about
+// 2^-90 relative of an fp64 rounding boundary.
+// Sums are reduced with butterflies in which both lanes of a pair combine the
+// same two operands, and across waves through LDS in wave order, so every
+// lane of a row holds identical bits and every decision is uniform.
 #include "ptq_dev.hpp"
 #include "ptq_launch.hpp"
 
@@ -28,57 +58,108 @@ namespace ptq {
 
 namespace {
 
-struct PassSums {
-  double a;  // sum w_hat q
-  int b;     // sum q^2
+constexpr double kU = 0x1p-53;  // unit roundoff of binary64
+
+// An interval [lo, hi] holding an exact error value.
+struct Ival {
+  double lo, hi;
 };
 
-template <int TPR, int CPT, bool WIDE>
-__device__ __forceinline__ PassSums row_pass(const float (&wh)[CPT][16], const double (&wd)[WIDE ? CPT : 1][16],
-                                             float S, float qmax, double* red_d, int* red_i, int tid) {
-  const float inv = 1.0f / S;
-  double a = 0.0;
-  float bq = 0.0f;  // at most 16*CPT terms of <= 127^2 each: exact in fp32
-#pragma unroll
-  for (int m = 0; m < CPT; ++m) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float q = code_f(wh[m][k], inv, qmax);
-      const double w = WIDE ? wd[WIDE ? m : 0][k] : (double)wh[m][k];
-      a = __builtin_fma(w, (double)q, a);
-      bq = __builtin_fmaf(q, q, bq);
-    }
+enum : int { kNo = 0, kYes = 1, kUnk = 2 };
+
+__device__ __forceinline__ int tri_or(int a, int b) {
+  return (a == kYes || b == kYes) ? kYes : ((a == kNo && b == kNo) ? kNo : kUnk);
+}
+
+struct Decision {
+  int keep, conv;
+};
+
+// The greedy rule (keep the candidate iff cur < best) and the convergence test
+//   best == 0  or  |d| < thr  or  fl64(d / best) < thr,   d = fl64(best - cur),
+// for every best in b and cur in c.  Rounding is monotone, so fl64(best - cur) lies in
+// [fl64(b.lo - c.hi), fl64(b.hi - c.lo)] and the quotient between the quotients of the end points.  The
+// relative test matters only when best > 0 (best == 0 converges anyway).  On points the result is the plain
+// rule and test.
+__device__ __forceinline__ Decision decide(Ival b, Ival c, double thr) {
+  Decision r;
+  r.keep = c.hi < b.lo ? kYes : (c.lo >= b.hi ? kNo : kUnk);
+  const double dlo = b.lo - c.hi, dhi = b.hi - c.lo;
+  const int z = b.hi == 0.0 ? kYes : (b.lo > 0.0 ? kNo : kUnk);
+  const int ab = (dlo > -thr && dhi < thr) ? kYes : ((dlo >= thr || dhi <= -thr) ? kNo : kUnk);
+  int rel;
+  if (thr > 0.0 && dhi <= 0.0) {
+    rel = kYes;  // quotient <= 0 < thr
+  } else if (dlo >= 2.0 * (thr * b.hi)) {
+    rel = kNo;  // d > thr * best exactly (one rounding cannot halve the product), so the quotient rounds to >= thr
+  } else {
+    const double inf = __builtin_huge_val();
+    const double fmax = dhi >= 0.0 ? (b.lo > 0.0 ? dhi / b.lo : inf) : dhi / b.hi;
+    const double fmin = dlo >= 0.0 ? dlo / b.hi : (b.lo > 0.0 ? dlo / b.lo : -inf);
+    rel = fmax < thr ? kYes : (fmin >= thr ? kNo : kUnk);
   }
-  PassSums r;
-  r.a = wave_sum(a);
-  r.b = wave_sum((int)bq);
-  constexpr int NW = TPR / kWave;
-  if constexpr (NW > 1) {
-    // red_d / red_i point at this pass's half of a two-pass slot ring: the previous readers of
-    // these slots (two passes ago) finished before the barrier of the pass in between
-    const int w = tid / kWave;
-    if ((tid & (kWave - 1)) == 0) {
-      red_d[w] = r.a;
-      red_i[w] = r.b;
-    }
-    __syncthreads();
-    r.a = red_d[0];
-    r.b = red_i[0];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) {
-      r.a += red_d[i];
-      r.b += red_i[i];
-    }
-  }
+  r.conv = tri_or(z, tri_or(ab, rel));
   return r;
+}
+
+// e / K in fp64.  For a power-of-two K the quotient is an exact scaling, so it is taken with
+// ldexp (one instruction) instead of the division sequence; the result is the same double.
+struct DivK {
+  double kd;
+  int lg;  // log2 K when K is a power of two, else -1
+  __device__ __forceinline__ double operator()(double e) const {
+    if (lg >= 0) return __builtin_ldexp(e, -lg);
+    return e / kd;
+  }
+};
+
+__device__ __forceinline__ DivK make_divk(int64_t K) {
+  DivK d;
+  d.kd = (double)K;
+  d.lg = (K & (K - 1)) == 0 ? 63 - __builtin_clzll((unsigned long long)K) : -1;
+  return d;
+}
+
+// The interval of the exact mean error for exact pass sums, from the expansion and its rounding bound
+// hu * (W2 + 2 S P + S^2 R2), hu = (h + 8) u.
+__device__ __forceinline__ Ival err_ival(double w2, float S, double P, double R2, double hu, const DivK& per_elem) {
+  const double Sd = (double)S;
+  const double s2 = Sd * Sd * R2;
+  const double e = (w2 - 2.0 * Sd * P) + s2;
+  const double bnd = hu * ((w2 + 2.0 * Sd * P) + s2);
+  const double lo = e - bnd, hi = e + bnd;
+  return Ival{per_elem(lo > 0.0 ? lo : 0.0), per_elem(hi > 0.0 ? hi : 0.0)};
+}
+
+// 2^(E + 27), E the binary exponent of a normal S: a computed P below it is exact (see the file header)
+__device__ __forceinline__ double p_cert(float S) {
+  const int e = (int)((__float_as_uint(S) >> 23) & 0xFFu) - 127;
+  return __builtin_ldexp(1.0, e + 27);
+}
+
+// Offset-relative code r = q - Z of one element, q = clamp(rne(fl32(w / S)) + Z); symmetric: Z = 0 and the
+// range [-qmax, qmax].  rS = fl32(1 / S), 2^-100 <= S <= 2^100.
+template <bool ASYM>
+__device__ __forceinline__ float rel_code(float w, float S, float rS, float zf, float qmax) {
+  const float t = __builtin_rintf(div_rn(w, S, rS));
+  if constexpr (ASYM) return fminf(fmaxf(t + zf, -128.0f), 127.0f) - zf;
+  return fminf(fmaxf(t, -qmax), qmax);
+}
+
+// the same code through the IEEE division (any S)
+template <bool ASYM>
+__device__ __forceinline__ float rel_code_ieee(float w, float S, float zf, float qmax) {
+  const float t = __builtin_rintf(w / S);
+  if constexpr (ASYM) return fminf(fmaxf(t + zf, -128.0f), 127.0f) - zf;
+  return fminf(fmaxf(t, -qmax), qmax);
 }
 
 // Row n of w, folded (w_hat = fl32(w * s_j)), into registers: CPT chunks of 16 elements per thread,
 // chunk c8 of thread tid at elements (tid + TPR*c8)*16 ..; chunks past the row are zeros (they add
-// nothing to any sum and never change a max of magnitudes).  WIDE also keeps an fp64 copy.
-template <int DT, bool HAS_S, int TPR, int CPT, bool WIDE>
+// nothing to any sum, have the code r = 0, and never change a max of magnitudes).
+template <int DT, bool HAS_S, int TPR, int CPT>
 __device__ __forceinline__ void load_row(const void* __restrict__ w, int64_t n, int64_t K, const float* __restrict__ s,
-                                         int tid, float (&wh)[CPT][16], double (&wd)[WIDE ? CPT : 1][16]) {
+                                         int tid, float (&wh)[CPT][16]) {
   const int64_t nchunk = K / 16;
 #pragma unroll
   for (int c8 = 0; c8 < CPT; ++c8) {
@@ -107,181 +188,293 @@ __device__ __forceinline__ void load_row(const void* __restrict__ w, int64_t n, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
     }
-    if constexpr (WIDE) {
+  }
+}
+
+// One pass over a thread's elements for (S, Z): P, R2, R1 of its elements.
+template <int CPT, bool ASYM>
+__device__ __forceinline__ void lane_pass(const float (&wh)[CPT][16], float S, float zf, float qmax, double& p,
+                                          float& r2, float& r1) {
+  const float rS = 1.0f / S;
+  double a = 0.0;
+  float b = 0.0f;  // at most 16*CPT terms of <= 255^2 each: exact in fp32
+  float c = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) wd[c8][e] = (double)wh[c8][e];
+  for (int m = 0; m < CPT; ++m) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float r = rel_code<ASYM>(wh[m][k], S, rS, zf, qmax);
+      a = __builtin_fma((double)wh[m][k], (double)r, a);
+      b = __builtin_fmaf(r, r, b);
+      if constexpr (ASYM) c += r;
     }
   }
+  p = a;
+  r2 = b;
+  r1 = c;
 }
 
-// e / K in fp64.  For a power-of-two K the quotient is an exact scaling, so it is taken with
-// ldexp (one instruction) instead of the division sequence; the result is the same double.
-struct DivK {
-  double kd;
-  int lg;  // log2 K when K is a power of two, else -1
-  __device__ __forceinline__ double operator()(double e) const {
-    if (lg >= 0) return __builtin_ldexp(e, -lg);
-    return e / kd;
+// Writes a row's codes (int8, or int4 nibbles) for chunk c of the row.
+template <int BITS>
+__device__ __forceinline__ void store_codes(void* wq, int64_t n, int64_t K, int64_t c, const float (&q)[16]) {
+  if constexpr (BITS == 8) {
+    uint4 o;
+    o.x = pack4_i8(q[0], q[1], q[2], q[3]);
+    o.y = pack4_i8(q[4], q[5], q[6], q[7]);
+    o.z = pack4_i8(q[8], q[9], q[10], q[11]);
+    o.w = pack4_i8(q[12], q[13], q[14], q[15]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(wq) + n * K + c * 16) = o;
+  } else {
+    uint2 o;
+    o.x = pack8_i4(q);
+    o.y = pack8_i4(q + 8);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(wq) + n * (K / 2) + c * 8) = o;
   }
+}
+
+// The state of a row's search, identical in every lane of the row.
+struct RowState {
+  float S;
+  int Z;
+  double P, R2, R1;  // the kept parameters' pass sums (exact)
+  Ival best;
 };
 
-__device__ __forceinline__ DivK make_divk(int64_t K) {
-  DivK d;
-  d.kd = (double)K;
-  d.lg = (K & (K - 1)) == 0 ? 63 - __builtin_clzll((unsigned long long)K) : -1;
-  return d;
+// One step of the search from the kept state st: the least-squares refit.  Returns false when there is nothing
+// to fit (the row stops); else the candidate (Sc, Zc).
+template <bool ASYM>
+__device__ __forceinline__ bool refit(const RowState& st, double Kd, double w1, const DivK& per_elem,
+                                      float min_scale, float& Sc, int& Zc) {
+  if constexpr (ASYM) {
+    const double det = Kd * st.R2 - st.R1 * st.R1;  // exact: integers below 2^53
+    if (det <= 0.0) return false;
+    const double a = (Kd * st.P - w1 * st.R1) / det;
+    const double b = per_elem(w1 - a * st.R1);
+    Sc = (float)a;
+    Sc = Sc < min_scale ? min_scale : Sc;
+    const double zr = (double)st.Z - __builtin_rint(b / a);
+    Zc = zr < -128.0 ? -128 : (zr > 127.0 ? 127 : (int)zr);
+  } else {
+    if (st.R2 == 0.0) return false;
+    Sc = (float)(st.P / st.R2);
+    Sc = Sc < min_scale ? min_scale : Sc;
+    Zc = 0;
+  }
+  return true;
 }
 
-// The relative convergence test fl64(d / best) < thr, for best > 0 and thr >= 0, with the division
-// taken only where its rounding can decide.  d <= 0 gives a quotient <= 0, below any thr > 0.
-// d >= 2 fl64(thr * best) means d > thr * best exactly (one rounding, or an underflow below the
-// smallest positive d, cannot halve the product), so the quotient exceeds thr and rounds to >= thr.
-// On these weights the division then runs only for improvements within a factor of two of the
-// threshold; it was 15 of the ~95 per-pass instructions of a row's wave.
-__device__ __forceinline__ bool rel_below(double d, double best, double thr) {
-  if (thr > 0.0 && d <= 0.0) return true;
-  if (d >= 2.0 * (thr * best)) return false;
-  return d / best < thr;
+// MinMax init of the parameters from the row's max magnitude (symmetric, `hi`) or min lo and max hi
+template <bool ASYM>
+__device__ __forceinline__ void minmax_init(float lo, float hi, float qmax, float min_scale, float& S, int& Z) {
+  if constexpr (ASYM) {
+    S = (hi - lo) / 255.0f;
+    S = S < min_scale ? min_scale : S;
+    const float z0 = -128.0f - __builtin_rintf(lo / S);
+    Z = (int)fminf(fmaxf(z0, -128.0f), 127.0f);
+  } else {
+    S = hi / qmax;
+    S = S < min_scale ? min_scale : S;
+    Z = 0;
+  }
 }
 
-// K * mse(S) from the pass sums: W2 - 2 S A + S^2 B, never below 0
-__device__ __forceinline__ double sq_err(double w2, float S, const PassSums& p) {
-  const double Sd = (double)S;
-  const double e = (w2 - 2.0 * Sd * p.a) + Sd * Sd * (double)p.b;
-  return e > 0.0 ? e : 0.0;
-}
-
-// WIDE_MODE 1 keeps an explicit fp64 copy of the row in registers.  The default (0) leaves the
-// widening to the compiler, which hoists it out of the pass loop: the same 6 VALU operations per
-// element and pass in about 2/3 of the registers (2 waves per SIMD instead of 1 on 4096- and
-// 16384-wide rows; measured 25-30% faster, int8 and int4).  Forcing the conversion into every pass
-// (3 waves per SIMD, 7 operations) measured 5% slower than the default.
-template <int DT, bool HAS_S, int BITS, int TPR, int CPT, int WIDE_MODE = 0>
+// MinMax + SSZ, symmetric (ASYM = false; qmax 127 or 7) or asymmetric int8; one row per block of TPR threads.
+// Rows it cannot certify get a NaN scale (and no other output) for k_ssz_exact.
+template <int DT, bool HAS_S, int BITS, bool ASYM, int TPR, int CPT>
 __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t N, int64_t K,
                                              const float* __restrict__ s, int max_iter, double thr, float min_scale,
-                                             float* __restrict__ scale, void* __restrict__ wq,
-                                             int32_t* __restrict__ iters, double* __restrict__ mse) {
+                                             float* __restrict__ scale, int32_t* __restrict__ zero_point,
+                                             void* __restrict__ wq, int32_t* __restrict__ iters,
+                                             double* __restrict__ mse) {
   constexpr int NW = TPR / kWave;
-  constexpr bool WIDE = WIDE_MODE == 1;
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
-  __shared__ double red_d[NW];
-  __shared__ float red_f[NW];
-  __shared__ double ring_d[2][NW];  // pass sums, alternating halves
-  __shared__ int ring_i[2][NW];
+  __shared__ double ring[2][3 * NW];  // pass sums, alternating halves
+  __shared__ double xd[2 * NW];
+  __shared__ float xf[2 * NW];
   int par = 0;
   const int tid = threadIdx.x;
   const int64_t nchunk = K / 16;
+  const double Kd = (double)K;
   const DivK per_elem = make_divk(K);
+  // rounding bound of the expansion: the longest addition chain of W2 is CPT*16 per lane, 6 butterfly steps,
+  // NW - 1 wave partials; (h + 8) u, rounded up
+  const double hu = (double)(CPT * 16 + 6 + NW + 8) * kU * (1.0 + 0x1p-20);
 
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
     float wh[CPT][16];
-    double wd[WIDE ? CPT : 1][16];
-    load_row<DT, HAS_S, TPR, CPT, WIDE>(w, n, K, s, tid, wh, wd);
-    float m = 0.0f;
+    load_row<DT, HAS_S, TPR, CPT>(w, n, K, s, tid, wh);
+
+    // row statistics: W2 = sum w_hat^2 (fp64); the max magnitude (symmetric) or min and max; W1 = sum w_hat
+    float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
     double w2 = 0.0;
+    DD w1dd{0.0, 0.0};
 #pragma unroll
     for (int c8 = 0; c8 < CPT; ++c8) {
+      const bool in = tid + (int64_t)TPR * c8 < nchunk;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        m = fmaxf(m, fabsf(wh[c8][e]));
-        const double x = (double)wh[c8][e];
+        const float v = wh[c8][e];
+        if constexpr (ASYM) {
+          lo = fminf(lo, in ? v : lo);
+          hi = fmaxf(hi, in ? v : hi);
+          w1dd = dd_add_d(w1dd, (double)v);
+        } else {
+          hi = fmaxf(hi, fabsf(v));
+        }
+        const double x = (double)v;
         w2 = __builtin_fma(x, x, w2);
       }
     }
-    m = wave_max(m);
+    if constexpr (ASYM) lo = -wave_max(-lo);
+    hi = wave_max(hi);
     w2 = wave_sum(w2);
+    if constexpr (ASYM) w1dd = group_sum_dd<64>(w1dd);
     if constexpr (NW > 1) {
       __syncthreads();
       if ((tid & (kWave - 1)) == 0) {
-        red_f[tid / kWave] = m;
-        red_d[tid / kWave] = w2;
+        xf[tid / kWave] = lo;
+        xf[NW + tid / kWave] = hi;
+        xd[tid / kWave] = w2;
       }
       __syncthreads();
-      m = red_f[0];
-      w2 = red_d[0];
+      lo = xf[0];
+      hi = xf[NW];
+      w2 = xd[0];
 #pragma unroll
       for (int i = 1; i < NW; ++i) {
-        m = fmaxf(m, red_f[i]);
-        w2 += red_d[i];
+        lo = fminf(lo, xf[i]);
+        hi = fmaxf(hi, xf[NW + i]);
+        w2 += xd[i];
+      }
+      if constexpr (ASYM) {
+        __syncthreads();
+        if ((tid & (kWave - 1)) == 0) {
+          xd[tid / kWave] = w1dd.hi;
+          xd[NW + tid / kWave] = w1dd.lo;
+        }
+        __syncthreads();
+        DD t{xd[0], xd[NW]};
+#pragma unroll
+        for (int i = 1; i < NW; ++i) t = dd_add(t, DD{xd[i], xd[NW + i]});
+        w1dd = t;
       }
     }
+    const double w1 = uni(w1dd.hi + w1dd.lo);
+    w2 = uni(w2);
+    lo = uni(lo);
+    hi = uni(hi);
 
-    // MinMax init
-    float S = m / QMAX;
-    S = S < min_scale ? min_scale : S;
-    PassSums cur = row_pass<TPR, CPT, WIDE>(wh, wd, S, QMAX, ring_d[par], ring_i[par], tid);
-    par ^= 1;
-    double best = per_elem(sq_err(w2, S, cur));
-    double A = cur.a;
-    int B = cur.b;
+    // pass sums for (S, Z) over the row; false when the scale is outside div_rn's range or P is not certified
+    auto pass = [&](float Sx, int Zx, double& P, double& R2, double& R1) -> bool {
+      if (!div_rn_divisor_ok(Sx)) return false;
+      float r2, r1;
+      lane_pass<CPT, ASYM>(wh, Sx, (float)Zx, QMAX, P, r2, r1);
+      P = wave_sum(P);
+      int i2 = wave_sum((int)r2), i1 = ASYM ? wave_sum((int)r1) : 0;
+      R2 = (double)i2;
+      R1 = (double)i1;
+      if constexpr (NW > 1) {
+        // a two-pass slot ring: the readers of a slot two passes ago finished before the barrier in between
+        double* rs = ring[par];
+        par ^= 1;
+        const int wv = tid / kWave;
+        if ((tid & (kWave - 1)) == 0) {
+          rs[wv] = P;
+          rs[NW + wv] = R2;
+          if constexpr (ASYM) rs[2 * NW + wv] = R1;
+        }
+        __syncthreads();
+        P = rs[0];
+        R2 = rs[NW];
+        if constexpr (ASYM) R1 = rs[2 * NW];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) {
+          P += rs[i];
+          R2 += rs[NW + i];
+          if constexpr (ASYM) R1 += rs[2 * NW + i];
+        }
+      }
+      P = uni(P);
+      R2 = uni(R2);
+      if constexpr (ASYM) R1 = uni(R1);
+      return P < p_cert(Sx);
+    };
+
+    RowState st;
+    minmax_init<ASYM>(lo, hi, QMAX, min_scale, st.S, st.Z);
+    bool ok = pass(st.S, st.Z, st.P, st.R2, st.R1);
+    st.best = err_ival(w2, st.S, st.P, st.R2, hu, per_elem);
+    st.best = Ival{uni(st.best.lo), uni(st.best.hi)};
 
     // least-squares refits, greedy, per-row convergence
     int it = 0;
-    for (int i = 1; i <= max_iter; ++i) {
+    for (int i = 1; ok && i <= max_iter; ++i) {
       it = i;
-      if (B == 0) break;
-      float Sc = (float)(A / (double)B);
-      Sc = Sc < min_scale ? min_scale : Sc;
-      const PassSums p = row_pass<TPR, CPT, WIDE>(wh, wd, Sc, QMAX, ring_d[par], ring_i[par], tid);
-      par ^= 1;
-      const double c = per_elem(sq_err(w2, Sc, p));
-      const double d = best - c;
-      const bool conv = (best == 0.0) || (fabs(d) < thr) || rel_below(d, best, thr);
-      if (c < best) {
-        S = Sc;
-        best = c;
-        A = p.a;
-        B = p.b;
+      float Sc;
+      int Zc;
+      if (!refit<ASYM>(st, Kd, w1, per_elem, min_scale, Sc, Zc)) break;
+      if (Sc == st.S && Zc == st.Z) {
+        // the kept parameters again: the same codes and error, d = 0
+        if (thr > 0.0 || st.best.hi == 0.0) break;
+        if (st.best.lo > 0.0) it = max_iter;  // thr == 0, best > 0: the same candidate at every remaining step
+        else ok = false;
+        break;
       }
-      if (conv) break;
+      RowState c;
+      c.S = Sc;
+      c.Z = Zc;
+      if (!pass(Sc, Zc, c.P, c.R2, c.R1)) {
+        ok = false;
+        break;
+      }
+      c.best = err_ival(w2, Sc, c.P, c.R2, hu, per_elem);
+      c.best = Ival{uni(c.best.lo), uni(c.best.hi)};
+      const Decision dc = decide(st.best, c.best, thr);
+      if (dc.keep == kUnk || dc.conv == kUnk) {
+        ok = false;
+        break;
+      }
+      if (dc.keep == kYes) st = c;
+      if (dc.conv == kYes) break;
     }
 
-    // codes of the kept scale, and its error summed directly (the reported mse; the expansion
-    // above loses relative accuracy when the error is tiny next to W2)
+    if (!ok) {
+      if (tid == 0) scale[n] = __builtin_nanf("");
+      continue;
+    }
+    // codes of the kept parameters, and their error summed directly (the reported mse)
     double e_dir = 0.0;
     if (wq || mse) {
-      const float inv = 1.0f / S;
-      const double Sd = (double)S;
+      const float rS = 1.0f / st.S, zf = (float)st.Z;
+      const double Sd = (double)st.S;
 #pragma unroll
       for (int c8 = 0; c8 < CPT; ++c8) {
         const int64_t c = tid + (int64_t)TPR * c8;
         float q[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          q[e] = code_f(wh[c8][e], inv, QMAX);
-          const double dd = __builtin_fma(-Sd, (double)q[e], (double)wh[c8][e]);  // S*q is exact in fp64
+          const float r = rel_code<ASYM>(wh[c8][e], st.S, rS, zf, QMAX);
+          q[e] = ASYM ? r + zf : r;
+          const double dd = __builtin_fma(-Sd, (double)r, (double)wh[c8][e]);  // S r is exact in fp64
           e_dir = __builtin_fma(dd, dd, e_dir);
         }
-        if (wq && c < nchunk) {
-          if constexpr (BITS == 8) {
-            uint4 o;
-            o.x = pack4_i8(q[0], q[1], q[2], q[3]);
-            o.y = pack4_i8(q[4], q[5], q[6], q[7]);
-            o.z = pack4_i8(q[8], q[9], q[10], q[11]);
-            o.w = pack4_i8(q[12], q[13], q[14], q[15]);
-            *reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(wq) + n * K + c * 16) = o;
-          } else {
-            uint2 o;
-            o.x = pack8_i4(q);
-            o.y = pack8_i4(q + 8);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(wq) + n * (K / 2) + c * 8) = o;
-          }
-        }
+        if (wq && c < nchunk) store_codes<BITS>(wq, n, K, c, q);
       }
       if (mse) {
         e_dir = wave_sum(e_dir);
         if constexpr (NW > 1) {
           __syncthreads();
-          if ((tid & (kWave - 1)) == 0) red_d[tid / kWave] = e_dir;
+          if ((tid & (kWave - 1)) == 0) xd[tid / kWave] = e_dir;
           __syncthreads();
-          e_dir = red_d[0];
+          e_dir = xd[0];
 #pragma unroll
-          for (int i = 1; i < NW; ++i) e_dir += red_d[i];
+          for (int i = 1; i < NW; ++i) e_dir += xd[i];
         }
       }
     }
     if (tid == 0) {
-      scale[n] = S;
+      scale[n] = st.S;
+      if constexpr (ASYM) zero_point[n] = st.Z;
       if (iters) iters[n] = it;
       if (mse) mse[n] = per_elem(e_dir);
     }
@@ -289,17 +482,13 @@ __global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Short rows (K <= 512, at most 32 chunks of 16): one wave holds R = 64 / G rows, G lanes each
-// (G = the chunk count rounded up to a power of two, 1 to 32), one 16-element chunk per lane -- the
-// same pass length per lane as the one-wave row kernel, which at these K leaves half its lanes or
-// more idle.  Each group
-// of G lanes carries its own row's state, reduces inside the group only (DPP moves within the 16-lane
-// row, plus the 16-lane swap for G = 32), and stops updating when its row converges, while the wave
-// runs until all its rows have; a pass never takes longer than in the row kernel, and R rows share it.
-// Same formulas and decisions per row as k_ssz.
+// Short symmetric rows (K <= 512, at most 32 chunks of 16): one wave holds R = 64 / G rows, G lanes each
+// (G = the chunk count rounded up to a power of two, 1 to 32), one 16-element chunk per lane -- the same pass
+// length per lane as the one-wave row kernel, which at these K leaves half its lanes or more idle.  Each group
+// of G lanes carries its own row's state, reduces inside the group only (DPP moves within the 16-lane row, plus
+// the 16-lane swap for G = 32), and stops updating when its row converges or is deferred, while the wave runs
+// until all its rows have.  Same formulas and decisions per row as k_ssz.
 
-// sums and maximum over aligned groups of G lanes (G a power of two up to 32); every lane of a group
-// ends with the group's total, bit-identical across the group (each step adds the same two operands)
 template <int G>
 __device__ __forceinline__ double group_sum(double v) {
   if constexpr (G >= 2) v += dpp_f64<kDppXor1>(v);
@@ -353,418 +542,331 @@ __global__ __launch_bounds__(kWave) void k_ssz_rows(const void* __restrict__ w, 
   const int gl = lane % G;  // lane in the row's group
   const int64_t nchunk = K / 16;
   const DivK per_elem = make_divk(K);
+  int lg = 0;
+  while ((1 << lg) < G) ++lg;
+  const double hu = (double)(16 + lg + 8) * kU * (1.0 + 0x1p-20);
 
   // every lane runs the same number of row groups (uniform loop); rows past N compute on zeros, unwritten
   for (int64_t n0 = (int64_t)blockIdx.x * R; n0 < N; n0 += (int64_t)gridDim.x * R) {
     const int64_t n = n0 + lane / G;
     const bool live = n < N;
     float wh[CPT][16];
-    double wd[1][16];
-    load_row<DT, HAS_S, G, CPT, false>(w, live ? n : n0, K, s, gl, wh, wd);
+    load_row<DT, HAS_S, G, CPT>(w, live ? n : n0, K, s, gl, wh);
     if (!live) {
 #pragma unroll
-      for (int c8 = 0; c8 < CPT; ++c8)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) wh[0][e] = 0.0f;
     }
     float m = 0.0f;
     double w2 = 0.0;
 #pragma unroll
-    for (int c8 = 0; c8 < CPT; ++c8) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        m = fmaxf(m, fabsf(wh[c8][e]));
-        const double x = (double)wh[c8][e];
-        w2 = __builtin_fma(x, x, w2);
-      }
+    for (int e = 0; e < 16; ++e) {
+      m = fmaxf(m, fabsf(wh[0][e]));
+      const double x = (double)wh[0][e];
+      w2 = __builtin_fma(x, x, w2);
     }
     m = group_max<G>(m);
     w2 = group_sum<G>(w2);
 
-    // one pass over the group's row for the scale S of that row: A = sum w_hat q (fp64), B = sum q^2
-    auto pass = [&](float Sx, double& A, int& B) {
-      const float inv = 1.0f / Sx;
-      double a = 0.0;
-      float bq = 0.0f;
-#pragma unroll
-      for (int c8 = 0; c8 < CPT; ++c8) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float q = code_f(wh[c8][e], inv, QMAX);
-          a = __builtin_fma((double)wh[c8][e], (double)q, a);
-          bq = __builtin_fmaf(q, q, bq);
-        }
-      }
-      A = group_sum<G>(a);
-      B = group_sum<G>((int)bq);
+    // the group's pass sums for its own scale Sx (a scale outside div_rn's range computes garbage, and the
+    // caller defers the row); returns whether P is certified
+    auto pass = [&](float Sx, double& P, double& R2) -> bool {
+      const bool in = div_rn_divisor_ok(Sx);
+      const float Su = in ? Sx : 1.0f;
+      float r2, r1;
+      lane_pass<CPT, false>(wh, Su, 0.0f, QMAX, P, r2, r1);
+      P = group_sum<G>(P);
+      R2 = (double)group_sum<G>((int)r2);
+      return in && P < p_cert(Su);
     };
 
     // MinMax init
-    float S = m / QMAX;
-    S = S < min_scale ? min_scale : S;
-    double A;
-    int B;
-    pass(S, A, B);
-    double best = per_elem(sq_err(w2, S, PassSums{A, B}));
+    float S, Sp;
+    int Z;
+    minmax_init<false>(0.0f, m, QMAX, min_scale, S, Z);
+    double P, R2;
+    bool ok = pass(S, P, R2);
+    Ival best = err_ival(w2, S, P, R2, hu, per_elem);
 
     // least-squares refits, greedy, per-row convergence; a row's state stays fixed once it stops
     int it = 0;
-    bool active = live;  // rows past N take no step
+    bool active = live && ok;  // rows past N take no step
     for (int i = 1; i <= max_iter; ++i) {
       if (!__builtin_amdgcn_ballot_w64(active)) break;
       if (active) it = i;
-      const bool fit = active && B != 0;
-      if (active && B == 0) active = false;
-      float Sc = fit ? (float)(A / (double)B) : S;
+      if (active && R2 == 0.0) active = false;
+      float Sc = active ? (float)(P / R2) : S;
       Sc = Sc < min_scale ? min_scale : Sc;
-      double Ap;
-      int Bp;
-      pass(Sc, Ap, Bp);
-      const double c = per_elem(sq_err(w2, Sc, PassSums{Ap, Bp}));
-      const double d = best - c;
-      const bool conv = (best == 0.0) || (fabs(d) < thr) || rel_below(d, best, thr);
-      if (fit && c < best) {
-        S = Sc;
-        best = c;
-        A = Ap;
-        B = Bp;
+      if (active && Sc == S) {
+        // the kept scale again: the same codes and error (see k_ssz)
+        if (!(thr > 0.0 || best.hi == 0.0)) {
+          if (best.lo > 0.0) it = max_iter;
+          else ok = false;
+        }
+        active = false;
       }
-      if (fit && conv) active = false;
+      Sp = active ? Sc : S;
+      double Pc, R2c;
+      const bool pok = pass(Sp, Pc, R2c);
+      if (active && !pok) {
+        ok = false;
+        active = false;
+      }
+      const Ival cur = err_ival(w2, Sc, Pc, R2c, hu, per_elem);
+      const Decision dc = decide(best, cur, thr);
+      if (active && (dc.keep == kUnk || dc.conv == kUnk)) {
+        ok = false;
+        active = false;
+      }
+      if (active && dc.keep == kYes) {
+        S = Sc;
+        best = cur;
+        P = Pc;
+        R2 = R2c;
+      }
+      if (active && dc.conv == kYes) active = false;
     }
 
     // codes of the kept scale, and its error summed directly
     double e_dir = 0.0;
     if (wq || mse) {
-      const float inv = 1.0f / S;
-      const double Sd = (double)S;
+      const float Su = div_rn_divisor_ok(S) ? S : 1.0f;
+      const float rS = 1.0f / Su;
+      const double Sd = (double)Su;
+      const int64_t c = gl;
+      float q[16];
 #pragma unroll
-      for (int c8 = 0; c8 < CPT; ++c8) {
-        const int64_t c = gl + (int64_t)G * c8;
-        float q[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          q[e] = code_f(wh[c8][e], inv, QMAX);
-          const double dd = __builtin_fma(-Sd, (double)q[e], (double)wh[c8][e]);  // S*q is exact in fp64
-          e_dir = __builtin_fma(dd, dd, e_dir);
-        }
-        if (wq && live && c < nchunk) {
-          if constexpr (BITS == 8) {
-            uint4 o;
-            o.x = pack4_i8(q[0], q[1], q[2], q[3]);
-            o.y = pack4_i8(q[4], q[5], q[6], q[7]);
-            o.z = pack4_i8(q[8], q[9], q[10], q[11]);
-            o.w = pack4_i8(q[12], q[13], q[14], q[15]);
-            *reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(wq) + n * K + c * 16) = o;
-          } else {
-            uint2 o;
-            o.x = pack8_i4(q);
-            o.y = pack8_i4(q + 8);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(wq) + n * (K / 2) + c * 8) = o;
-          }
-        }
+      for (int e = 0; e < 16; ++e) {
+        q[e] = rel_code<false>(wh[0][e], Su, rS, 0.0f, QMAX);
+        const double dd = __builtin_fma(-Sd, (double)q[e], (double)wh[0][e]);  // S*q is exact in fp64
+        e_dir = __builtin_fma(dd, dd, e_dir);
       }
+      if (wq && live && ok && c < nchunk) store_codes<BITS>(wq, n, K, c, q);
       if (mse) e_dir = group_sum<G>(e_dir);
     }
     if (live && gl == 0) {
-      scale[n] = S;
-      if (iters) iters[n] = it;
-      if (mse) mse[n] = per_elem(e_dir);
+      scale[n] = ok ? S : __builtin_nanf("");
+      if (ok && iters) iters[n] = it;
+      if (ok && mse) mse[n] = per_elem(e_dir);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Asymmetric int8 ([SSZ] asymmetric mode: scale and offset fitted together;
-// [INT8] 2.1 Q = round(R/S) + Z with saturation).  Codes
-//   q = clamp(rne(fl32(w_hat * inv S)) + Z, -128, 127),  dequantized S (q - Z).
-// A pass for (S, Z) accumulates A = sum w_hat q (fp64), B = sum q^2 and
-// C = sum q (exact).  With the row's W1 = sum w_hat and W2 = sum w_hat^2:
-//   K mse = W2 - 2 S (A - Z W1) + S^2 (B - 2 Z C + K Z^2),
-// and the least-squares line w_hat ~ a q + b through the pass's codes solves
-// the 2x2 normal equations: det = K B - C^2, a = (K A - W1 C) / det,
-// b = (W1 - a C) / K, giving S' = max(fl32(a), min_scale) and
-// Z' = clamp(rne(-b / a), -128, 127).  MinMax init from the row's min lo and
-// max hi: S0 = max(fl32(fl32(hi - lo) / 255), min_scale),
-// Z0 = clamp(-128 - rne(fl32(lo * inv S0)), -128, 127).
-// Register slots past the row hold w_hat = 0, whose code is Z: each adds Z^2
-// to B and Z to C, which the pass subtracts exactly.
+// The exact search for deferred rows (scale[n] is NaN), one row per block of 256 threads, reading the row from
+// memory on every pass: codes by the IEEE division, P, the error and the asymmetric W1 summed in
+// double-double and rounded once, R2 and R1 exact; then the plain greedy rule and convergence test on those
+// values.  Rows with a finite scale are left as they are.
 
-struct PassSumsA {
-  double a;  // sum w_hat q
-  double b;  // sum q^2 (an exact integer)
-  double c;  // sum q   (an exact integer)
-};
+constexpr int kExactTpr = 256;
 
-__device__ __forceinline__ float code_asym_f(float x, float inv, float zf) {
-  return fminf(fmaxf(__builtin_rintf(x * inv) + zf, -128.0f), 127.0f);
+template <int DT, bool HAS_S>
+__device__ __forceinline__ float load_folded(const void* __restrict__ w, const float* __restrict__ s, int64_t n,
+                                             int64_t K, int64_t k) {
+  float v;
+  if constexpr (DT == PTQ_BF16)
+    v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(w)[n * K + k] << 16);
+  else
+    v = reinterpret_cast<const float*>(w)[n * K + k];
+  if constexpr (HAS_S) v = v * s[k];
+  return v;
 }
 
-template <int TPR, int CPT, bool WIDE>
-__device__ __forceinline__ PassSumsA row_pass_asym(const float (&wh)[CPT][16], const double (&wd)[WIDE ? CPT : 1][16],
-                                                   float S, int Z, double pad, double* red_d, int tid) {
-  const float inv = 1.0f / S;
-  const float zf = (float)Z;
-  double a = 0.0;
-  float bq = 0.0f;  // at most 16*CPT terms of <= 128^2 each: exact in fp32
-  float cq = 0.0f;
-#pragma unroll
-  for (int m = 0; m < CPT; ++m) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float q = code_asym_f(wh[m][k], inv, zf);
-      const double w = WIDE ? wd[WIDE ? m : 0][k] : (double)wh[m][k];
-      a = __builtin_fma(w, (double)q, a);
-      bq = __builtin_fmaf(q, q, bq);
-      cq += q;
-    }
-  }
-  PassSumsA r;
-  r.a = wave_sum(a);
-  r.b = (double)wave_sum((int)bq);
-  r.c = (double)wave_sum((int)cq);
-  constexpr int NW = TPR / kWave;
-  if constexpr (NW > 1) {
-    // red_d points at this pass's half of a two-pass slot ring (see row_pass)
-    const int w = tid / kWave;
-    if ((tid & (kWave - 1)) == 0) {
-      red_d[w] = r.a;
-      red_d[NW + w] = r.b;
-      red_d[2 * NW + w] = r.c;
-    }
-    __syncthreads();
-    r.a = red_d[0];
-    r.b = red_d[NW];
-    r.c = red_d[2 * NW];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) {
-      r.a += red_d[i];
-      r.b += red_d[NW + i];
-      r.c += red_d[2 * NW + i];
-    }
-  }
-  const double zd = (double)Z;
-  r.b -= pad * zd * zd;
-  r.c -= pad * zd;
-  return r;
-}
-
-// K * mse(S, Z) from the pass sums, never below 0
-__device__ __forceinline__ double sq_err_asym(double w2, double w1, double Kd, float S, int Z, const PassSumsA& p) {
-  const double Sd = (double)S, zd = (double)Z;
-  const double cross = p.a - zd * w1;
-  const double quad = (p.b - 2.0 * zd * p.c) + Kd * zd * zd;  // sum (q - Z)^2, exact
-  const double e = (w2 - 2.0 * Sd * cross) + Sd * Sd * quad;
-  return e > 0.0 ? e : 0.0;
-}
-
-template <int DT, bool HAS_S, int TPR, int CPT, int WIDE_MODE = 0>
-__global__ __launch_bounds__(TPR) void k_ssz_asym(const void* __restrict__ w, int64_t N, int64_t K,
-                                                  const float* __restrict__ s, int max_iter, double thr,
-                                                  float min_scale, float* __restrict__ scale,
-                                                  int32_t* __restrict__ zero_point, int8_t* __restrict__ wq,
-                                                  int32_t* __restrict__ iters, double* __restrict__ mse) {
-  constexpr int NW = TPR / kWave;
-  constexpr bool WIDE = WIDE_MODE == 1;
-  __shared__ double red_d[3 * NW];
-  __shared__ float red_f[2 * NW];
-  __shared__ double ring_d[2][3 * NW];  // pass sums, alternating halves
-  int par = 0;
+template <int DT, bool HAS_S, int BITS, bool ASYM>
+__global__ __launch_bounds__(kExactTpr) void k_ssz_exact(const void* __restrict__ w, int64_t N, int64_t K,
+                                                         const float* __restrict__ s, int max_iter, double thr,
+                                                         float min_scale, float* __restrict__ scale,
+                                                         int32_t* __restrict__ zero_point, void* __restrict__ wq,
+                                                         int32_t* __restrict__ iters, double* __restrict__ mse) {
+  constexpr int NW = kExactTpr / kWave;
+  constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
+  __shared__ double xd[4 * NW];
+  __shared__ float xf[2 * NW];
+  __shared__ int flag;
   const int tid = threadIdx.x;
-  const int64_t nchunk = K / 16;
   const double Kd = (double)K;
   const DivK per_elem = make_divk(K);
-  const double pad = (double)((int64_t)TPR * CPT * 16 - K);  // zero slots per row
 
-  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-    float wh[CPT][16];
-    double wd[WIDE ? CPT : 1][16];
-    load_row<DT, HAS_S, TPR, CPT, WIDE>(w, n, K, s, tid, wh, wd);
-    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-    double w1 = 0.0, w2 = 0.0;
-#pragma unroll
-    for (int c8 = 0; c8 < CPT; ++c8) {
-      const bool in = tid + (int64_t)TPR * c8 < nchunk;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float v = wh[c8][e];
-        lo = fminf(lo, in ? v : lo);
-        hi = fmaxf(hi, in ? v : hi);
-        const double x = (double)v;
-        w1 += x;
-        w2 = __builtin_fma(x, x, w2);
-      }
+  // sums over the block (every thread gets the same bits)
+  auto bsum_dd = [&](DD v) -> double {
+    v = group_sum_dd<64>(v);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+      xd[tid / kWave] = v.hi;
+      xd[NW + tid / kWave] = v.lo;
     }
+    __syncthreads();
+    DD t{xd[0], xd[NW]};
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t = dd_add(t, DD{xd[i], xd[NW + i]});
+    return t.hi + t.lo;
+  };
+  auto bsum = [&](double v) -> double {  // exact integer sums
+    v = wave_sum(v);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) xd[2 * NW + tid / kWave] = v;
+    __syncthreads();
+    double t = xd[2 * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t += xd[2 * NW + i];
+    return t;
+  };
+  auto bminmax = [&](float& lo, float& hi) {
     lo = -wave_max(-lo);
     hi = wave_max(hi);
-    w1 = wave_sum(w1);
-    w2 = wave_sum(w2);
-    if constexpr (NW > 1) {
-      __syncthreads();
-      if ((tid & (kWave - 1)) == 0) {
-        red_f[tid / kWave] = lo;
-        red_f[NW + tid / kWave] = hi;
-        red_d[tid / kWave] = w1;
-        red_d[NW + tid / kWave] = w2;
-      }
-      __syncthreads();
-      lo = red_f[0];
-      hi = red_f[NW];
-      w1 = red_d[0];
-      w2 = red_d[NW];
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+      xf[tid / kWave] = lo;
+      xf[NW + tid / kWave] = hi;
+    }
+    __syncthreads();
+    lo = xf[0];
+    hi = xf[NW];
 #pragma unroll
-      for (int i = 1; i < NW; ++i) {
-        lo = fminf(lo, red_f[i]);
-        hi = fmaxf(hi, red_f[NW + i]);
-        w1 += red_d[i];
-        w2 += red_d[NW + i];
+    for (int i = 1; i < NW; ++i) {
+      lo = fminf(lo, xf[i]);
+      hi = fmaxf(hi, xf[NW + i]);
+    }
+  };
+
+  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    if (tid == 0) flag = __builtin_isnan(scale[n]) ? 1 : 0;
+    __syncthreads();
+    const bool deferred = flag != 0;
+    __syncthreads();
+    if (!deferred) continue;
+
+    float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
+    DD w1{0.0, 0.0};
+    for (int64_t k = tid; k < K; k += kExactTpr) {
+      const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+      if constexpr (ASYM) {
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+        w1 = dd_add_d(w1, (double)v);
+      } else {
+        hi = fmaxf(hi, fabsf(v));
       }
     }
+    bminmax(lo, hi);
+    const double W1 = ASYM ? bsum_dd(w1) : 0.0;
 
-    // MinMax init
-    const float range = hi - lo;
-    float S = range / 255.0f;
-    S = S < min_scale ? min_scale : S;
-    int Z;
-    {
-      const float inv0 = 1.0f / S;
-      const float z0 = -128.0f - __builtin_rintf(lo * inv0);
-      Z = (int)fminf(fmaxf(z0, -128.0f), 127.0f);
-    }
-    PassSumsA cur = row_pass_asym<TPR, CPT, WIDE>(wh, wd, S, Z, pad, ring_d[par], tid);
-    par ^= 1;
-    double best = per_elem(sq_err_asym(w2, w1, Kd, S, Z, cur));
+    // P, R2, R1 and the mean error of (S, Z), every sum exact
+    auto pass = [&](float S, int Z, double& P, double& R2, double& R1) -> double {
+      const float zf = (float)Z;
+      const double Sd = (double)S;
+      DD p{0.0, 0.0}, e{0.0, 0.0};
+      double r2 = 0.0, r1 = 0.0;
+      for (int64_t k = tid; k < K; k += kExactTpr) {
+        const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+        const float r = rel_code_ieee<ASYM>(v, S, zf, QMAX);
+        p = dd_add_d(p, (double)v * (double)r);  // exact product
+        double dh, dl;
+        two_sum((double)v, -(Sd * (double)r), dh, dl);  // S r is exact in fp64
+        DD t = two_sqr(dh);
+        t.lo += dh * (2.0 * dl) + dl * dl;
+        e = dd_add(e, t);
+        r2 += (double)r * (double)r;
+        r1 += (double)r;
+      }
+      P = bsum_dd(p);
+      R2 = bsum(r2);
+      R1 = ASYM ? bsum(r1) : 0.0;
+      return per_elem(bsum_dd(e));
+    };
 
+    RowState st;
+    minmax_init<ASYM>(lo, hi, QMAX, min_scale, st.S, st.Z);
+    const double b0 = pass(st.S, st.Z, st.P, st.R2, st.R1);
+    double best = b0;
     int it = 0;
     for (int i = 1; i <= max_iter; ++i) {
       it = i;
-      const double det = Kd * cur.b - cur.c * cur.c;  // exact: integers below 2^53
-      if (det <= 0.0) break;
-      const double a = (Kd * cur.a - w1 * cur.c) / det;
-      const double b = per_elem(w1 - a * cur.c);
-      float Sc = (float)a;
-      Sc = Sc < min_scale ? min_scale : Sc;
-      const double zr = __builtin_rint(-b / a);
-      const int Zc = zr < -128.0 ? -128 : (zr > 127.0 ? 127 : (int)zr);
-      const PassSumsA p = row_pass_asym<TPR, CPT, WIDE>(wh, wd, Sc, Zc, pad, ring_d[par], tid);
-      par ^= 1;
-      const double c = per_elem(sq_err_asym(w2, w1, Kd, Sc, Zc, p));
-      const double d = best - c;
-      const bool conv = (best == 0.0) || (fabs(d) < thr) || rel_below(d, best, thr);
-      if (c < best) {
-        S = Sc;
-        Z = Zc;
-        best = c;
-        cur = p;
+      float Sc;
+      int Zc;
+      if (!refit<ASYM>(st, Kd, W1, per_elem, min_scale, Sc, Zc)) break;
+      RowState c;
+      c.S = Sc;
+      c.Z = Zc;
+      const double cur = pass(Sc, Zc, c.P, c.R2, c.R1);
+      const double d = best - cur;
+      const bool conv = (best == 0.0) || (fabs(d) < thr) || (d / best < thr);
+      if (cur < best) {
+        st = c;
+        best = cur;
       }
       if (conv) break;
     }
 
-    // codes of the kept (S, Z) and their error summed directly (the reported mse)
-    double e_dir = 0.0;
-    if (wq || mse) {
-      const float inv = 1.0f / S;
-      const float zf = (float)Z;
-      const double Sd = (double)S;
-#pragma unroll
-      for (int c8 = 0; c8 < CPT; ++c8) {
-        const int64_t c = tid + (int64_t)TPR * c8;
-        float q[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          q[e] = code_asym_f(wh[c8][e], inv, zf);
-          // slots past the row: w_hat = 0 and q = Z, so they add 0
-          const double dd = __builtin_fma(-Sd, (double)(q[e] - zf), (double)wh[c8][e]);  // S*(q-Z) exact in fp64
-          e_dir = __builtin_fma(dd, dd, e_dir);
-        }
-        if (wq && c < nchunk) {
-          uint4 o;
-          o.x = pack4_i8(q[0], q[1], q[2], q[3]);
-          o.y = pack4_i8(q[4], q[5], q[6], q[7]);
-          o.z = pack4_i8(q[8], q[9], q[10], q[11]);
-          o.w = pack4_i8(q[12], q[13], q[14], q[15]);
-          *reinterpret_cast<uint4*>(wq + n * K + c * 16) = o;
-        }
-      }
-      if (mse) {
-        e_dir = wave_sum(e_dir);
-        if constexpr (NW > 1) {
-          __syncthreads();
-          if ((tid & (kWave - 1)) == 0) red_d[tid / kWave] = e_dir;
-          __syncthreads();
-          e_dir = red_d[0];
-#pragma unroll
-          for (int i = 1; i < NW; ++i) e_dir += red_d[i];
+    // codes of the kept parameters
+    if (wq) {
+      const float zf = (float)st.Z;
+      for (int64_t k = tid; k < K; k += kExactTpr) {
+        const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+        const float q = rel_code_ieee<ASYM>(v, st.S, zf, QMAX) + (ASYM ? zf : 0.0f);
+        if constexpr (BITS == 8) {
+          reinterpret_cast<int8_t*>(wq)[n * K + k] = (int8_t)(int)q;
+        } else {
+          // two codes per byte: the thread of the even element writes the pair
+          const float v1 = load_folded<DT, HAS_S>(w, s, n, K, k ^ 1);
+          const float q1 = rel_code_ieee<false>(v1, st.S, 0.0f, QMAX);
+          if ((k & 1) == 0)
+            reinterpret_cast<uint8_t*>(wq)[n * (K / 2) + k / 2] =
+                (uint8_t)(((uint32_t)(int)q & 0xFu) | (((uint32_t)(int)q1 & 0xFu) << 4));
         }
       }
     }
     if (tid == 0) {
-      scale[n] = S;
-      zero_point[n] = Z;
+      scale[n] = st.S;
+      if constexpr (ASYM) zero_point[n] = st.Z;
       if (iters) iters[n] = it;
-      if (mse) mse[n] = per_elem(e_dir);
+      if (mse) mse[n] = best;
     }
   }
 }
 
-template <int DT, bool HAS_S>
-hipError_t dispatch_asym(const void* w, int64_t N, int64_t K, const float* s, int max_iter, double thr,
-                         float min_scale, float* scale, int32_t* zp, int8_t* wq, int32_t* iters, double* mse,
-                         hipStream_t stream) {
-  const int64_t nchunk = K / 16;
-  int tpr = 64;
-  while (tpr < 1024 && (nchunk + tpr - 1) / tpr > 4) tpr *= 2;
-  const int64_t cpt = (nchunk + tpr - 1) / tpr;
-#define PTQ_SA(TPR_, CPT_)                                                                                \
-  if (tpr == TPR_ && cpt <= CPT_) {                                                                       \
-    k_ssz_asym<DT, HAS_S, TPR_, CPT_><<<(unsigned)N, TPR_, 0, stream>>>(w, N, K, s, max_iter, thr,        \
-                                                                        min_scale, scale, zp, wq, iters,  \
-                                                                        mse);                             \
-    return hipGetLastError();                                                                             \
-  }
-  PTQ_SA(64, 1) PTQ_SA(64, 2) PTQ_SA(64, 4)
-  PTQ_SA(128, 4) PTQ_SA(256, 4) PTQ_SA(512, 4) PTQ_SA(1024, 4) PTQ_SA(1024, 8)
-#undef PTQ_SA
-  return hipErrorInvalidValue;
-}
+// ---------------------------------------------------------------------------
 
-template <int DT, bool HAS_S, int BITS>
+template <int DT, bool HAS_S, int BITS, bool ASYM>
 hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max_iter, double thr, float min_scale,
-                    float* scale, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
+                    float* scale, int32_t* zp, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
   const int64_t nchunk = K / 16;
-  // short rows: several rows per wave, one chunk per lane
-  if (nchunk <= 32) {
+  bool launched = false;
+  // short symmetric rows: several rows per wave, one chunk per lane
+  if (!ASYM && nchunk <= 32) {
 #define PTQ_SR(G_)                                                                                        \
-  if (nchunk <= G_) {                                                                                     \
+  if (!launched && nchunk <= G_) {                                                                        \
     constexpr int64_t R_ = kWave / G_;                                                                    \
     k_ssz_rows<DT, HAS_S, BITS, G_><<<(unsigned)((N + R_ - 1) / R_), kWave, 0, stream>>>(                 \
         w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse);                                     \
-    return hipGetLastError();                                                                             \
+    launched = true;                                                                                      \
   }
     PTQ_SR(1) PTQ_SR(2) PTQ_SR(4) PTQ_SR(8) PTQ_SR(16) PTQ_SR(32)
 #undef PTQ_SR
   }
-  // longer rows: about 64 elements per thread; one wave per row up to K = 4096
-  int tpr = 64;
-  while (tpr < 1024 && (nchunk + tpr - 1) / tpr > 4) tpr *= 2;
-  const int64_t cpt = (nchunk + tpr - 1) / tpr;
-  const int64_t blocks = N;
+  if (!launched) {
+    // longer rows: about 64 elements per thread; one wave per row up to K = 4096
+    int tpr = 64;
+    while (tpr < 1024 && (nchunk + tpr - 1) / tpr > 4) tpr *= 2;
+    const int64_t cpt = (nchunk + tpr - 1) / tpr;
 #define PTQ_S(TPR_, CPT_)                                                                                 \
-  if (tpr == TPR_ && cpt <= CPT_) {                                                                       \
-    k_ssz<DT, HAS_S, BITS, TPR_, CPT_><<<(unsigned)blocks, TPR_, 0, stream>>>(                            \
-        w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse);                                     \
-    return hipGetLastError();                                                                             \
+  if (!launched && tpr == TPR_ && cpt <= CPT_) {                                                          \
+    k_ssz<DT, HAS_S, BITS, ASYM, TPR_, CPT_><<<(unsigned)N, TPR_, 0, stream>>>(                           \
+        w, N, K, s, max_iter, thr, min_scale, scale, zp, wq, iters, mse);                                 \
+    launched = true;                                                                                      \
   }
-  PTQ_S(64, 1) PTQ_S(64, 2) PTQ_S(64, 4)
-  PTQ_S(128, 4) PTQ_S(256, 4) PTQ_S(512, 4) PTQ_S(1024, 4) PTQ_S(1024, 8)
+    PTQ_S(64, 1) PTQ_S(64, 2) PTQ_S(64, 4)
+    PTQ_S(128, 4) PTQ_S(256, 4) PTQ_S(512, 4) PTQ_S(1024, 4) PTQ_S(1024, 8)
 #undef PTQ_S
-  return hipErrorInvalidValue;
-}
-
-template <int DT, bool HAS_S>
-hipError_t dispatch_bits(const void* w, int64_t N, int64_t K, const float* s, int bits, int max_iter, double thr,
-                         float min_scale, float* scale, void* wq, int32_t* iters, double* mse, hipStream_t stream) {
-  if (bits == 8) return dispatch<DT, HAS_S, 8>(w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse, stream);
-  return dispatch<DT, HAS_S, 4>(w, N, K, s, max_iter, thr, min_scale, scale, wq, iters, mse, stream);
+  }
+  if (!launched) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the deferred rows, if any (a block per row up to 2048 blocks; each reads its rows' scales first)
+  const int64_t blocks = N < 2048 ? N : 2048;
+  k_ssz_exact<DT, HAS_S, BITS, ASYM><<<(unsigned)blocks, kExactTpr, 0, stream>>>(w, N, K, s, max_iter, thr,
+                                                                                 min_scale, scale, zp, wq, iters,
+                                                                                 mse);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -773,28 +875,31 @@ hipError_t launch_ssz_asym(const void* w, int dtype, int64_t N, int64_t K, const
                            double threshold, float min_scale, float* scale, int32_t* zero_point, int8_t* wq,
                            int32_t* iters, double* mse, hipStream_t stream) {
   if (dtype == PTQ_BF16)
-    return s ? dispatch_asym<PTQ_BF16, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
-                                             iters, mse, stream)
-             : dispatch_asym<PTQ_BF16, false>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
-                                              iters, mse, stream);
-  return s ? dispatch_asym<PTQ_F32, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq, iters,
-                                          mse, stream)
-           : dispatch_asym<PTQ_F32, false>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq, iters,
-                                           mse, stream);
+    return s ? dispatch<PTQ_BF16, true, 8, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                                 iters, mse, stream)
+             : dispatch<PTQ_BF16, false, 8, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                                  iters, mse, stream);
+  return s ? dispatch<PTQ_F32, true, 8, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                              iters, mse, stream)
+           : dispatch<PTQ_F32, false, 8, true>(w, N, K, s, max_iter, threshold, min_scale, scale, zero_point, wq,
+                                               iters, mse, stream);
 }
 
 hipError_t launch_ssz(const void* w, int dtype, int64_t N, int64_t K, const float* s, int bits, int max_iter,
                       double threshold, float min_scale, float* scale, void* wq, int32_t* iters, double* mse,
                       hipStream_t stream) {
-  if (dtype == PTQ_BF16)
-    return s ? dispatch_bits<PTQ_BF16, true>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters,
-                                             mse, stream)
-             : dispatch_bits<PTQ_BF16, false>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters,
-                                              mse, stream);
-  return s ? dispatch_bits<PTQ_F32, true>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters, mse,
-                                          stream)
-           : dispatch_bits<PTQ_F32, false>(w, N, K, s, bits, max_iter, threshold, min_scale, scale, wq, iters, mse,
-                                           stream);
+#define PTQ_B(DT_, HS_)                                                                                       \
+  return bits == 8 ? dispatch<DT_, HS_, 8, false>(w, N, K, s, max_iter, threshold, min_scale, scale, nullptr, wq, \
+                                                  iters, mse, stream)                                         \
+                   : dispatch<DT_, HS_, 4, false>(w, N, K, s, max_iter, threshold, min_scale, scale, nullptr, wq, \
+                                                  iters, mse, stream)
+  if (dtype == PTQ_BF16) {
+    if (s) PTQ_B(PTQ_BF16, true);
+    PTQ_B(PTQ_BF16, false);
+  }
+  if (s) PTQ_B(PTQ_F32, true);
+  PTQ_B(PTQ_F32, false);
+#undef PTQ_B
 }
 
 }  // namespace ptq

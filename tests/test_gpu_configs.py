@@ -384,22 +384,12 @@ def _random_shapes(n=_RANDOM_CASES, seed=_RANDOM_SEED):
     return out
 
 
-def _ties_only(g_S, g_mse, ref, what, g_Z=None):
-    """Rows where the GPU kept a different scale than the oracle must be ties: at most one per case, with the
-    GPU's reported error (a direct sum at its kept scale) within 1e-11 relative of the oracle's.  The GPU takes
-    each pass's error from the expansion W2 - 2 S A + S^2 B, which cannot separate two candidates whose errors
-    differ by ~1e-12 relative (a candidate one fp32 step from the kept scale); the strict keep-if-better rule
-    then keeps the other one.  Scales stay within the 1e-6 bar either way.  Returns the rows with equal scales."""
-    diff = (g_S != ref["S"]) if g_Z is None else ((g_S != ref["S"]) | (g_Z != ref["Z"]))
-    rows = np.nonzero(diff)[0]
-    assert rows.size <= 1, f"{what}: {rows.size} rows with a different scale"
-    for n in rows:
-        assert abs(g_mse[n] - ref["mse"][n]) <= 1e-11 * ref["mse"][n], f"{what}: row {n} differs and is no tie"
-        announce(f"{what}: row {n} keeps the other of two tied scales ({g_S[n]!r} vs {ref['S'][n]!r})")
-    return ~diff
+# Two cases of earlier sweeps whose SSZ rows hold a candidate one fp32 step from the kept scale, with errors
+# 1.15e-12 relative apart (seed 22 case 55, row 515; seed 25 case 1315, row 306): kept as fixed cases.
+_TIED_ROW_CASES = [_random_shapes(56, 22)[55], _random_shapes(1316, 25)[1315]]
 
 
-@pytest.mark.parametrize("seed,i,T,K,N,dtype,smooth,alpha,std", _random_shapes())
+@pytest.mark.parametrize("seed,i,T,K,N,dtype,smooth,alpha,std", _TIED_ROW_CASES + _random_shapes())
 def test_random_shapes_whole_path(pq, seed, i, T, K, N, dtype, smooth, alpha, std):
     """The whole path on seeded random shapes (ragged tokens, widths of 16 to ~4 K, any channel count, both input
     types, three weight spreads with heavy-tailed entries, with and without smoothing), every output against the
@@ -420,23 +410,18 @@ def test_random_shapes_whole_path(pq, seed, i, T, K, N, dtype, smooth, alpha, st
         s_ref, s = None, None
     ref = oracle.ssz(wf, s_ref, 8)
     S, wq, it, mse = pq.ssz_weight_qparams(wd, s, bits=8)
-    compare_ssz(host(S), host(wq), host(it), host(mse), ref, tag, allow_scale_mismatch=1)
-    same = _ties_only(host(S), host(mse), ref, tag)
+    compare_ssz(host(S), host(wq), host(it), host(mse), ref, tag)
     xq_ref, d_ref = oracle.quant_per_token(xf, s_ref)
     xq, d = pq.quant_per_token_i8(xd, s)
     np.testing.assert_array_equal(host(xq), xq_ref, err_msg=tag + " xq")
     np.testing.assert_array_equal(host(d), d_ref, err_msg=tag + " tok_scale")
     acc_ref = oracle.gemm_i8(xq_ref, ref["q"])
     y, acc = pq.w8a8_gemm_dequant(xq, wq, d, S, want_acc=True)
-    # output channels of a tied row hold the other scale's codes: the GEMM is compared on all the others
-    if same.any():
-        np.testing.assert_array_equal(host(acc)[:, same], acc_ref[:, same], err_msg=tag + " acc")
-        assert_y(host(y)[:, same], oracle.dequant(acc_ref, d_ref, ref["S"])[:, same], tag + " y")
+    np.testing.assert_array_equal(host(acc), acc_ref, err_msg=tag + " acc")
+    assert_y(host(y), oracle.dequant(acc_ref, d_ref, ref["S"]), tag + " y")
     r4 = oracle.ssz(wf, s_ref, 4)
     S4, q4, it4, m4 = pq.ssz_weight_qparams(wd, s, bits=4)
-    compare_ssz(host(S4), unpack_int4(host(q4)), host(it4), host(m4), r4, tag + " int4", allow_scale_mismatch=1)
-    _ties_only(host(S4), host(m4), r4, tag + " int4")
+    compare_ssz(host(S4), unpack_int4(host(q4)), host(it4), host(m4), r4, tag + " int4")
     ra = oracle.ssz_asym(wf, s_ref)
     Sa, Za, qa, ita, ma = pq.ssz_weight_qparams_asym(wd, s)
-    compare_ssz_asym(host(Sa), host(Za), host(qa), host(ita), host(ma), ra, tag + " asym", allow_scale_mismatch=1)
-    _ties_only(host(Sa), host(ma), ra, tag + " asym", g_Z=host(Za))
+    compare_ssz_asym(host(Sa), host(Za), host(qa), host(ita), host(ma), ra, tag + " asym")

@@ -380,6 +380,18 @@ def test_asym_code_table():
     for r, z, want in cases:
         got = oracle.quant_row_asym(np.array([r], dtype=np.float32), 1.0, z)[0]
         assert got == want, (r, z, got, want)
+    # quotients far beyond the int range saturate at their own end
+    for r, z, want in ((3e9, 0, 127), (-3e9, 0, -128), (1e36, -128, 127), (-1e36, 127, -128)):
+        got = oracle.quant_row_asym(np.array([r], dtype=np.float32), 1.0, z)[0]
+        assert got == want, (r, z, got, want)
+
+
+def test_asym_init_of_a_constant_row_under_a_tiny_floor():
+    """A constant positive row: range 0, so S is the floor; with the floor 1e-38 the offset
+    -128 - rne(w / S) saturates at -128 and every code at 127 (the value sits far above the grid)."""
+    w = np.full((1, 64), 0.01, dtype=np.float32)
+    r = oracle.ssz_asym(w, None, min_scale=1e-38)
+    assert r["S"][0] == np.float32(1e-38) and r["Z"][0] == -128 and np.all(r["q"][0] == 127)
 
 
 def test_asym_lsq_brute_force():
@@ -566,12 +578,13 @@ def test_gemm_brute_force():
 
 
 def test_gemm_int32_bound():
-    """K = floor((2^31 - 1) / 127^2) = 133144 is the largest K with no possible int32 overflow."""
-    K = (2 ** 31 - 1) // (127 * 127)
-    assert K == 133144
-    a = np.full((1, K), 127, dtype=np.int8)
-    assert oracle.gemm_i8(a, a)[0, 0] == 127 * 127 * K
-    a2 = np.full((1, K + 1), 127, dtype=np.int8)
+    """K = 131056, the largest multiple of 16 with 128^2 K <= 2^31 - 1, is the largest K for which no int8 codes
+    (-128 included) can overflow int32: the oracle's int64 sums stay in range there and leave it 16 columns on."""
+    K = ((2 ** 31 - 1) // (128 * 128)) // 16 * 16
+    assert K == 131056
+    a = np.full((1, K), -128, dtype=np.int8)
+    assert oracle.gemm_i8(a, a)[0, 0] == 128 * 128 * K
+    a2 = np.full((1, K + 16), -128, dtype=np.int8)
     with pytest.raises(oracle.OracleError):
         oracle.gemm_i8(a2, a2)
 
