@@ -268,6 +268,18 @@ __device__ __forceinline__ DD group_sum_dd(DD v) {
   return v;
 }
 
+// rne(t) for |t| < 2^22, as the low bits of fl32(t + 1.5 * 2^23): the addition rounds the exact sum to an
+// integer (ties to even) inside the binade [2^23, 2^24), so the low mantissa bits hold rne(t) in two's
+// complement -- one instruction instead of a rounding and a conversion.
+__device__ __forceinline__ uint32_t rne_bits(float t) { return __float_as_uint(t + 12582912.0f); }
+
+// The low bytes of four words packed into one dword, word 0's in the low byte (three byte permutes).
+__device__ __forceinline__ uint32_t pack4_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // [a0, b0, 0, 0]
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);  // [c0, d0, 0, 0]
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);               // [a0, b0, c0, d0]
+}
+
 // Four codes in [-128,127] packed into one dword, element 0 in the low byte.
 __device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d) {
   const uint32_t ia = (uint32_t)(int)a & 0xFFu, ib = (uint32_t)(int)b & 0xFFu;

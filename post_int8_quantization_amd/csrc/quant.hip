@@ -89,17 +89,34 @@ __device__ __forceinline__ void unpack16(const uint4 (&raw)[Piece<DT>::P], float
   }
 }
 
-// One row: fold, absmax (wave butterfly + LDS across waves), codes, store.  STATIC: the scale is
-// given (static_delta, its reciprocal static_inv) and no maximum is taken.  HAS_S folds by the per-column
-// factors sf: x * sf (fold_mul) or x / sf through their reciprocals rf.  cols_ok: every s_j of the block is in
-// div_rn's fold range (see the file header); the row takes the IEEE division when it is not, or when its
-// maximum (or the static scale) is out of range.
-template <int DT, bool HAS_S, int TPR, int CPT, bool STATIC>
-__device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P], const float (&sf)[CPT][16],
-                                          const float (&rf)[CPT][16], bool fold_mul, bool cols_ok, int64_t t,
-                                          int64_t T, int64_t K, int tid, int8_t* __restrict__ xq,
-                                          float* __restrict__ tok_scale, float (*red)[TPR / kWave], int parity,
-                                          float static_delta, float static_inv) {
+enum { FOLD_NONE = 0, FOLD_DIV = 1, FOLD_MUL = 2 };
+
+// The per-column factors of a thread's columns, in registers: s_j, and for the division fold also
+// r_j = fl32(1/s_j).  (Keeping s_j in LDS instead, read per element, measured slower.)
+template <int DT, int FOLD, int TPR, int CPT>
+struct ColFactors {
+  static constexpr int kRegS = FOLD != FOLD_NONE ? CPT : 1;
+  static constexpr int kRegR = FOLD == FOLD_DIV ? CPT : 1;
+  float sreg[kRegS][16];
+  float rreg[kRegR][16];
+
+  __device__ __forceinline__ float s(int m, int e, int) const { return sreg[kRegS == 1 ? 0 : m][e]; }
+  __device__ __forceinline__ float r(int m, int e) const { return rreg[kRegR == 1 ? 0 : m][e]; }
+};
+
+// One row: fold, absmax (wave butterfly + LDS across waves), codes, store.  STATIC: the scale is given
+// (static_delta, its reciprocal static_inv) and no maximum is taken.  FOLD: none, x / s_j (div_rn with the
+// reciprocals), or x * s_j.  cols_ok: every s_j of the launch is in div_rn's fold range (see the file header);
+// the row takes the IEEE division when it is not, or when its maximum (or the static scale) is out of range --
+// re-reading the row from memory, so that the loaded words need not stay live for that rare path.
+// refill() is called as soon as the row's words are unpacked: the caller reuses their registers for the
+// next row's loads, which then overlap this row's reduction and codes.
+template <int DT, int FOLD, int TPR, int CPT, bool STATIC, typename Refill>
+__device__ __forceinline__ void quant_row(uint4 (&raw)[CPT][Piece<DT>::P], const ColFactors<DT, FOLD, TPR, CPT>& cf,
+                                          bool cols_ok, const void* __restrict__ x, int64_t t, int64_t T, int64_t K,
+                                          int tid, int8_t* __restrict__ xq, float* __restrict__ tok_scale,
+                                          float (*red)[TPR / kWave], int parity, float static_delta,
+                                          float static_inv, Refill refill) {
   constexpr int NW = TPR / kWave;
   constexpr int E = Piece<DT>::E, P = Piece<DT>::P;
   float v[CPT][16];
@@ -109,10 +126,12 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
     unpack16<DT>(raw[m], v[m]);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if constexpr (HAS_S) v[m][e] = fold_mul ? v[m][e] * sf[m][e] : div_rn(v[m][e], sf[m][e], rf[m][e]);
+      if constexpr (FOLD == FOLD_DIV) v[m][e] = div_rn(v[m][e], cf.s(m, e, tid), cf.r(m, e));
+      else if constexpr (FOLD == FOLD_MUL) v[m][e] = v[m][e] * cf.s(m, e, tid);
       if constexpr (!STATIC) amax = fmaxf(amax, fabsf(v[m][e]));
     }
   }
+  refill(raw);
   float delta, inv;
   if constexpr (STATIC) {
     delta = static_delta;
@@ -130,14 +149,17 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
   const bool fast = cols_ok && (STATIC ? (delta >= 0x1p-60f && delta <= 0x1p100f)
                                        : (amax >= 0x1p-60f && amax <= 0x1p100f));
   if (!fast) {
-    // the IEEE division throughout (uniform over the row)
+    // the IEEE division throughout (uniform over the row), on the row read again
+    uint4 again[CPT][P];
+    load_raw<DT, TPR, CPT>(x, t, T, K, tid, again);
     amax = 0.0f;
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
-      unpack16<DT>(raw[m], v[m]);
+      unpack16<DT>(again[m], v[m]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if constexpr (HAS_S) v[m][e] = fold_mul ? v[m][e] * sf[m][e] : v[m][e] / sf[m][e];
+        if constexpr (FOLD == FOLD_DIV) v[m][e] = v[m][e] / cf.s(m, e, tid);
+        else if constexpr (FOLD == FOLD_MUL) v[m][e] = v[m][e] * cf.s(m, e, tid);
         if constexpr (!STATIC) amax = fmaxf(amax, fabsf(v[m][e]));
       }
     }
@@ -162,24 +184,33 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + (live ? t : 0) * K, live ? (uint32_t)K : 0u);
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    float q[16];
+    // the quotients x_hat / delta; a per-token one needs no saturation: |x_hat| <= a, so the quotient is at
+    // most 127 (1 + 2^-24) and rounds to at most 127.  The static scale saturates (before rounding: the same
+    // code, since the bounds are integers).  The codes are rounded by rne_bits and packed byte-wise.
+    uint32_t qb[16];
+    float tq[16];
     if (fast) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = code_f(v[m][e], delta, inv, 127.0f);
+      for (int e = 0; e < 16; ++e) tq[e] = div_rn(v[m][e], delta, inv);
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = code_f_ieee(v[m][e], delta, 127.0f);
+      for (int e = 0; e < 16; ++e) tq[e] = v[m][e] / delta;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if constexpr (STATIC) tq[e] = fminf(fmaxf(tq[e], -127.0f), 127.0f);
+      qb[e] = rne_bits(tq[e]);
     }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint32_t c = (uint32_t)piece_col<DT, TPR>(m, p, tid);
       if constexpr (E == 8) {
         uint2 o;
-        o.x = pack4_i8(q[p * 8 + 0], q[p * 8 + 1], q[p * 8 + 2], q[p * 8 + 3]);
-        o.y = pack4_i8(q[p * 8 + 4], q[p * 8 + 5], q[p * 8 + 6], q[p * 8 + 7]);
+        o.x = pack4_low_bytes(qb[p * 8 + 0], qb[p * 8 + 1], qb[p * 8 + 2], qb[p * 8 + 3]);
+        o.y = pack4_low_bytes(qb[p * 8 + 4], qb[p * 8 + 5], qb[p * 8 + 6], qb[p * 8 + 7]);
         buf_store8(rq, c, o);
       } else {
-        buf_store4(rq, c, pack4_i8(q[p * 4 + 0], q[p * 4 + 1], q[p * 4 + 2], q[p * 4 + 3]));
+        buf_store4(rq, c, pack4_low_bytes(qb[p * 4 + 0], qb[p * 4 + 1], qb[p * 4 + 2], qb[p * 4 + 3]));
       }
     }
   }
@@ -194,13 +225,13 @@ __device__ __forceinline__ void quant_row(const uint4 (&raw)[CPT][Piece<DT>::P],
 // refilled with the row D strides ahead as soon as its row is quantized.  A
 // block walks whole rounds of D rows; the rows of a round past T are no-ops
 // (zero-length descriptors).
-// STATIC: one given scale (scale[0]) for every row, as a per-tensor static quantization; fold_mul
-// folds by s_j (the weight side, fl32(x * s_j)) instead of fl32(x / s_j) (the activation side).
-template <int DT, bool HAS_S, int TPR, int CPT, int D, bool STATIC>
+// STATIC: one given scale (scale[0]) for every row, as a per-tensor static quantization.  FOLD_MUL folds by
+// s_j (the weight side, fl32(x * s_j)), FOLD_DIV by fl32(x / s_j) (the activation side).
+template <int DT, int FOLD, int TPR, int CPT, int D, bool STATIC>
 __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, int64_t T, int64_t K,
                                                    const float* __restrict__ s, int8_t* __restrict__ xq,
-                                                   float* __restrict__ tok_scale, const float* __restrict__ scale,
-                                                   int fold_mul) {
+                                                   float* __restrict__ tok_scale, const float* __restrict__ scale) {
+  using CF = ColFactors<DT, FOLD, TPR, CPT>;
   constexpr int E = Piece<DT>::E, P = Piece<DT>::P;
   __shared__ float red[2][TPR / kWave];
   const int tid = threadIdx.x;
@@ -208,6 +239,7 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 
   // the smoothing factors of this thread's columns are loaded first, so that waiting for them (loads
   // complete in issue order) leaves the first D rows in flight while the reciprocals are computed
+  constexpr bool HAS_S = FOLD != FOLD_NONE;
   uint4 sv[HAS_S ? CPT : 1][4];
   if constexpr (HAS_S) {
     const __amdgpu_buffer_rsrc_t rsc = buf_rsrc(s, (uint32_t)(K * 4));
@@ -223,34 +255,33 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 #pragma unroll
   for (int d = 0; d < D; ++d) load_raw<DT, TPR, CPT>(x, blockIdx.x + d * G, T, K, tid, ring[d]);
 
-  float sf[CPT][16], rf[CPT][16];
+  CF cf;
   bool cols_ok = true;
   if constexpr (HAS_S) {
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const bool in = piece_col<DT, TPR>(m, p, tid) < K;
+        const int64_t c0 = piece_col<DT, TPR>(m, p, tid);
+        const bool in = c0 < K;
 #pragma unroll
         for (int h = 0; h < E / 4; ++h) {
           const uint4 w = sv[m][p * (E / 4) + h];
           const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            const int e = p * E + 4 * h + i;
             const float sj = in ? __uint_as_float(u[i]) : 1.0f;
-            sf[m][p * E + 4 * h + i] = sj;
-            rf[m][p * E + 4 * h + i] = fold_mul ? 1.0f : 1.0f / sj;
-            cols_ok = cols_ok && (fold_mul || (sj >= 0x1p-20f && sj <= 0x1p100f));
+            cf.sreg[m][e] = sj;
+            if constexpr (FOLD == FOLD_DIV) {
+              cf.rreg[m][e] = 1.0f / sj;
+              cols_ok = cols_ok && (sj >= 0x1p-20f && sj <= 0x1p100f);
+            }
           }
         }
       }
     }
     cols_ok = __syncthreads_and(cols_ok) != 0;
-  } else {
-#pragma unroll
-    for (int m = 0; m < CPT; ++m)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sf[m][e] = rf[m][e] = 1.0f;
   }
   float static_delta = 1.0f, static_inv = 1.0f;
   if constexpr (STATIC) {
@@ -262,25 +293,24 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int64_t t = base + d * G;
-      quant_row<DT, HAS_S, TPR, CPT, STATIC>(ring[d], sf, rf, fold_mul != 0, cols_ok, t, T, K, tid, xq, tok_scale,
-                                             red, parity, static_delta, static_inv);
+      quant_row<DT, FOLD, TPR, CPT, STATIC>(
+          ring[d], cf, cols_ok, x, t, T, K, tid, xq, tok_scale, red, parity, static_delta, static_inv,
+          [&](uint4 (&slot)[CPT][P]) { load_raw<DT, TPR, CPT>(x, t + D * G, T, K, tid, slot); });
       parity ^= 1;
-      load_raw<DT, TPR, CPT>(x, t + D * G, T, K, tid, ring[d]);
     }
   }
 }
 
-template <int DT, bool HAS_S, int TPR, int CPT, bool STATIC>
+template <int DT, int FOLD, int TPR, int CPT, bool STATIC>
 void launch_one(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, const float* scale,
-                int fold_mul, int64_t blocks, hipStream_t stream) {
+                int64_t blocks, hipStream_t stream) {
   constexpr int D = CPT >= 4 ? 1 : 4 / CPT;  // rows in flight per block: about 4 groups of 16 elements per thread
-  k_quant_tok<DT, HAS_S, TPR, CPT, D, STATIC><<<(unsigned)blocks, TPR, 0, stream>>>(x, T, K, s, xq, ts, scale,
-                                                                                    fold_mul);
+  k_quant_tok<DT, FOLD, TPR, CPT, D, STATIC><<<(unsigned)blocks, TPR, 0, stream>>>(x, T, K, s, xq, ts, scale);
 }
 
-template <int DT, bool HAS_S, bool STATIC>
+template <int DT, int FOLD, bool STATIC>
 hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t* xq, float* ts, const float* scale,
-                    int fold_mul, int64_t rows_per_block, hipStream_t stream) {
+                    int64_t rows_per_block, hipStream_t stream) {
   const int64_t ngroup = K / 16;
   // the narrowest block with at most 2 groups of 16 elements per thread (up to 8 at 1024 threads)
   int tpr = 64;
@@ -294,7 +324,7 @@ hipError_t dispatch(const void* x, int64_t T, int64_t K, const float* s, int8_t*
   if (blocks < 1) blocks = 1;
 #define PTQ_Q(TPR_, CPT_)                                                           \
   if (tpr == TPR_ && cpt <= CPT_) {                                                 \
-    launch_one<DT, HAS_S, TPR_, CPT_, STATIC>(x, T, K, s, xq, ts, scale, fold_mul, blocks, stream); \
+    launch_one<DT, FOLD, TPR_, CPT_, STATIC>(x, T, K, s, xq, ts, scale, blocks, stream); \
     return hipGetLastError();                                                       \
   }
   PTQ_Q(64, 1) PTQ_Q(64, 2) PTQ_Q(128, 2) PTQ_Q(256, 2) PTQ_Q(512, 2)
@@ -311,25 +341,28 @@ static int64_t default_rows_per_block(int64_t T, int64_t K) {
   return r < 1 ? 1 : (r > 16 ? 16 : r);
 }
 
+template <int DT, bool STATIC>
+hipError_t dispatch_fold(const void* x, int64_t T, int64_t K, const float* s, int fold_mul, int8_t* xq, float* ts,
+                         const float* scale, int64_t rpb, hipStream_t stream) {
+  if (!s) return dispatch<DT, FOLD_NONE, STATIC>(x, T, K, s, xq, ts, scale, rpb, stream);
+  if (fold_mul) return dispatch<DT, FOLD_MUL, STATIC>(x, T, K, s, xq, ts, scale, rpb, stream);
+  return dispatch<DT, FOLD_DIV, STATIC>(x, T, K, s, xq, ts, scale, rpb, stream);
+}
+
 // rows_per_block <= 0 picks the default
 hipError_t launch_quant_per_token_rpb(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,
                                       float* tok_scale, int64_t rows_per_block, hipStream_t stream) {
   if (rows_per_block <= 0) rows_per_block = default_rows_per_block(T, K);
   if (dtype == PTQ_BF16)
-    return s ? dispatch<PTQ_BF16, true, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream)
-             : dispatch<PTQ_BF16, false, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream);
-  return s ? dispatch<PTQ_F32, true, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream)
-           : dispatch<PTQ_F32, false, false>(x, T, K, s, xq, tok_scale, nullptr, 0, rows_per_block, stream);
+    return dispatch_fold<PTQ_BF16, false>(x, T, K, s, 0, xq, tok_scale, nullptr, rows_per_block, stream);
+  return dispatch_fold<PTQ_F32, false>(x, T, K, s, 0, xq, tok_scale, nullptr, rows_per_block, stream);
 }
 
 hipError_t launch_quant_static(const void* x, int dtype, int64_t rows, int64_t cols, const float* s, int fold_mul,
                                const float* scale, int8_t* q, float* row_scale, hipStream_t stream) {
   const int64_t rpb = default_rows_per_block(rows, cols);
-  if (dtype == PTQ_BF16)
-    return s ? dispatch<PTQ_BF16, true, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream)
-             : dispatch<PTQ_BF16, false, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream);
-  return s ? dispatch<PTQ_F32, true, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream)
-           : dispatch<PTQ_F32, false, true>(x, rows, cols, s, q, row_scale, scale, fold_mul, rpb, stream);
+  if (dtype == PTQ_BF16) return dispatch_fold<PTQ_BF16, true>(x, rows, cols, s, fold_mul, q, row_scale, scale, rpb, stream);
+  return dispatch_fold<PTQ_F32, true>(x, rows, cols, s, fold_mul, q, row_scale, scale, rpb, stream);
 }
 
 hipError_t launch_quant_per_token(const void* x, int dtype, int64_t T, int64_t K, const float* s, int8_t* xq,

@@ -681,7 +681,8 @@ __global__ __launch_bounds__(kExactTpr) void k_ssz_exact(const void* __restrict_
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
   __shared__ double xd[4 * NW];
   __shared__ float xf[2 * NW];
-  __shared__ int flag;
+  __shared__ int flag;                // deferred rows in the current chunk
+  __shared__ int list[kExactTpr];     // and their indices in the chunk
   const int tid = threadIdx.x;
   const double Kd = (double)K;
   const DivK per_elem = make_divk(K);
@@ -728,99 +729,107 @@ __global__ __launch_bounds__(kExactTpr) void k_ssz_exact(const void* __restrict_
     }
   };
 
-  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-    if (tid == 0) flag = __builtin_isnan(scale[n]) ? 1 : 0;
+  // chunks of kExactTpr rows: every thread reads one row's scale, the deferred rows of the chunk are listed in
+  // LDS (in any order), then searched one at a time by the whole block
+  const int64_t nchunks = (N + kExactTpr - 1) / kExactTpr;
+  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+    if (tid == 0) flag = 0;
     __syncthreads();
-    const bool deferred = flag != 0;
+    const int64_t mine = ch * kExactTpr + tid;
+    if (mine < N && __builtin_isnan(scale[mine])) list[atomicAdd(&flag, 1)] = (int)tid;
     __syncthreads();
-    if (!deferred) continue;
+    const int count = flag;
+    for (int li = 0; li < count; ++li) {
+      const int64_t n = ch * kExactTpr + list[li];
 
-    float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
-    DD w1{0.0, 0.0};
-    for (int64_t k = tid; k < K; k += kExactTpr) {
-      const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
-      if constexpr (ASYM) {
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-        w1 = dd_add_d(w1, (double)v);
-      } else {
-        hi = fmaxf(hi, fabsf(v));
-      }
-    }
-    bminmax(lo, hi);
-    const double W1 = ASYM ? bsum_dd(w1) : 0.0;
-
-    // P, R2, R1 and the mean error of (S, Z), every sum exact
-    auto pass = [&](float S, int Z, double& P, double& R2, double& R1) -> double {
-      const float zf = (float)Z;
-      const double Sd = (double)S;
-      DD p{0.0, 0.0}, e{0.0, 0.0};
-      double r2 = 0.0, r1 = 0.0;
+      float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
+      DD w1{0.0, 0.0};
       for (int64_t k = tid; k < K; k += kExactTpr) {
         const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
-        const float r = rel_code_ieee<ASYM>(v, S, zf, QMAX);
-        p = dd_add_d(p, (double)v * (double)r);  // exact product
-        double dh, dl;
-        two_sum((double)v, -(Sd * (double)r), dh, dl);  // S r is exact in fp64
-        DD t = two_sqr(dh);
-        t.lo += dh * (2.0 * dl) + dl * dl;
-        e = dd_add(e, t);
-        r2 += (double)r * (double)r;
-        r1 += (double)r;
-      }
-      P = bsum_dd(p);
-      R2 = bsum(r2);
-      R1 = ASYM ? bsum(r1) : 0.0;
-      return per_elem(bsum_dd(e));
-    };
-
-    RowState st;
-    minmax_init<ASYM>(lo, hi, QMAX, min_scale, st.S, st.Z);
-    const double b0 = pass(st.S, st.Z, st.P, st.R2, st.R1);
-    double best = b0;
-    int it = 0;
-    for (int i = 1; i <= max_iter; ++i) {
-      it = i;
-      float Sc;
-      int Zc;
-      if (!refit<ASYM>(st, Kd, W1, per_elem, min_scale, Sc, Zc)) break;
-      RowState c;
-      c.S = Sc;
-      c.Z = Zc;
-      const double cur = pass(Sc, Zc, c.P, c.R2, c.R1);
-      const double d = best - cur;
-      const bool conv = (best == 0.0) || (fabs(d) < thr) || (d / best < thr);
-      if (cur < best) {
-        st = c;
-        best = cur;
-      }
-      if (conv) break;
-    }
-
-    // codes of the kept parameters
-    if (wq) {
-      const float zf = (float)st.Z;
-      for (int64_t k = tid; k < K; k += kExactTpr) {
-        const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
-        const float q = rel_code_ieee<ASYM>(v, st.S, zf, QMAX) + (ASYM ? zf : 0.0f);
-        if constexpr (BITS == 8) {
-          reinterpret_cast<int8_t*>(wq)[n * K + k] = (int8_t)(int)q;
+        if constexpr (ASYM) {
+          lo = fminf(lo, v);
+          hi = fmaxf(hi, v);
+          w1 = dd_add_d(w1, (double)v);
         } else {
-          // two codes per byte: the thread of the even element writes the pair
-          const float v1 = load_folded<DT, HAS_S>(w, s, n, K, k ^ 1);
-          const float q1 = rel_code_ieee<false>(v1, st.S, 0.0f, QMAX);
-          if ((k & 1) == 0)
-            reinterpret_cast<uint8_t*>(wq)[n * (K / 2) + k / 2] =
-                (uint8_t)(((uint32_t)(int)q & 0xFu) | (((uint32_t)(int)q1 & 0xFu) << 4));
+          hi = fmaxf(hi, fabsf(v));
         }
       }
+      bminmax(lo, hi);
+      const double W1 = ASYM ? bsum_dd(w1) : 0.0;
+
+      // P, R2, R1 and the mean error of (S, Z), every sum exact
+      auto pass = [&](float S, int Z, double& P, double& R2, double& R1) -> double {
+        const float zf = (float)Z;
+        const double Sd = (double)S;
+        DD p{0.0, 0.0}, e{0.0, 0.0};
+        double r2 = 0.0, r1 = 0.0;
+        for (int64_t k = tid; k < K; k += kExactTpr) {
+          const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+          const float r = rel_code_ieee<ASYM>(v, S, zf, QMAX);
+          p = dd_add_d(p, (double)v * (double)r);  // exact product
+          double dh, dl;
+          two_sum((double)v, -(Sd * (double)r), dh, dl);  // S r is exact in fp64
+          DD t = two_sqr(dh);
+          t.lo += dh * (2.0 * dl) + dl * dl;
+          e = dd_add(e, t);
+          r2 += (double)r * (double)r;
+          r1 += (double)r;
+        }
+        P = bsum_dd(p);
+        R2 = bsum(r2);
+        R1 = ASYM ? bsum(r1) : 0.0;
+        return per_elem(bsum_dd(e));
+      };
+
+      RowState st;
+      minmax_init<ASYM>(lo, hi, QMAX, min_scale, st.S, st.Z);
+      const double b0 = pass(st.S, st.Z, st.P, st.R2, st.R1);
+      double best = b0;
+      int it = 0;
+      for (int i = 1; i <= max_iter; ++i) {
+        it = i;
+        float Sc;
+        int Zc;
+        if (!refit<ASYM>(st, Kd, W1, per_elem, min_scale, Sc, Zc)) break;
+        RowState c;
+        c.S = Sc;
+        c.Z = Zc;
+        const double cur = pass(Sc, Zc, c.P, c.R2, c.R1);
+        const double d = best - cur;
+        const bool conv = (best == 0.0) || (fabs(d) < thr) || (d / best < thr);
+        if (cur < best) {
+          st = c;
+          best = cur;
+        }
+        if (conv) break;
+      }
+
+      // codes of the kept parameters
+      if (wq) {
+        const float zf = (float)st.Z;
+        for (int64_t k = tid; k < K; k += kExactTpr) {
+          const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+          const float q = rel_code_ieee<ASYM>(v, st.S, zf, QMAX) + (ASYM ? zf : 0.0f);
+          if constexpr (BITS == 8) {
+            reinterpret_cast<int8_t*>(wq)[n * K + k] = (int8_t)(int)q;
+          } else {
+            // two codes per byte: the thread of the even element writes the pair
+            const float v1 = load_folded<DT, HAS_S>(w, s, n, K, k ^ 1);
+            const float q1 = rel_code_ieee<false>(v1, st.S, 0.0f, QMAX);
+            if ((k & 1) == 0)
+              reinterpret_cast<uint8_t*>(wq)[n * (K / 2) + k / 2] =
+                  (uint8_t)(((uint32_t)(int)q & 0xFu) | (((uint32_t)(int)q1 & 0xFu) << 4));
+          }
+        }
+      }
+      if (tid == 0) {
+        scale[n] = st.S;
+        if constexpr (ASYM) zero_point[n] = st.Z;
+        if (iters) iters[n] = it;
+        if (mse) mse[n] = best;
+      }
     }
-    if (tid == 0) {
-      scale[n] = st.S;
-      if constexpr (ASYM) zero_point[n] = st.Z;
-      if (iters) iters[n] = it;
-      if (mse) mse[n] = best;
-    }
+    __syncthreads();  // the chunk's list is read by all before the next chunk rebuilds it
   }
 }
 
@@ -861,8 +870,10 @@ hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max
   if (!launched) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the deferred rows, if any (a block per row up to 2048 blocks; each reads its rows' scales first)
-  const int64_t blocks = N < 2048 ? N : 2048;
+  // the deferred rows, if any: a block per chunk of kExactTpr rows (up to 1024 blocks), which reads the chunk's
+  // scales first, so a launch with nothing deferred costs one load per row
+  const int64_t nchunks = (N + kExactTpr - 1) / kExactTpr;
+  const int64_t blocks = nchunks < 1024 ? nchunks : 1024;
   k_ssz_exact<DT, HAS_S, BITS, ASYM><<<(unsigned)blocks, kExactTpr, 0, stream>>>(w, N, K, s, max_iter, thr,
                                                                                  min_scale, scale, zp, wq, iters,
                                                                                  mse);
