@@ -38,6 +38,10 @@ once, untimed; a step is the per-token quantization of the token batch and
 the int8 GEMM with dequantization.  The int8 weight is rotated over three
 copies so that it is read from HBM, not from the 256 MB last-level cache.
 
+The default line also times the same step at alpha 0.8 (the other point of the smoothing sweep) and reports,
+beside the oracle on the host cores, the oracle on one host thread on samples of the tiny, hidden-1024 and
+decode configurations.
+
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--alpha 0.5] [--no-cpu-baseline]
                   [--workload opt67b|gpt345m|decode|ssz_scale|mlp_static]
 """
@@ -58,7 +62,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_I8 = 5.0e15           # int8 dense MFMA ops/s
 PEAK_ALU = 256 * 64 * 2.4e9  # VALU lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
-SSZ_OPS_PER_ELEM_PASS = 5  # scale-multiply, round, clamp, two multiply-adds (sum w q, sum q^2)
+# lane operations per element and pass of the SSZ search: the quotient w / S (the product with the reciprocal and
+# its two-multiply-add correction), the rounding, the clamp, and the two sums (w q in fp64, q^2)
+SSZ_OPS_PER_ELEM_PASS = 7
 METRIC = "W8A8 GEMM TOPS + quant/SSZ GB/s at hidden 4096; % of INT8/HBM peak"
 
 
@@ -74,6 +80,10 @@ def parse():
     p.add_argument("--workload", choices=("opt67b", "gpt345m", "decode", "ssz_scale", "mlp_static"), default="opt67b")
     p.add_argument("--momentum", type=float, default=0.9, help="mlp_static: moving-average momentum")
     p.add_argument("--layers", type=int, default=32, help="ssz_scale workload: number of 4-matrix layers")
+    p.add_argument("--alpha2", type=float, default=0.8, help="second smoothing strength timed (opt67b; <0: none)")
+    p.add_argument("--oracle-single-thread", action="store_true",
+                   help="only time the oracle on samples of the tiny, hidden-1024 and decode configurations and print "
+                        "one JSON line (run by the default line in a child process with one OpenMP thread)")
     p.add_argument("--copy-ref", action="store_true",
                    help="only run a plain 1 GiB device copy three times (reference for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -112,6 +122,19 @@ class Timer:
         for name, a, b in self.marks:
             ms, n = out.get(name, (0.0, 0))
             out[name] = (ms + a.elapsed_time(b), n + 1)
+        return out
+
+    def medians(self, steps):
+        """Median over the steps of each stage's time per step (ms): a stage's launches within a step are
+        summed, then the median is taken over steps."""
+        per = {}
+        for name, a, b in self.marks:
+            per.setdefault(name, []).append(a.elapsed_time(b))
+        out = {}
+        for name, v in per.items():
+            k = len(v) // steps  # launches per step
+            sums = sorted(sum(v[i * k:(i + 1) * k]) for i in range(steps))
+            out[name] = sums[len(sums) // 2] if len(sums) % 2 else 0.5 * (sums[len(sums) // 2 - 1] + sums[len(sums) // 2])
         return out
 
 
@@ -218,6 +241,9 @@ def main():
     if args.copy_ref:
         copy_reference()
         return
+    if args.oracle_single_thread:
+        oracle_single_thread()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the path "
@@ -273,11 +299,13 @@ def main():
     torch.cuda.synchronize()
 
     # every launch goes to the current stream (None), so the same step also captures into a graph
+    alpha = [args.alpha]
+
     def step(tm):
         for L in layers:
             tm.stage("calib_x", lambda: pq.sq_absmax_calib(L["calib"], L["ax"], stream=None))
             tm.stage("calib_w", lambda: pq.sq_absmax_calib(L["w"], L["aw"], stream=None))
-            tm.stage("smooth", lambda: pq.sq_smooth_factors(L["ax"], L["aw"], args.alpha, s=L["s"], stream=None))
+            tm.stage("smooth", lambda: pq.sq_smooth_factors(L["ax"], L["aw"], alpha[0], s=L["s"], stream=None))
             tm.stage("ssz", lambda: pq.ssz_weight_qparams(L["w"], L["s"], bits=8, scale=L["S"], wq=L["wq"],
                                                           iters=L["it"], mse=L["mse"], stream=None))
             tm.stage("quant", lambda: pq.quant_per_token_i8(L["x"], L["s"], xq=L["xq"], tok_scale=L["d"],
@@ -297,6 +325,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     tot = tm.totals()
+    med = tm.medians(args.steps)
     graph_ms = graph_step_ms(torch, step, args.steps)
     graph_stage = graph_stage_ms(torch, step, ("calib_x", "calib_w", "smooth", "ssz", "quant", "gemm"), args.steps)
 
@@ -338,6 +367,10 @@ def main():
                   "frac_hbm": quant_bytes / sec("quant") / PEAK_HBM},
         "gemm": {"ms": gemm_s * 1e3, "TOPS": gemm_tops, "frac_i8": gemm_ops / gemm_s / PEAK_I8},
     }
+    for nm in stages:
+        stages[nm]["ms_median"] = med[nm]
+    stages["gemm"]["TOPS_median"] = gemm_ops / (med["gemm"] / 1e3) / 1e12
+    stages["ssz"]["frac_alu_median"] = SSZ_OPS_PER_ELEM_PASS * elem_passes / (med["ssz"] / 1e3) / PEAK_ALU
     stage_bytes = {"calib_x": calib_x_bytes, "calib_w": calib_w_bytes, "quant": quant_bytes}
     for nm, g in graph_stage.items():
         stages[nm]["graph_ms"] = g
@@ -389,9 +422,93 @@ def main():
         "graph_ms_per_step": graph_ms,
         "stages": stages, "roofline": roof,
     }
+    if wl == "opt67b" and args.alpha2 >= 0:
+        out["alpha_%g" % args.alpha2] = second_alpha(torch, np, step, layers, alpha, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args, synth)
+        out["cpu_single_thread"] = single_thread_child()
     print(json.dumps(out), flush=True)
+
+
+def second_alpha(torch, np, step, layers, alpha, args):
+    """The same step at the second smoothing strength of the sweep (fewer steps): stage times (mean and
+    median over the steps), SSZ steps and its VALU fraction, GEMM rate."""
+    alpha[0] = args.alpha2
+    step(Timer(torch))
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 4)
+    tm = Timer(torch)
+    for _ in range(n):
+        step(tm)
+    torch.cuda.synchronize()
+    alpha[0] = args.alpha
+    tot, med = tm.totals(), tm.medians(n)
+    passes = sum(int(L["case"].K * (L["it"].cpu().numpy().astype(np.int64) + 1).sum()) for L in layers)
+    ops = sum(2 * L["case"].T * L["case"].N * L["case"].K for L in layers)
+    out = {"steps": n, "gpu_ms_per_step": sum(v[0] for v in tot.values()) / n,
+           "stages_ms": {k: v[0] / n for k, v in tot.items()}, "stages_ms_median": med,
+           "ssz_mean_iters": {L["case"].name: float(L["it"].float().mean()) for L in layers},
+           "ssz_frac_alu": SSZ_OPS_PER_ELEM_PASS * passes / (tot["ssz"][0] / n / 1e3) / PEAK_ALU,
+           "gemm_TOPS": ops / (tot["gemm"][0] / n / 1e3) / 1e12}
+    out["gemm_frac_i8"] = out["gemm_TOPS"] * 1e12 / PEAK_I8
+    return out
+
+
+def single_thread_child():
+    """The oracle on one host thread (a child process with OMP_NUM_THREADS=1): see oracle_single_thread."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-single-thread"], env=env,
+                       capture_output=True, text=True, timeout=600)
+    for line in r.stdout.splitlines():
+        if line.startswith("{"):
+            return json.loads(line)
+    return {"error": (r.stderr or r.stdout)[-400:]}
+
+
+def oracle_single_thread():
+    """The oracle on one host thread on samples of three configurations (seconds per sample; reported, not a
+    target): the tiny layer whole (calibration, smoothing, SSZ, per-token quantization, GEMM, dequantization);
+    the hidden-1024 QKV layer on 64 tokens and 64 weight rows (calibration over all 8 batches, all weight columns);
+    the decode layer on its 16 tokens against 2048 weight rows (SSZ on 64 of them)."""
+    import oracle
+    import synth
+    res = {"threads": oracle.num_threads()}
+
+    def path(c, tok, rows, ssz_rows, batches):
+        w = synth.widen(c.w())[:rows]
+        xs = [synth.widen(c.x_batch(b, T=tok)) for b in range(batches)]
+        xe = synth.widen(c.x_batch(c.eval_index(), T=tok))
+        t = {}
+        t0 = time.perf_counter()
+        ax = None
+        for xb in xs:
+            ax = oracle.absmax_cols(xb, ax)
+        aw = oracle.absmax_cols(w)
+        sm = oracle.smooth_factors(ax, aw, 0.5)
+        t["calib_smooth_s"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        q = oracle.ssz(w[:ssz_rows], sm, 8)
+        t["ssz_s"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        xq, d = oracle.quant_per_token(xe, sm)
+        t["quant_s"] = time.perf_counter() - t0
+        wq = oracle.quant_per_token(w)[0] if rows > ssz_rows else q["q"]  # codes of the sampled rows for the GEMM
+        t0 = time.perf_counter()
+        acc = oracle.gemm_i8(xq, wq)
+        oracle.dequant(acc, d, np.ones(rows, np.float32))
+        t["gemm_dequant_s"] = time.perf_counter() - t0
+        t["sample"] = {"tokens": tok, "weight_rows": rows, "ssz_rows": ssz_rows, "K": c.K, "calib_batches": batches}
+        return t
+
+    import numpy as np
+    c1 = synth.cases("tiny")[0]
+    res["tiny"] = path(c1, c1.T, c1.N, c1.N, 1)
+    c2 = synth.cases("gpt345m")[0]
+    res["gpt345m_qkv"] = path(c2, 64, 64, 64, c2.calib_batches)
+    c3 = synth.cases("decode")[0]
+    res["decode"] = path(c3, c3.T, 2048, 64, c3.calib_batches)
+    print(json.dumps(res), flush=True)
 
 
 def decode(args):
@@ -757,9 +874,11 @@ def cpu_baseline(layers, args, synth):
         oracle.gemm_i8(xq, wq)
         rate = 2 * probe_tok * c.N * c.K / (time.perf_counter() - g0)
         plans.append((L, w, rate))
+    import numpy as np
     gemm_ops = 0
     gemm_s = path_s = 0.0
     detail = {}
+    ssz_rows = 256
     for L, w, rate in plans:
         c = L["case"]
         tok = int(args.cpu_seconds / len(plans) * rate / (2 * c.N * c.K))
@@ -773,8 +892,11 @@ def cpu_baseline(layers, args, synth):
         aw = oracle.absmax_cols(w)
         s = oracle.smooth_factors(ax, aw, args.alpha)
         t1 = time.perf_counter()
-        q = oracle.ssz(w, s, 8)
+        # SSZ on a row sample (the oracle sums in binary128; all rows would take ~30 s on 16 cores); the
+        # GEMM below takes codes of every row (any int8 codes of the right shape time the same)
+        qs = oracle.ssz(w[:ssz_rows], s, 8)
         t2 = time.perf_counter()
+        q = {"q": oracle.quant_per_token(w)[0], "S": np.ones(c.N, np.float32)}
         xq, d = oracle.quant_per_token(xe, s)
         t3 = time.perf_counter()
         acc = oracle.gemm_i8(xq, q["q"])
@@ -784,12 +906,14 @@ def cpu_baseline(layers, args, synth):
         gemm_ops += 2 * tok * c.N * c.K
         gemm_s += t4 - t3
         path_s += t5 - t0
-        detail[c.name] = {"tokens": tok, "weight_rows": c.N, "calib_s": t1 - t0, "ssz_s": t2 - t1,
+        detail[c.name] = {"tokens": tok, "weight_rows": c.N, "calib_s": t1 - t0, "ssz_rows": ssz_rows,
+                          "ssz_s": t2 - t1, "ssz_mean_iters": float(qs["iters"].mean()),
+                          "ssz_s_all_rows_estimate": (t2 - t1) * c.N / ssz_rows,
                           "quant_s": t3 - t2, "gemm_s": t4 - t3, "dequant_s": t5 - t4}
     return {"value": gemm_ops / gemm_s / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "per layer: all weight rows, a slice of tokens (see detail) of each of the %d calibration "
-                      "batches and of the forward batch; whole path timed, GEMM share sized to ~%gs"
-                      % (args.calib_batches, args.cpu_seconds),
+            "sample": "per layer: a slice of tokens (see detail) of each of the %d calibration batches and of the "
+                      "forward batch against all weight rows (GEMM sized to ~%gs), SSZ on the first %d weight rows; "
+                      "whole path timed" % (args.calib_batches, args.cpu_seconds, ssz_rows),
             "path_seconds": path_s, "detail": detail}
 
 
