@@ -279,9 +279,11 @@ __device__ __forceinline__ void minmax_init(float lo, float hi, float qmax, floa
 }
 
 // MinMax + SSZ, symmetric (ASYM = false; qmax 127 or 7) or asymmetric int8; one row per block of TPR threads.
-// Rows it cannot certify get a NaN scale (and no other output) for k_ssz_exact.
+// Rows it cannot certify get a NaN scale (and no other output) for k_ssz_exact.  Register use is capped at two waves
+// per SIMD (256 registers): left free, the asymmetric variant takes more and runs one wave per SIMD.
 template <int DT, bool HAS_S, int BITS, bool ASYM, int TPR, int CPT>
-__global__ __launch_bounds__(TPR) void k_ssz(const void* __restrict__ w, int64_t N, int64_t K,
+__global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k_ssz(
+                                             const void* __restrict__ w, int64_t N, int64_t K,
                                              const float* __restrict__ s, int max_iter, double thr, float min_scale,
                                              float* __restrict__ scale, int32_t* __restrict__ zero_point,
                                              void* __restrict__ wq, int32_t* __restrict__ iters,

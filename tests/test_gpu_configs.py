@@ -171,6 +171,39 @@ def test_ssz_scale_all_rows_properties(pq, bits):
             assert np.all(mse[r0:r1] <= e0 * (1 + 1e-9)), f"{case.name} rows {r0}..{r1}: worse than MinMax"
 
 
+@pytest.mark.parametrize("idx", [0, 1])
+def test_opt67b_smoothed_ssz_all_rows_properties(pq, idx):
+    """Every row of the smoothed hidden-4096 weight (fc1 [16384,4096] or fc2 [4096,16384], alpha 0.5 -- the rows
+    that run the most steps: 5147 of fc1's run all 20) at full size, by the properties of the method: the floor,
+    1 to 20 steps, codes equal to the quantizer's codes of the returned scale on the folded weight, the reported
+    error equal to those codes' error, and no row worse than its MinMax start.  The smoothing factors are the
+    oracle's (the GPU's are bit-identical to them in the other tests)."""
+    case = synth.cases("opt67b")[idx]
+    w_host = case.w()
+    ax = None
+    for b in range(case.calib_batches):
+        ax = oracle.absmax_cols(synth.widen(case.x_batch(b)), ax)
+    w = synth.widen(w_host)
+    s = oracle.smooth_factors(ax, oracle.absmax_cols(w), 0.5)
+    announce(f"{case.name}: ssz_weight_qparams int8 smoothed N={case.N} K={case.K}, every row")
+    S, wq, it, mse = pq.ssz_weight_qparams(dev(w_host), dev(s), bits=8)
+    S, it, mse, codes = host(S), host(it), host(mse), host(wq)
+    assert S.min() >= np.float32(1e-5) and it.min() >= 1 and it.max() <= 20, case.name
+    for r0 in range(0, case.N, 1024):
+        r1 = min(r0 + 1024, case.N)
+        wr = oracle.fold_weight(w[r0:r1], s)
+        Sr, cr = S[r0:r1], codes[r0:r1]
+        q = np.clip(np.rint(wr / Sr[:, None]), -127, 127)
+        np.testing.assert_array_equal(q, cr, err_msg=f"{case.name} rows {r0}..{r1}: codes of the returned scale")
+        e = ((wr.astype(np.float64) - Sr.astype(np.float64)[:, None] * cr) ** 2).mean(axis=1)
+        rel = np.abs(mse[r0:r1] - e) / np.maximum(e, 1e-300)
+        assert rel.max() <= 1e-9, f"{case.name} rows {r0}..{r1}: reported error {rel.max():.2e} off"
+        S0 = np.maximum((np.abs(wr).max(axis=1) / np.float32(127)).astype(np.float32), np.float32(1e-5))
+        q0 = np.clip(np.rint(wr / S0[:, None]), -127, 127)
+        e0 = ((wr.astype(np.float64) - S0.astype(np.float64)[:, None] * q0) ** 2).mean(axis=1)
+        assert np.all(mse[r0:r1] <= e0 * (1 + 1e-9)), f"{case.name} rows {r0}..{r1}: worse than MinMax"
+
+
 @pytest.mark.parametrize("layer", [0, 31])
 def test_ssz_scale_asym(pq, layer):
     """Asymmetric int8 SSZ at full size on the 4 matrices of a layer (sampled rows on the oracle)."""
