@@ -84,10 +84,59 @@ def parse():
     p.add_argument("--oracle-single-thread", action="store_true",
                    help="only time the oracle on samples of the tiny, hidden-1024 and decode configurations and print "
                         "one JSON line (run by the default line in a child process with one OpenMP thread)")
+    p.add_argument("--probe-clock", action="store_true",
+                   help="only run the matrix-core clock probe (four kinds) and the hidden-4096 GEMMs on random and on "
+                        "zero operands, and print one JSON line")
     p.add_argument("--copy-ref", action="store_true",
                    help="only run a plain 1 GiB device copy three times (reference for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def probe_clock():
+    """The int8 matrix cores under the power limit: the probe's four kinds (shader clock and throughput with the
+    operands random, zero, or read from LDS as the GEMM does), then the fc1 and fc2 GEMMs of the hidden-4096 step
+    on random and on zero operands (same instructions and cycle count; the time ratio is the clock ratio)."""
+    import torch
+
+    import post_int8_quantization_amd as pq
+    torch.cuda.set_device(0)
+    out = {"probe": {}, "gemm": {}}
+    for kind in ("mfma16_random", "mfma32_random", "mfma16_lds_random", "mfma16_zero"):
+        for _ in range(3):  # the clock settles within a few launches
+            pq.probe_mfma(kind, iters=4000)
+        r = pq.probe_mfma(kind, iters=4000)
+        out["probe"][kind] = {"us": round(r["us"], 1), "clock_GHz": round(r["clock_GHz"], 3),
+                              "TOPS": round(r["TOPS"], 1), "frac_i8": round(r["TOPS"] * 1e12 / PEAK_I8, 3)}
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    for name, (M, N, K) in (("fc1", (4096, 16384, 4096)), ("fc2", (4096, 4096, 16384))):
+        ts = torch.rand(M, device="cuda:0", generator=g) * 0.01
+        cs = torch.rand(N, device="cuda:0", generator=g) * 0.001
+        y = torch.empty(M, N, device="cuda:0")
+        res = {}
+        for data in ("random", "zero"):
+            if data == "random":
+                xq = torch.randint(-127, 128, (M, K), device="cuda:0", dtype=torch.int8, generator=g)
+                wq = torch.randint(-127, 128, (N, K), device="cuda:0", dtype=torch.int8, generator=g)
+            else:
+                xq = torch.zeros(M, K, device="cuda:0", dtype=torch.int8)
+                wq = torch.zeros(N, K, device="cuda:0", dtype=torch.int8)
+            for _ in range(200):  # about 50 ms of back-to-back launches before timing
+                pq.w8a8_gemm_dequant(xq, wq, ts, cs, y=y)
+            t = []
+            for _ in range(20):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                pq.w8a8_gemm_dequant(xq, wq, ts, cs, y=y)
+                b.record()
+                b.synchronize()
+                t.append(a.elapsed_time(b) * 1e3)
+            t.sort()
+            med = t[len(t) // 2]
+            res[data] = {"median_us": round(med, 1), "TOPS": round(2 * M * N * K / med / 1e6, 1)}
+        res["time_ratio_random_over_zero"] = round(res["random"]["median_us"] / res["zero"]["median_us"], 3)
+        out["gemm"][name] = res
+    print(json.dumps(out), flush=True)
 
 
 def copy_reference():
@@ -243,6 +292,9 @@ def main():
         return
     if args.oracle_single_thread:
         oracle_single_thread()
+        return
+    if args.probe_clock:
+        probe_clock()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -422,6 +474,16 @@ def main():
         "graph_ms_per_step": graph_ms,
         "stages": stages, "roofline": roof,
     }
+    if wl == "opt67b":
+        # the matrix cores' throughput under the power limit, on the GEMM's instruction mix (after the timed region)
+        probe = {}
+        for kind in ("mfma16_random", "mfma16_lds_random"):
+            for _ in range(3):
+                pq.probe_mfma(kind, iters=4000)
+            r = pq.probe_mfma(kind, iters=4000)
+            probe[kind] = {"TOPS": r["TOPS"], "clock_GHz": r["clock_GHz"]}
+        stages["gemm"]["mfma_probe"] = probe
+        stages["gemm"]["frac_of_probe_lds"] = gemm_tops / probe["mfma16_lds_random"]["TOPS"]
     if wl == "opt67b" and args.alpha2 >= 0:
         out["alpha_%g" % args.alpha2] = second_alpha(torch, np, step, layers, alpha, args)
     if not args.no_cpu_baseline:

@@ -1,0 +1,52 @@
+/* ptq_probe.h -- matrix-core clock probe exported by libptq.so.
+ *
+ * A measurement aid for the int8 GEMM's roofline, not a step of the
+ * quantization method.  The published dense int8 peak of the chip assumes its
+ * 2.4 GHz top shader clock; under the board's power limit the clock that int8
+ * MFMAs on varied operands allow is lower.  This probe measures that clock and
+ * the throughput that goes with it, on the GEMM kernel's own instruction mix.
+ */
+#ifndef PTQ_PROBE_H
+#define PTQ_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define PTQ_PROBE_API __attribute__((visibility("default")))
+#else
+#define PTQ_PROBE_API
+#endif
+
+#define PTQ_PROBE_ERR_ARG 5 /* same code as PTQ_ERR_ARG */
+#define PTQ_PROBE_ERR_HIP 7 /* same code as PTQ_ERR_HIP */
+
+/* Multiply-adds per block and iteration, for every kind: 8 waves x 64 instructions of 16x16x64 (or 32 of
+ * 32x32x32) = 8 * 64 * 16 * 16 * 64; operations are twice that. */
+#define PTQ_PROBE_MACS_PER_BLOCK_ITER (8LL * 64 * 16 * 16 * 64)
+
+/* Launch the probe on `stream` (a hipStream_t, or NULL for the default stream).
+ *   kind    0: v_mfma_i32_16x16x64_i8 on pseudo-random operands
+ *           1: v_mfma_i32_32x32x32_i8 on pseudo-random operands
+ *           2: kind 0 plus the GEMM kernel's LDS operand reads (24 ds_read_b128 per 64 MFMAs per wave)
+ *           3: kind 0 with zero operands
+ *   blocks  1..65536 blocks of 512 threads (one block per CU fills the chip: 256 on MI355X)
+ *   iters   1..1000000 loop iterations
+ *   seed    operand hash seed
+ *   out     device buffer of 3*blocks uint64, 8-byte aligned, written by the kernel: per block, the shader-clock
+ *           cycles and the 100 MHz real-time ticks wave 0 spent in the loop, then a meaningless sink value.
+ *           The shader clock is cycles / (ticks * 10 ns).  Owned by the caller.
+ * Returns 0, PTQ_PROBE_ERR_ARG (nothing launched; ptq_probe_last_error() says why) or PTQ_PROBE_ERR_HIP. */
+PTQ_PROBE_API int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed, uint64_t* out, void* stream);
+
+/* Message of the last failed ptq_probe_mfma call on this thread. */
+PTQ_PROBE_API const char* ptq_probe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTQ_PROBE_H */

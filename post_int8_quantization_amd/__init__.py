@@ -17,6 +17,9 @@ Entry points (same names as the C ABI):
   sq_act_scale_ema(col_amax, s=None, momentum=0.9, first=False, state=None, rows=0) -> (state, scale, row_scale)
   weight_scale_per_tensor(col_amax, s=None, min_scale=1e-5, n=0) -> (scale[1], ch_scale[n] or None)
   quant_static_i8(x, scale, s=None, fold="div") -> (q int8, row_scale)
+
+Measurement aid (include/ptq_probe.h, not a step of the method):
+  probe_mfma(kind, blocks=256, iters=2000, seed=1) -> dict with the loop's shader clock and int8 throughput
 """
 from __future__ import annotations
 
@@ -39,7 +42,11 @@ STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE"
 
 EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
            "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant",
-           "w8a8_gemm_fused", "sq_act_scale_ema", "weight_scale_per_tensor", "quant_static_i8")
+           "w8a8_gemm_fused", "sq_act_scale_ema", "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma",
+           "ptq_probe_last_error")
+
+PROBE_KINDS = {"mfma16_random": 0, "mfma32_random": 1, "mfma16_lds_random": 2, "mfma16_zero": 3}
+PROBE_MACS_PER_BLOCK_ITER = 8 * 64 * 16 * 16 * 64
 
 
 class PtqError(RuntimeError):
@@ -69,6 +76,10 @@ def _load():
     lib.sq_act_scale_ema.argtypes = [vp, vp, i64, f32, ci, vp, vp, vp, i64, vp]
     lib.weight_scale_per_tensor.argtypes = [vp, vp, i64, f32, vp, vp, i64, vp]
     lib.quant_static_i8.argtypes = [vp, ci, i64, i64, vp, ci, vp, vp, vp, vp]
+    lib.ptq_probe_mfma.argtypes = [ci, ci, ci, ctypes.c_uint32, vp, vp]
+    lib.ptq_probe_mfma.restype = ci
+    lib.ptq_probe_last_error.argtypes = []
+    lib.ptq_probe_last_error.restype = ctypes.c_char_p
     for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
                "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused", "sq_act_scale_ema",
                "weight_scale_per_tensor", "quant_static_i8"):
@@ -355,3 +366,32 @@ def quant_static_i8(x, scale, s=None, fold="div", q=None, row_scale=None, want_r
     _check(lib.quant_static_i8(_ptr(x), _dtype_code(x), R, C, _ptr(s), FOLD[fold] if s is not None else 0,
                                _ptr(scale), _ptr(q), _ptr(row_scale), _stream(stream)))
     return q, row_scale
+
+
+def probe_mfma(kind, blocks=256, iters=2000, seed=1, stream=None):
+    """Matrix-core clock probe (include/ptq_probe.h): runs `kind` ("mfma16_random", "mfma32_random",
+    "mfma16_lds_random", "mfma16_zero" or its code) on `blocks` blocks of 512 threads and returns the elapsed
+    time, the mean shader clock wave 0 of each block saw, and the int8 throughput (2 operations per
+    multiply-add)."""
+    k = PROBE_KINDS.get(kind, kind)
+    if not isinstance(k, int):
+        raise ValueError(f"unknown probe kind {kind!r}")
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("probe_mfma takes a torch.cuda.Stream or None")
+    out = torch.zeros(3 * blocks, dtype=torch.int64, device="cuda")
+    st = _stream(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream() if stream is None else stream
+    e0.record(s)
+    rc = lib.ptq_probe_mfma(k, blocks, iters, seed, _ptr(out), st)
+    if rc != 0:
+        raise PtqError(rc, lib.ptq_probe_last_error().decode(errors="replace"))
+    e1.record(s)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    rec = out.view(blocks, 3).cpu().double()
+    cycles, ticks = rec[:, 0], rec[:, 1]
+    ops = 2.0 * PROBE_MACS_PER_BLOCK_ITER * iters * blocks
+    return {"kind": k, "us": us, "clock_GHz": float((cycles / (ticks * 10.0)).mean()),
+            "wave_cycles": float(cycles.mean()), "TOPS": ops / us / 1e6}
+

@@ -1,0 +1,171 @@
+// probe.hip -- matrix-core clock probe (a measurement aid for the GEMM's roofline, not a step of the method).
+//
+// Every block (one per CU: 512 threads, two waves per SIMD, 64 KB of LDS) issues int8 MFMAs back to back into
+// 32 independent accumulators, on operands drawn from a hash of (seed, thread, register), so consecutive
+// instructions see unrelated bytes as the GEMM's do.  Wave 0 of each block reads the shader-clock counter
+// (s_memtime) and the constant 100 MHz counter (s_memrealtime) around the loop; their ratio is the shader
+// clock the chip held while doing it.  Kinds:
+//   0  v_mfma_i32_16x16x64_i8, pseudo-random operands
+//   1  v_mfma_i32_32x32x32_i8, pseudo-random operands (the same multiply-adds per iteration)
+//   2  as 0, plus the GEMM kernel's operand traffic: 24 ds_read_b128 of pseudo-random LDS per 64 MFMAs
+//   3  as 0, all operands zero
+// The published dense int8 peak assumes the 2.4 GHz top clock; under a power limit the clock that random
+// operands allow is lower, and kinds 0 and 2 measure what the GEMM's own instruction mix can reach.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/ptq_probe.h"
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int hash3(uint32_t seed, uint32_t a, uint32_t b) {
+  uint32_t h = seed * 0x9E3779B9u ^ (a * 0x85EBCA6Bu + b * 0xC2B2AE35u + 0x27D4EB2Fu);
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  h *= 0x297A2D39u;
+  h ^= h >> 15;
+  return (int)h;
+}
+
+constexpr int kLdsChunks = 4096;  // 64 KB of 16-byte chunks
+
+template <int KIND>
+__global__ __launch_bounds__(512) void k_probe_mfma(int iters, uint32_t seed, unsigned long long* __restrict__ out) {
+  __shared__ uint4 sm[kLdsChunks];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kLdsChunks; i += 512)
+    sm[i] = make_uint4((uint32_t)hash3(seed, i, 0), (uint32_t)hash3(seed, i, 1), (uint32_t)hash3(seed, i, 2),
+                       (uint32_t)hash3(seed, i, 3));
+  __syncthreads();
+  const uint32_t t = blockIdx.x * 512u + tid;
+  int sink = 0;
+  unsigned long long c0 = 0, r0 = 0;
+  if constexpr (KIND == 1) {
+    v16i acc[4][2];
+    v4i a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[i][e] = hash3(seed, t, 16 + i * 4 + e);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[j][e] = hash3(seed, t, 64 + j * 4 + e);
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sink ^= acc[i][j][r];
+  } else {
+    v4i acc[8][4];
+    v4i a[8], b[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[i][e] = KIND == 3 ? 0 : hash3(seed, t, 16 + i * 4 + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[j][e] = KIND == 3 ? 0 : hash3(seed, t, 64 + j * 4 + e);
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+          if constexpr (KIND == 2) {
+            // the GEMM's per-wave fragment reads: an A fragment after each group, a B fragment after the first four
+            const uint4 v = sm[((wave * 8 + i) * 64 + lane + ks * 16 + it) & (kLdsChunks - 1)];
+            a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            if (i < 4) {
+              const uint4 w = sm[((wave * 4 + i) * 64 + lane + kLdsChunks / 2 + ks * 16 + it) & (kLdsChunks - 1)];
+              b[i] = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sink ^= acc[i][j][0] ^ acc[i][j][1] ^ acc[i][j][2] ^ acc[i][j][3];
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (tid == 0) {
+    out[3 * blockIdx.x] = c1 - c0;
+    out[3 * blockIdx.x + 1] = r1 - r0;
+  }
+  // keeps the accumulators live; the value itself is meaningless
+  if (lane == 0 && wave == 0) out[3 * blockIdx.x + 2] = (unsigned long long)(uint32_t)sink;
+}
+
+thread_local char g_probe_err[256] = "";
+
+}  // namespace
+
+extern "C" {
+
+const char* ptq_probe_last_error(void) { return g_probe_err; }
+
+int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed, uint64_t* out, void* stream) {
+  if (!out) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_mfma: out is required");
+    return PTQ_PROBE_ERR_ARG;
+  }
+  if (kind < 0 || kind > 3 || blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_mfma: kind=%d blocks=%d iters=%d out of range", kind, blocks,
+             iters);
+    return PTQ_PROBE_ERR_ARG;
+  }
+  if (reinterpret_cast<uintptr_t>(out) & 7u) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_mfma: out must be 8-byte aligned");
+    return PTQ_PROBE_ERR_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
+  switch (kind) {
+    case 0: k_probe_mfma<0><<<blocks, 512, 0, s>>>(iters, seed, o); break;
+    case 1: k_probe_mfma<1><<<blocks, 512, 0, s>>>(iters, seed, o); break;
+    case 2: k_probe_mfma<2><<<blocks, 512, 0, s>>>(iters, seed, o); break;
+    default: k_probe_mfma<3><<<blocks, 512, 0, s>>>(iters, seed, o); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_mfma: launch failed: %s", hipGetErrorString(e));
+    return PTQ_PROBE_ERR_HIP;
+  }
+  return 0;
+}
+
+}  // extern "C"

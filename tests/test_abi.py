@@ -6,6 +6,7 @@ either NULL or deliberately misaligned host-side integers that are never
 dereferenced because validation stops first.
 """
 import ctypes
+import glob
 import math
 import os
 import re
@@ -15,6 +16,7 @@ import pytest
 from conftest import ROOT, read_golden
 
 HEADER = os.path.join(ROOT, "include", "ptq.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 LIB = os.path.join(ROOT, "post_int8_quantization_amd", "libptq.so")
 
 OK, NULL, SHAPE, DTYPE, UNSUP, ARG, ALIGN, HIP = range(8)
@@ -54,8 +56,11 @@ def lib():
 
 
 def header_functions():
-    src = open(HEADER).read()
-    return re.findall(r"PTQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+    """Every function declared in include/*.h (PTQ_API in ptq.h, PTQ_PROBE_API in ptq_probe.h)."""
+    names = []
+    for h in HEADERS:
+        names += re.findall(r"PTQ_(?:PROBE_)?API\s+[\w\s\*]+?\b(\w+)\s*\(", open(h).read())
+    return names
 
 
 def header_define(name):
@@ -68,7 +73,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
                           "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
                           "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused", "sq_act_scale_ema",
-                          "weight_scale_per_tensor", "quant_static_i8"}
+                          "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma", "ptq_probe_last_error"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.ptq_abi_version() == int(header_define("PTQ_ABI_VERSION"))
@@ -317,3 +322,15 @@ def test_gemm_k_bound_is_the_int8_worst_case(lib):
     c = lib.w8a8_gemm_dequant
     _expect(lib, c(P, P, P, P, 4, 4, 131072, P, None, None), SHAPE, "overflow")
     _expect(lib, c(MIS, P, P, P, 4, 4, 131056, P, None, None), ALIGN)
+
+
+def test_probe_rejects_bad_arguments(lib):
+    """The clock probe validates on the host: nothing is launched for a bad kind, size, count or buffer."""
+    f = lib.ptq_probe_mfma
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ptq_probe_last_error.restype = ctypes.c_char_p
+    for args in [(4, 256, 10, 1, P), (-1, 256, 10, 1, P), (0, 0, 10, 1, P), (0, 65537, 10, 1, P), (0, 256, 0, 1, P),
+                 (0, 256, 1000001, 1, P), (0, 256, 10, 1, None), (0, 256, 10, 1, MIS)]:
+        assert f(*args, None) == ARG, args
+        assert lib.ptq_probe_last_error().decode().startswith("ptq_probe_mfma")
+
