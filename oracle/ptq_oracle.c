@@ -135,6 +135,19 @@ int o_fold_act(const float* x, const float* s, int64_t T, int64_t K, float* xh) 
   return O_OK;
 }
 
+/* Whether every folded value (x * s_j with mul, x / s_j without; x itself when s is NULL) is finite: the path
+ * requires it (a folded value that overflows has no code), and the quantizers below refuse such input with
+ * O_ENONFINITE instead of coding it. */
+static int fold_finite(const float* x, const float* s, int64_t rows, int64_t cols, int mul) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols; ++j) {
+      const float v = x[r * cols + j];
+      const float f = !s ? v : (mul ? v * s[j] : v / s[j]);
+      if (!isfinite(f)) return 0;
+    }
+  return 1;
+}
+
 /* ---------------------------------------------------------------------------
  * Linear quantization, symmetric.  [INT8] 2.1: Q = round(R/S) + Z followed by
  * saturation to the representable range; Z = 0 for symmetric quantization
@@ -151,6 +164,7 @@ static int code_of(float r, float S, int qmax) {
 
 int o_quant_row(const float* r, int64_t K, float S, int qmax, int8_t* q) {
   if (!r || !q || K <= 0 || !(S > 0.0f) || qmax <= 0 || qmax > 127) return O_EARG;
+  if (!all_finite(r, K)) return O_ENONFINITE;
   for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_of(r[k], S, qmax);
   return O_OK;
 }
@@ -281,6 +295,7 @@ int o_ssz(const float* w, const float* s, int64_t N, int64_t K, int bits, int ma
   if (bits != 8 && bits != 4) return O_EARG;
   if (max_iter < 0 || !(thr >= 0.0) || !(min_scale > 0.0f)) return O_EARG;
   if (!all_finite(w, N * K)) return O_ENONFINITE;
+  if (!fold_finite(w, s, N, K, 1)) return O_ENONFINITE;
   const int qmax = bits == 8 ? 127 : 7;
   int bad = 0;
 #pragma omp parallel
@@ -328,6 +343,7 @@ int o_ssz_variant(const float* w, const float* s, int64_t N, int64_t K, int bits
   if (bits != 8 && bits != 4) return O_EARG;
   if (max_iter < 0 || !(thr >= 0.0) || !(min_scale > 0.0f)) return O_EARG;
   if (!all_finite(w, N * K)) return O_ENONFINITE;
+  if (!fold_finite(w, s, N, K, 1)) return O_ENONFINITE;
   const int qmax = bits == 8 ? 127 : 7;
   const double scale = err_sum ? (double)K : 1.0;  /* mean -> sum */
   float* wh = (float*)malloc(sizeof(float) * (size_t)(N * K));
@@ -418,6 +434,7 @@ static int code_asym(float r, float S, int z) {
 
 int o_quant_row_asym(const float* r, int64_t K, float S, int Z, int8_t* q) {
   if (!r || !q || K <= 0 || !(S > 0.0f) || Z < O_QMIN_ASYM || Z > O_QMAX_ASYM) return O_EARG;
+  if (!all_finite(r, K)) return O_ENONFINITE;
   for (int64_t k = 0; k < K; ++k) q[k] = (int8_t)code_asym(r[k], S, Z);
   return O_OK;
 }
@@ -533,6 +550,7 @@ int o_ssz_asym(const float* w, const float* s, int64_t N, int64_t K, int max_ite
   if (!w || !S || !Z || !q || N < 0 || K <= 0) return O_EARG;
   if (max_iter < 0 || !(thr >= 0.0) || !(min_scale > 0.0f)) return O_EARG;
   if (!all_finite(w, N * K)) return O_ENONFINITE;
+  if (!fold_finite(w, s, N, K, 1)) return O_ENONFINITE;
   int bad = 0;
 #pragma omp parallel
   {
@@ -561,6 +579,7 @@ int o_ssz_asym(const float* w, const float* s, int64_t N, int64_t K, int max_ite
 int o_minmax_per_tensor(const float* w, int64_t N, int64_t K, int bits, float min_scale, float* S_out,
                         int8_t* q) {
   if (!w || !S_out || !q || N <= 0 || K <= 0 || (bits != 8 && bits != 4)) return O_EARG;
+  if (!all_finite(w, N * K)) return O_ENONFINITE;
   const int qmax = bits == 8 ? 127 : 7;
   float m = 0.0f;
   for (int64_t i = 0; i < N * K; ++i) {
@@ -602,6 +621,7 @@ int o_pack_int4(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
 int o_quant_per_token(const float* x, const float* s, int64_t T, int64_t K, int8_t* xq, float* delta) {
   if (!x || !xq || !delta || T < 0 || K <= 0) return O_EARG;
   if (!all_finite(x, T * K)) return O_ENONFINITE;
+  if (!fold_finite(x, s, T, K, 0)) return O_ENONFINITE;
   int bad = 0;
 #pragma omp parallel
   {
@@ -721,6 +741,7 @@ int o_epilogue(const int64_t* acc, int64_t M, int64_t N, const float* tok_scale,
         ((uint16_t*)out)[t * N + n] = o_bf16_rne(v);
       } else {
         float xh = next_s ? v / next_s[n] : v;
+        if (isnan(xh)) return O_ENONFINITE; /* 0 * inf or inf - inf upstream: no code */
         ((int8_t*)out)[t * N + n] = (int8_t)code_of(xh, out_scale, 127);
       }
     }
@@ -797,6 +818,7 @@ float o_weight_scale_per_tensor(float amax, float min_scale) {
 int o_quant_static(const float* x, int64_t rows, int64_t cols, const float* s, int fold, float S, int8_t* q) {
   if (!x || !q || rows < 0 || cols <= 0 || !(S > 0.0f) || fold < O_FOLD_NONE || fold > O_FOLD_MUL) return O_EARG;
   if (!all_finite(x, rows * cols)) return O_ENONFINITE;
+  if (fold != O_FOLD_NONE && !fold_finite(x, s, rows, cols, fold == O_FOLD_MUL)) return O_ENONFINITE;
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t j = 0; j < cols; ++j) q[r * cols + j] = (int8_t)code_of(fold_one(x[r * cols + j], s, j, fold), S, 127);
   return O_OK;

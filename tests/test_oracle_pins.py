@@ -833,3 +833,22 @@ def test_ssz_reading_variants_properties():
     m = oracle.ssz_variant(w, None, 8, err_sum=True)
     assert np.mean(m["iters"] >= ref["iters"]) >= 0.99
     assert m["iters"].mean() > ref["iters"].mean()
+
+
+def test_folded_overflow_is_refused():
+    """A folded value that overflows fp32 (x / s_j or w * s_j beyond the largest float) has no code: the path
+    requires finite folded values, and the oracle refuses such input instead of converting a NaN quotient."""
+    x = np.ones((2, 16), np.float32)
+    x[1, 3] = np.float32(3e38)
+    s = np.ones(16, np.float32)
+    s[3] = np.float32(0.5)
+    with pytest.raises(oracle.OracleError):
+        oracle.quant_per_token(x, s)
+    with pytest.raises(oracle.OracleError):
+        oracle.ssz(x, 1.0 / s)
+    with pytest.raises(oracle.OracleError):
+        oracle.ssz_asym(x, 1.0 / s)
+    # the same rows without the overflowing factor are accepted
+    s[3] = np.float32(1.0)
+    oracle.quant_per_token(x, s)
+    oracle.ssz(x, s)
