@@ -188,6 +188,7 @@ class Timer:
 
 
 KERNEL_SOURCES = {"k_ssz": "ssz.hip", "k_ssz_asym": "ssz.hip", "k_gemm_pipe": "gemm.hip", "k_gemm_dec": "gemm.hip",
+                  "k_gemm_dec_w": "gemm.hip",
                   "k_absmax_cols": "calib.hip", "k_tensor_scale": "calib.hip", "k_quant_tok": "quant.hip"}
 
 
@@ -630,6 +631,19 @@ def decode(args):
     def sec(name):
         return tot[name][0] / 1e3 / K
 
+    # the GEMM kernel's own duration: a burst of back-to-back launches (over the three weight copies, so no
+    # launch finds its weights in a cache) between two events on the launch stream -- the host stays ahead of
+    # the GPU, so no host gap enters, unlike the per-stage events of the eager steps above
+    burst = 30
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    eb0.record()
+    for i in range(burst):
+        pq.w8a8_gemm_dequant(xq, wqs[i % len(wqs)], d, S, y=y, stream=None)
+    eb1.record()
+    torch.cuda.synchronize()
+    burst_s = eb0.elapsed_time(eb1) / 1e3 / burst
+
     gemm_ops = 2 * c.T * c.N * c.K
     gemm_bytes = c.T * c.K + c.N * c.K + 4 * c.T + 4 * c.N + 4 * c.T * c.N
     quant_bytes = c.T * c.K * 2 + c.T * c.K + c.T * 4 + c.K * 4
@@ -638,14 +652,17 @@ def decode(args):
         "quant": {"ms": sec("quant") * 1e3, "GB/s": quant_bytes / sec("quant") / 1e9,
                   "frac_hbm": quant_bytes / sec("quant") / PEAK_HBM},
         "gemm": {"ms": gemm_s * 1e3, "TOPS": gemm_ops / gemm_s / 1e12, "GB/s": gemm_bytes / gemm_s / 1e9,
-                 "frac_hbm": gemm_bytes / gemm_s / PEAK_HBM},
+                 "frac_hbm": gemm_bytes / gemm_s / PEAK_HBM, "burst_ms": burst_s * 1e3,
+                 "burst_GB/s": gemm_bytes / burst_s / 1e9, "burst_frac_hbm": gemm_bytes / burst_s / PEAK_HBM},
     }
-    roof = {"kernel": "k_gemm_dec", "bound": "hbm", "achieved": gemm_bytes / gemm_s / 1e9, "peak": PEAK_HBM / 1e9,
-            "unit": "GB/s", "per_launch_bytes": gemm_bytes}
+    roof = {"kernel": "k_gemm_dec_w", "bound": "hbm", "achieved": gemm_bytes / burst_s / 1e9, "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s", "per_launch_bytes": gemm_bytes,
+            "timing": f"burst of {burst} back-to-back launches between two events (kernel time, no host gaps)"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = load_counters("k_gemm_dec", "decode")
+    rec = load_counters("k_gemm_dec_w", "decode")
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
-    roof["avg_launch_us"] = tot["gemm"][0] * 1e3 / tot["gemm"][1]
+    roof["avg_launch_us"] = burst_s * 1e6
+    roof["eager_stage_avg_us"] = tot["gemm"][0] * 1e3 / tot["gemm"][1]
     out = {
         "metric": METRIC, "value": gemm_ops / gemm_s / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak",

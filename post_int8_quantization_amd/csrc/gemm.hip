@@ -718,6 +718,143 @@ __global__ __launch_bounds__(KS * 64) void k_gemm_dec(const int8_t* __restrict__
   }
 }
 
+// Decode with at most 16 tokens and K = 1024*KW: persistent blocks of KW waves walk groups of 16 weight rows
+// (group g = blockIdx.x + i*gridDim.x, at most kDecGroups per block); wave w owns bytes [1024w, 1024w + 1024) of
+// K.  The wave's slice of the token rows is loaded once and kept in registers in the MFMA operand layout; its
+// slice of each group's weight rows (16 rows x 1 KB) arrives with 16 loads of 8 rows x 128 B (whole cache
+// lines), issued one group ahead so that 16 KB per wave stay in flight, and is transposed through the wave's LDS
+// area.  The waves never wait for each other while streaming: each adds its int32 partial tile into the group's
+// LDS accumulator (integer atomics, exact in any order).  After one barrier at the end the waves run the
+// epilogues of the block's tiles, with the per-column inputs staged in LDS at the start.  Loads of groups past
+// the end and of rows past N or M read zeros through the range-checked descriptors, so every wave issues the
+// same loads and the wait counts are static.
+template <int KW>
+__device__ __forceinline__ void load_rows16(uint4 (&d)[16], const int8_t* __restrict__ base, uint32_t bytes,
+                                            int K, int kb, int lrow, int lch) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = i & 1, sl = i >> 1;
+    const uint32_t off = (uint32_t)((h * 8 + lrow) * K + kb + sl * 128 + lch * 16);
+    d[i] = buf_load16_once(buf_rsrc(base, bytes), off);
+  }
+}
+
+// 16 rows x 1 KB in the load layout -> the wave's LDS area (8 slabs of 128 slots)
+__device__ __forceinline__ void stage_rows16(uint4* ws, const uint4 (&d)[16], int lrow, int lch) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ws[(i >> 1) * 128 + slab_slot((i & 1) * 8 + lrow, lch)] = d[i];
+}
+
+// the MFMA operand of 64-k step q (0..15): row mrow, bytes q*64 + mg*16 of the slice
+__device__ __forceinline__ uint4 mfma_piece(const uint4* ws, int q, int mrow, int mg) {
+  return ws[(q >> 1) * 128 + slab_slot(mrow, (q & 1) * 4 + mg)];
+}
+
+// groups of 16 weight rows per block (LDS accumulators of 1 KB each): 8 waves keep 128 KB of transpose
+// areas beside 24 tiles (one block per CU); 4 waves 64 KB beside 12 (two blocks per CU)
+template <int KW>
+struct DecW {
+  static constexpr int kGroups = KW == 8 ? 24 : 12;
+  static constexpr int kBlocks = KW == 8 ? 256 : 512;
+};
+
+template <int KW, int OUT>
+__global__ __launch_bounds__(KW * 64) void k_gemm_dec_w(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                       const float* __restrict__ ts, const float* __restrict__ cs,
+                                                       int M, int N, int K, void* __restrict__ Y,
+                                                       int32_t* __restrict__ ACC, Epi epi, int groups) {
+  constexpr int NG = DecW<KW>::kGroups;
+  __shared__ uint4 tr[KW][1024];    // per-wave transpose area: 16 rows x 1 KB
+  __shared__ int tile[NG][4][64];   // the block's int32 tiles: [group][fragment row][lane]
+  __shared__ float col[3][NG][16];  // per-column scale, bias, next-layer factor of the block's groups
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane >> 3, lch = lane & 7;  // load layout
+  const int mrow = lane & 15, mg = lane >> 4;  // MFMA layout
+  const int kb = wave * 1024;
+  uint4* ws = tr[wave];
+  const int G = gridDim.x;
+  const int mine = blockIdx.x < groups ? (groups - 1 - blockIdx.x) / G + 1 : 0;  // this block's groups (<= NG)
+  static_assert(NG * 16 <= KW * 64, "one column input per thread");
+  uint4 b0[16], b1[16], a[16];
+
+  auto load_group = [&](int g, uint4 (&d)[16]) {
+    const bool live = g < groups;
+    const int n0 = live ? g * 16 : 0;
+    const int rows = live ? (N - n0 < 16 ? N - n0 : 16) : 0;
+    load_rows16<KW>(d, B + (int64_t)n0 * K, (uint32_t)rows * (uint32_t)K, K, kb, lrow, lch);
+  };
+  // group i of the block: transpose the slice, 16 MFMAs, add the partial tile into the group's accumulator
+  auto group = [&](const uint4 (&d)[16], int i) {
+    stage_rows16(ws, d, lrow, lch);
+    wave_sync_lds();
+    v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc = mfma16(a[q], mfma_piece(ws, q, mrow, mg), acc);
+    wave_sync_lds();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) atomicAdd(&tile[i][r][lane], acc[r]);
+  };
+
+  // in flight before any wait: the first group's rows, the token slice, the epilogue inputs, the second group
+  load_group(blockIdx.x, b0);
+  load_rows16<KW>(a, A, (uint32_t)M * (uint32_t)K, K, kb, lrow, lch);
+  const int r = wave & 3;          // the fragment row this wave finishes in the epilogues
+  const int m = mg * 4 + r;
+  const float tsm = __uint_as_float(
+      __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(ts, (uint32_t)M * 4u), m * 4, 0, 0));
+  const int ci = tid < mine * 16 ? tid : 0;  // the column input this thread stages (mine * 16 <= 384 < threads)
+  const int cn = (blockIdx.x + (ci >> 4) * G) * 16 + (ci & 15);
+  const uint32_t cb = tid < mine * 16 && cn < N ? 4u : 0u;
+  const float c_cs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(cs + cn, cb), 0, 0, 0));
+  const float c_b = epi.bias ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(epi.bias + cn, cb), 0, 0, 0))
+                             : 0.0f;
+  float c_ns = 1.0f;
+  if constexpr (OUT == EPI_I8)
+    if (epi.next_s && cb) c_ns = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(epi.next_s + cn, cb), 0, 0, 0));
+  load_group(blockIdx.x + G, b1);
+  for (int i = tid; i < NG * 4 * 64; i += KW * 64) (&tile[0][0][0])[i] = 0;
+  // the token slice into the MFMA layout (rows past M read zeros)
+  stage_rows16(ws, a, lrow, lch);
+  wave_sync_lds();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) a[q] = mfma_piece(ws, q, mrow, mg);
+  wave_sync_lds();
+  __syncthreads();  // accumulators zeroed
+
+  for (int i = 0; i < mine; i += 2) {
+    group(b0, i);
+    load_group(blockIdx.x + (i + 2) * G, b0);
+    if (i + 1 >= mine) break;
+    group(b1, i + 1);
+    load_group(blockIdx.x + (i + 3) * G, b1);
+  }
+  if (tid < mine * 16) {
+    col[0][tid >> 4][tid & 15] = c_cs;
+    col[1][tid >> 4][tid & 15] = c_b;
+    col[2][tid >> 4][tid & 15] = cb ? c_ns : 1.0f;
+  }
+  __syncthreads();  // every wave's partials and the column inputs are in
+
+  // epilogues: wave w finishes fragment row w & 3 of the tiles i = (w >> 2), (w >> 2) + KW/4, ...
+  const float os = OUT == EPI_I8 ? epi.out_scale[0] : 1.0f;
+  for (int i = wave >> 2; i < mine; i += KW / 4) {
+    const int n = (blockIdx.x + i * G) * 16 + mrow;
+    if (n < N && m < M) {
+      const int sum = tile[i][r][lane];
+      const float csn = col[0][i][mrow], bn = col[1][i][mrow], ns = col[2][i][mrow];
+      const EpiDiv dv{ns, 1.0f / ns, os, 1.0f / os};
+      const bool ieee = OUT == EPI_I8 && !(next_s_ok(ns) && out_scale_ok(os));
+      const float v = (float)sum * (tsm * csn);
+      if (OUT == EPI_I8 && ieee)
+        epi_store<OUT, false, EM_RUNTIME + EM_IEEE>(Y, (int64_t)m * N + n, v, bn, dv, epi);
+      else
+        epi_store<OUT, false>(Y, (int64_t)m * N + n, v, bn, dv, epi);
+      if (ACC) ACC[(int64_t)m * N + n] = sum;
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, int OUT>
 hipError_t launch_tiled(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
                         void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
@@ -738,11 +875,28 @@ hipError_t launch_dec(const int8_t* xq, const int8_t* wq, const float* ts, const
   return hipGetLastError();
 }
 
+template <int KW, int OUT>
+hipError_t launch_dec_w(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int M, int N, int K,
+                        void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
+  const int groups = (N + 15) / 16;
+  // one block per CU at 8 waves, two at 4; more blocks (in rounds) once a block would exceed its tile count
+  const int need = (groups + DecW<KW>::kGroups - 1) / DecW<KW>::kGroups;
+  const int cap = need > DecW<KW>::kBlocks ? need : DecW<KW>::kBlocks;
+  const int blocks = groups < cap ? groups : cap;
+  k_gemm_dec_w<KW, OUT><<<(unsigned)blocks, KW * 64, 0, stream>>>(xq, wq, ts, cs, M, N, K, y, acc, epi, groups);
+  return hipGetLastError();
+}
+
 template <int OUT>
 hipError_t dispatch_gemm(const int8_t* xq, const int8_t* wq, const float* ts, const float* cs, int64_t M, int64_t N,
                          int64_t K, void* y, int32_t* acc, const Epi& epi, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (M <= 16) return launch_dec<1, 1, 8, false, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  if (M <= 16) {
+    // K of 4 or 8 KB: persistent streaming blocks (one weight-row group ahead in flight)
+    if (K == 8192) return launch_dec_w<8, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+    if (K == 4096) return launch_dec_w<4, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+    return launch_dec<1, 1, 8, false, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
+  }
   if (M <= 32) return launch_dec<2, 1, 8, false, OUT>(xq, wq, ts, cs, m, n, k, y, acc, epi, stream);
   if (M <= 64) {
     // 64 channels per block re-read the token rows 4x less often, once that still fills the CUs

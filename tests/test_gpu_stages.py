@@ -267,6 +267,17 @@ def test_gemm_dequant(pq, M, N, K):
     assert_y(host(y), y_ref, f"y {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,act,out,want_acc", [
+    (1, 1, 4096, "none", "f32", True), (5, 17, 4096, "relu", "bf16", False), (16, 4096, 4096, "gelu", "i8", False),
+    (16, 9000, 4096, "none", "f32", True), (2, 16, 8192, "none", "i8", True), (16, 4100, 8192, "relu", "f32", False),
+    (13, 28672, 8192, "none", "f32", True), (16, 28688, 8192, "gelu", "bf16", True)])
+def test_gemm_decode_streaming(pq, M, N, K, act, out, want_acc):
+    """The streaming decode kernel (at most 16 tokens, K of 4 or 8 KB): persistent blocks over groups of 16
+    weight rows -- one group, fewer groups than blocks, more (ragged last group, blocks taking one or two more
+    groups), the full decode shape -- every output type, against the oracle."""
+    _fused_case(pq, M, N, K, act, out, want_acc, M * 31 + N + K)
+
+
 def test_gemm_max_k_extremes(pq):
     """K = 131056 (the largest multiple of 16 with 2^14 K < 2^31) with all-extreme codes, -128 included: exact
     int32 at the largest magnitudes any int8 codes reach (+2^14 K and -127 * 128 K)."""
