@@ -81,10 +81,7 @@ struct Decision {
 // [fl64(b.lo - c.hi), fl64(b.hi - c.lo)] and the quotient between the quotients of the end points.  The
 // relative test matters only when best > 0 (best == 0 converges anyway).  On points the result is the plain
 // rule and test.
-__device__ __forceinline__ Decision decide(Ival b, Ival c, double thr) {
-  Decision r;
-  r.keep = c.hi < b.lo ? kYes : (c.lo >= b.hi ? kNo : kUnk);
-  const double dlo = b.lo - c.hi, dhi = b.hi - c.lo;
+__device__ __forceinline__ int conv_of(Ival b, double dlo, double dhi, double thr) {
   const int z = b.hi == 0.0 ? kYes : (b.lo > 0.0 ? kNo : kUnk);
   const int ab = (dlo > -thr && dhi < thr) ? kYes : ((dlo >= thr || dhi <= -thr) ? kNo : kUnk);
   int rel;
@@ -98,7 +95,13 @@ __device__ __forceinline__ Decision decide(Ival b, Ival c, double thr) {
     const double fmin = dlo >= 0.0 ? dlo / b.hi : (b.lo > 0.0 ? dlo / b.lo : -inf);
     rel = fmax < thr ? kYes : (fmin >= thr ? kNo : kUnk);
   }
-  r.conv = tri_or(z, tri_or(ab, rel));
+  return tri_or(z, tri_or(ab, rel));
+}
+
+__device__ __forceinline__ Decision decide(Ival b, Ival c, double thr) {
+  Decision r;
+  r.keep = c.hi < b.lo ? kYes : (c.lo >= b.hi ? kNo : kUnk);
+  r.conv = conv_of(b, b.lo - c.hi, b.hi - c.lo, thr);
   return r;
 }
 
@@ -129,6 +132,31 @@ __device__ __forceinline__ Ival err_ival(double w2, float S, double P, double R2
   const double bnd = hu * ((w2 + 2.0 * Sd * P) + s2);
   const double lo = e - bnd, hi = e + bnd;
   return Ival{per_elem(lo > 0.0 ? lo : 0.0), per_elem(hi > 0.0 ? hi : 0.0)};
+}
+
+// A candidate S1 whose pass sums P and R2 equal the kept scale S0's (the same codes, or codes with the same two
+// sums) has the same error function e(S) = (W2 - 2 S P + S^2 R2) / K, so the difference of the two errors is
+//   e(S0) - e(S1) = (S0 - S1) (R2 (S0 + S1) - 2 P) / K,
+// free of the cancellation against W2 that widens the expansion's intervals -- such candidates differ from the
+// kept error by as little as 1e-11 relative when S1 is S0's neighbour.  With S1 in [S0/2, 2 S0] and R2 < 2^27,
+// S0 - S1, S0 + S1, R2 (S0 + S1) and 2 P are exact, so the computed difference d carries three or four roundings
+// (relative error below 8u).  The oracle's own fl64(best - cur), of its two rounded errors, lies within
+// 2^-51 (best + |d|) of the exact difference.  The decisions follow from d, and the candidate's error interval
+// from the kept one.  Returns false (nothing decided) outside those conditions.
+__device__ __forceinline__ bool same_sums_decide(float S0, float S1, double P, double R2, Ival best, double thr,
+                                                 const DivK& per_elem, Decision& dc, Ival& cur) {
+  if (!(R2 < 0x1p27) || !(S1 >= 0.5f * S0 && S1 <= 2.0f * S0)) return false;
+  const double s0 = (double)S0, s1 = (double)S1;
+  const double t = R2 * (s0 + s1) - 2.0 * P;
+  const double d = per_elem((s0 - s1) * t);
+  const double ad = __builtin_fabs(d);
+  const double ed = 8.0 * kU * ad;                        // the exact difference is within d +- ed
+  const double eo = ed + 0x1p-50 * (best.hi + ad);        // the oracle's difference is within d +- eo
+  dc.keep = d - eo > 0.0 ? kYes : (d <= 0.0 ? kNo : kUnk);  // d has the exact difference's sign
+  dc.conv = conv_of(best, d - eo, d + eo, thr);
+  const double clo = best.lo - (d + eo), chi = best.hi - (d - eo);
+  cur = Ival{clo > 0.0 ? clo : 0.0, chi > 0.0 ? chi : 0.0};
+  return true;
 }
 
 // 2^(E + 27), E the binary exponent of a normal S: a computed P below it is exact (see the file header)
@@ -431,7 +459,13 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
       c.best = err_ival(w2, Sc, c.P, c.R2, hu, per_elem);
       c.best = Ival{uni(c.best.lo), uni(c.best.hi)};
-      const Decision dc = decide(st.best, c.best, thr);
+      Decision dc = decide(st.best, c.best, thr);
+      if ((dc.keep == kUnk || dc.conv == kUnk) && c.P == st.P && c.R2 == st.R2) {
+        // (wave-uniform: the sums are) the kept codes' sums again: decide from the exact difference instead
+        Ival cs;
+        if (same_sums_decide(st.S, Sc, st.P, st.R2, st.best, thr, per_elem, dc, cs))
+          c.best = Ival{uni(cs.lo), uni(cs.hi)};
+      }
       if (dc.keep == kUnk || dc.conv == kUnk) {
         ok = false;
         break;
@@ -613,8 +647,12 @@ __global__ __launch_bounds__(kWave) void k_ssz_rows(const void* __restrict__ w, 
         ok = false;
         active = false;
       }
-      const Ival cur = err_ival(w2, Sc, Pc, R2c, hu, per_elem);
-      const Decision dc = decide(best, cur, thr);
+      Ival cur = err_ival(w2, Sc, Pc, R2c, hu, per_elem);
+      Decision dc = decide(best, cur, thr);
+      if ((dc.keep == kUnk || dc.conv == kUnk) && Pc == P && R2c == R2) {
+        Ival cs;
+        if (same_sums_decide(S, Sc, P, R2, best, thr, per_elem, dc, cs)) cur = cs;
+      }
       if (active && (dc.keep == kUnk || dc.conv == kUnk)) {
         ok = false;
         active = false;

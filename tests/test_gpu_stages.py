@@ -709,6 +709,64 @@ def test_ssz_deferred_wide_uniform_rows(pq, K):
     compare_ssz_asym(host(Sa), host(Za), host(qa), host(ita), host(ma), ra, f"asym wide uniform K={K}")
 
 
+def _near_grid_rows(rng, N, K, qmax, noise, asym=False):
+    """Rows fl32(S (q + noise u)) on a random grid S (not a power of two) with integer codes q that reach the end
+    of the range: the least-squares refit of the MinMax scale lands on the same codes, often one or two ulps
+    away, so the candidate's pass sums equal the kept ones and the two errors differ by ~1e-11 relative or
+    less.  asym: codes over [-128, 127] with a random offset."""
+    S = rng.uniform(0.003, 0.03, N)
+    lo, hi = (-128, 127) if asym else (-qmax, qmax)
+    q = rng.integers(lo, hi + 1, (N, K)).astype(np.float64)
+    q[:, 0] = hi
+    q[:, 1] = lo
+    if asym:
+        q -= rng.integers(-40, 41, (N, 1))
+    u = rng.uniform(-1.0, 1.0, (N, K))
+    return (S[:, None] * (q + noise * u)).astype(np.float32)
+
+
+def _same_sums_rows(w, qmax, min_scale=1e-5):
+    """Rows whose first refit keeps the MinMax codes under a different scale (oracle helpers only)."""
+    n = 0
+    for row in w:
+        S0 = max(np.float32(np.max(np.abs(row)) / np.float32(qmax)), np.float32(min_scale))
+        q0 = oracle.quant_row(row, S0, qmax)
+        S1 = max(np.float32(oracle.lsq_scale(row, q0)), np.float32(min_scale))
+        n += int(S1 != S0 and np.array_equal(oracle.quant_row(row, S1, qmax), q0))
+    return n
+
+
+@pytest.mark.parametrize("K", [48, 320, 1024, 4096, 16384])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_ssz_same_codes_candidates(pq, K, bits):
+    """Candidates with the kept codes under a neighbouring scale: the two errors share one quadratic, and the
+    decision between them is taken from its exact difference (on every row as the oracle decides it)."""
+    qmax = 127 if bits == 8 else 7
+    rng = np.random.default_rng(K * 5 + bits)
+    N = 96
+    w = np.concatenate([_near_grid_rows(rng, N // 4, K, qmax, noise) for noise in (0.0, 1e-6, 1e-4, 1e-2)])
+    assert _same_sums_rows(w, qmax) >= N // 4, "the rows do not exercise same-codes candidates"
+    s = np.exp(rng.uniform(-0.5, 0.5, K)).astype(np.float32)
+    for smooth in (False, True):
+        # smoothing: the folded rows fl32(w s) sit on the grid again (the division by s undone)
+        wi = (w / s).astype(np.float32) if smooth else w
+        ref = oracle.ssz(wi, s if smooth else None, bits)
+        announce(f"ssz_weight_qparams same-codes candidates K={K} int{bits} smooth={smooth}")
+        S, wq, it, mse = pq.ssz_weight_qparams(dev(wi), dev(s) if smooth else None, bits=bits)
+        codes = host(wq) if bits == 8 else unpack_int4(host(wq))
+        compare_ssz(host(S), codes, host(it), host(mse), ref, f"same codes K={K} int{bits} smooth={smooth}")
+
+
+@pytest.mark.parametrize("K", [64, 1024, 4096])
+def test_ssz_asym_same_codes_candidates(pq, K):
+    rng = np.random.default_rng(K * 7)
+    w = np.concatenate([_near_grid_rows(rng, 16, K, 127, noise, asym=True) for noise in (0.0, 1e-6, 1e-4)])
+    ref = oracle.ssz_asym(w, None)
+    announce(f"ssz_weight_qparams_asym same-codes candidates K={K}")
+    S, Z, wq, it, mse = pq.ssz_weight_qparams_asym(dev(w), None)
+    compare_ssz_asym(host(S), host(Z), host(wq), host(it), host(mse), ref, f"asym same codes K={K}")
+
+
 @pytest.mark.parametrize("T,K", [(40, 64), (33, 1040), (24, 4096), (9, 16384)])
 @pytest.mark.parametrize("smooth", ["none", "ok", "tiny_s"])
 def test_quant_per_token_domain_edges(pq, T, K, smooth):
