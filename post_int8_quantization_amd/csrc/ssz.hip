@@ -437,41 +437,52 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
     st.best = Ival{uni(st.best.lo), uni(st.best.hi)};
 
     // least-squares refits, greedy, per-row convergence
-    int it = 0;
-    for (int i = 1; ok && i <= max_iter; ++i) {
-      it = i;
-      float Sc;
-      int Zc;
-      if (!refit<ASYM>(st, Kd, w1, per_elem, min_scale, Sc, Zc)) break;
-      if (Sc == st.S && Zc == st.Z) {
-        // the kept parameters again: the same codes and error, d = 0
-        if (thr > 0.0 || st.best.hi == 0.0) break;
-        if (st.best.lo > 0.0) it = max_iter;  // thr == 0, best > 0: the same candidate at every remaining step
-        else ok = false;
-        break;
+    int it = 0, i = 1;
+    RowState c;  // the last candidate
+    for (;;) {
+      bool open = false;  // the intervals left the last candidate's decision open
+      for (; ok && i <= max_iter; ++i) {
+        it = i;
+        float Sc;
+        int Zc;
+        if (!refit<ASYM>(st, Kd, w1, per_elem, min_scale, Sc, Zc)) break;
+        if (Sc == st.S && Zc == st.Z) {
+          // the kept parameters again: the same codes and error, d = 0
+          if (thr > 0.0 || st.best.hi == 0.0) break;
+          if (st.best.lo > 0.0) it = max_iter;  // thr == 0, best > 0: the same candidate at every remaining step
+          else ok = false;
+          break;
+        }
+        c.S = Sc;
+        c.Z = Zc;
+        if (!pass(Sc, Zc, c.P, c.R2, c.R1)) {
+          ok = false;
+          break;
+        }
+        c.best = err_ival(w2, Sc, c.P, c.R2, hu, per_elem);
+        c.best = Ival{uni(c.best.lo), uni(c.best.hi)};
+        const Decision dc = decide(st.best, c.best, thr);
+        if (dc.keep == kUnk || dc.conv == kUnk) {
+          open = true;
+          break;
+        }
+        if (dc.keep == kYes) st = c;
+        if (dc.conv == kYes) break;
       }
-      RowState c;
-      c.S = Sc;
-      c.Z = Zc;
-      if (!pass(Sc, Zc, c.P, c.R2, c.R1)) {
+      if (!open) break;
+      // (off the loop, so the common path stays as it is) a candidate with the kept codes' sums again: decide
+      // from the exact difference of the two errors, then go on with the next step
+      Decision dc;
+      Ival cs;
+      if (!(c.P == st.P && c.R2 == st.R2 && same_sums_decide(st.S, c.S, st.P, st.R2, st.best, thr, per_elem, dc, cs)) ||
+          dc.keep == kUnk || dc.conv == kUnk) {
         ok = false;
         break;
       }
-      c.best = err_ival(w2, Sc, c.P, c.R2, hu, per_elem);
-      c.best = Ival{uni(c.best.lo), uni(c.best.hi)};
-      Decision dc = decide(st.best, c.best, thr);
-      if ((dc.keep == kUnk || dc.conv == kUnk) && c.P == st.P && c.R2 == st.R2) {
-        // (wave-uniform: the sums are) the kept codes' sums again: decide from the exact difference instead
-        Ival cs;
-        if (same_sums_decide(st.S, Sc, st.P, st.R2, st.best, thr, per_elem, dc, cs))
-          c.best = Ival{uni(cs.lo), uni(cs.hi)};
-      }
-      if (dc.keep == kUnk || dc.conv == kUnk) {
-        ok = false;
-        break;
-      }
+      c.best = Ival{uni(cs.lo), uni(cs.hi)};
       if (dc.keep == kYes) st = c;
       if (dc.conv == kYes) break;
+      ++i;
     }
 
     if (!ok) {
