@@ -222,9 +222,10 @@ __device__ __forceinline__ void quant_row(uint4 (&raw)[CPT][Piece<DT>::P], const
 }
 
 // Grid-stride over rows with D rows in flight: slot d of the register ring is
-// refilled with the row D strides ahead as soon as its row is quantized.  A
-// block walks whole rounds of D rows; the rows of a round past T are no-ops
-// (zero-length descriptors).
+// refilled with the row D strides ahead as soon as its row is quantized (a
+// row past T loads nothing: zero-length descriptor).  A block stops at its
+// first row past T, so a last round with fewer rows costs no work for the
+// missing ones.
 // STATIC: one given scale (scale[0]) for every row, as a per-tensor static quantization.  FOLD_MUL folds by
 // s_j (the weight side, fl32(x * s_j)), FOLD_DIV by fl32(x / s_j) (the activation side).
 template <int DT, int FOLD, int TPR, int CPT, int D, bool STATIC>
@@ -293,6 +294,7 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int64_t t = base + d * G;
+      if (t >= T) break;  // block-uniform: the round's remaining rows, and every later one, are past T
       quant_row<DT, FOLD, TPR, CPT, STATIC>(
           ring[d], cf, cols_ok, x, t, T, K, tid, xq, tok_scale, red, parity, static_delta, static_inv,
           [&](uint4 (&slot)[CPT][P]) { load_raw<DT, TPR, CPT>(x, t + D * G, T, K, tid, slot); });
