@@ -18,8 +18,8 @@ namespace ptq {
 
 namespace {
 
-constexpr int kWaves = 4;                // waves per block
-constexpr int kThreads = kWaves * kWave;  // 256
+constexpr int kWaves = 4;                // waves per block (default)
+constexpr int64_t kMaxRowBlocks = 64;     // row blocks per column strip (atomics per column)
 constexpr int kVecs = kWave;              // 16-byte vector columns per block strip
 constexpr int kBatch = 8;                 // row loads per batch; two batches in flight per lane
 
@@ -48,17 +48,17 @@ __device__ __forceinline__ void fold_max(float (&m)[Vec<DT>::kElems], const uint
 // current one is folded.  Rows are read through per-row range-checked descriptors, so rows past
 // the wave's run and lanes past the row's end read zeros (neutral for a max of magnitudes) with no
 // branch around any load.
-template <int DT, int KB = kBatch>
-__global__ __launch_bounds__(kThreads) void k_absmax_cols(const uint4* __restrict__ x, int64_t rows,
+template <int DT, int NWV = kWaves, int KB = kBatch>
+__global__ __launch_bounds__(NWV* kWave) void k_absmax_cols(const uint4* __restrict__ x, int64_t rows,
                                                          int64_t vecs_per_row, int64_t rows_per_block,
                                                          unsigned* __restrict__ amax_bits) {
   constexpr int E = Vec<DT>::kElems;
-  __shared__ float red[kWaves][kVecs * E];
+  __shared__ float red[NWV][kVecs * E];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: row descriptors in SGPRs
   const int64_t v = (int64_t)blockIdx.x * kVecs + lane;
-  const int64_t per_wave = (rows_per_block + kWaves - 1) / kWaves;
+  const int64_t per_wave = (rows_per_block + NWV - 1) / NWV;
   const int64_t b0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t b1 = b0 + rows_per_block < rows ? b0 + rows_per_block : rows;
   const int64_t r0 = b0 + wave * per_wave;
@@ -93,10 +93,10 @@ __global__ __launch_bounds__(kThreads) void k_absmax_cols(const uint4* __restric
 #pragma unroll
   for (int e = 0; e < E; ++e) red[wave][lane * E + e] = m[e];
   __syncthreads();
-  for (int c = tid; c < kVecs * E; c += kThreads) {
+  for (int c = tid; c < kVecs * E; c += NWV * kWave) {
     float mm = red[0][c];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, red[w][c]);
+    for (int w = 1; w < NWV; ++w) mm = fmaxf(mm, red[w][c]);
     const int64_t vcol = (int64_t)blockIdx.x * kVecs + c / E;
     if (vcol < vecs_per_row) atomicMax(amax_bits + vcol * E + (c % E), __float_as_uint(mm));
   }
@@ -187,20 +187,22 @@ hipError_t launch_absmax_cols(const void* x, int dtype, int64_t rows, int64_t co
   const int64_t vecs = cols / E;
   const int64_t gx = (vecs + kVecs - 1) / kVecs;
   // 2 (tall matrices) to 4 blocks per CU (256 CUs) and at least one row per wave; tall matrices stream
-  // better from fewer, longer row runs (measured: 6.4-6.6 vs 6.2 TB/s on a 1 GB bf16 stack)
+  // better from fewer, longer row runs (measured: 6.4-6.6 vs 6.2 TB/s on a 1 GB bf16 stack).  At most 64 row
+  // blocks: each adds one atomic per column, and more of them queue on the same addresses -- narrow or short
+  // matrices (1024-wide activations, 1024-4096-row weights) ran 1.1-2.3x slower at 128-512 row blocks than at 64
   const int64_t target = rows >= 16384 ? 512 : 1024;
   int64_t gy = (target + gx - 1) / gx;
   const int64_t max_gy = (rows + kWaves - 1) / kWaves;
   if (gy > max_gy) gy = max_gy;
-  if (gy > 65535) gy = 65535;
+  if (gy > kMaxRowBlocks) gy = kMaxRowBlocks;
   const int64_t rows_per_block = (rows + gy - 1) / gy;
   gy = (rows + rows_per_block - 1) / rows_per_block;
   dim3 grid((unsigned)gx, (unsigned)gy);
   if (dtype == PTQ_BF16)
-    k_absmax_cols<PTQ_BF16><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
+    k_absmax_cols<PTQ_BF16><<<grid, kWaves * kWave, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
                                                             rows_per_block, reinterpret_cast<unsigned*>(amax));
   else
-    k_absmax_cols<PTQ_F32><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
+    k_absmax_cols<PTQ_F32><<<grid, kWaves * kWave, 0, stream>>>(reinterpret_cast<const uint4*>(x), rows, vecs,
                                                            rows_per_block, reinterpret_cast<unsigned*>(amax));
   return hipGetLastError();
 }
