@@ -150,6 +150,23 @@ def copy_reference():
     print(json.dumps({"copy_reference_bytes": n, "repeats": 3}), flush=True)
 
 
+def hbm_probe(torch, pq, nbytes=1 << 31, reps=5):
+    """The measured HBM peak beside the datasheet's: the stream probe's plain streaming reads of `nbytes` (eight
+    times the 256 MB last-level cache) and its copy of half of them, each the median of `reps` launches after two
+    warm-up launches.  Rates in GB/s of bytes moved (a copy counts its reads and its writes)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda:0")
+    out = {}
+    for kind, a, b in (("read", src, None), ("copy", src[: nbytes // 2], dst)):
+        for _ in range(2):
+            pq.probe_stream(kind, a, b)
+        rates = sorted(pq.probe_stream(kind, a, b)["GBps"] for _ in range(reps))
+        out[kind + "_GBps"] = rates[reps // 2]
+    del src, dst
+    out["bytes"] = nbytes
+    return out
+
+
 class Timer:
     """HIP events on the current stream around named stages."""
 
@@ -485,6 +502,17 @@ def main():
             probe[kind] = {"TOPS": r["TOPS"], "clock_GHz": r["clock_GHz"]}
         stages["gemm"]["mfma_probe"] = probe
         stages["gemm"]["frac_of_probe_lds"] = gemm_tops / probe["mfma16_lds_random"]["TOPS"]
+    # the measured HBM peak (after the timed region): the memory-bound stages against it as well as the datasheet
+    hp = hbm_probe(torch, pq)
+    out["hbm_probe"] = hp
+    for nm in ("calib_x", "calib_w"):
+        stages[nm]["frac_of_read_probe"] = stages[nm]["GB/s"] * 1e9 / (hp["read_GBps"] * 1e9)
+        if stages[nm].get("graph_GB/s"):
+            stages[nm]["graph_frac_of_read_probe"] = stages[nm]["graph_GB/s"] / hp["read_GBps"]
+    # per-token quantization moves 2 bytes in for 1 out: held against the copy (1 in, 1 out)
+    stages["quant"]["frac_of_copy_probe"] = stages["quant"]["GB/s"] / hp["copy_GBps"]
+    if stages["quant"].get("graph_GB/s"):
+        stages["quant"]["graph_frac_of_copy_probe"] = stages["quant"]["graph_GB/s"] / hp["copy_GBps"]
     if wl == "opt67b" and args.alpha2 >= 0:
         out["alpha_%g" % args.alpha2] = second_alpha(torch, np, step, layers, alpha, args)
     if not args.no_cpu_baseline:
@@ -663,6 +691,10 @@ def decode(args):
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = burst_s * 1e6
     roof["eager_stage_avg_us"] = tot["gemm"][0] * 1e3 / tot["gemm"][1]
+    # the measured HBM peak beside the datasheet's: the weight stream against plain streaming reads
+    hp = hbm_probe(torch, pq)
+    roof["measured_peak"] = hp["read_GBps"]
+    roof["frac_of_measured_peak"] = roof["achieved"] / hp["read_GBps"]
     out = {
         "metric": METRIC, "value": gemm_ops / gemm_s / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak",
@@ -673,7 +705,7 @@ def decode(args):
                    "tokens": c.T, "hidden": c.K, "out": c.N, "alpha": args.alpha, "bits": 8,
                    "parallelism": "single GPU"},
         "gpu_ms_per_step": sum(v[0] for v in tot.values()) / K, "graph_ms_per_step": graph_ms,
-        "stages": stages, "roofline": roof,
+        "stages": stages, "roofline": roof, "hbm_probe": hp,
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -1,10 +1,14 @@
-/* ptq_probe.h -- matrix-core clock probe exported by libptq.so.
+/* ptq_probe.h -- matrix-core clock probe and HBM stream probe exported by libptq.so.
  *
- * A measurement aid for the int8 GEMM's roofline, not a step of the
- * quantization method.  The published dense int8 peak of the chip assumes its
- * 2.4 GHz top shader clock; under the board's power limit the clock that int8
- * MFMAs on varied operands allow is lower.  This probe measures that clock and
- * the throughput that goes with it, on the GEMM kernel's own instruction mix.
+ * Measurement aids for the rooflines, not steps of the quantization method.
+ * The published dense int8 peak of the chip assumes its 2.4 GHz top shader
+ * clock; under the board's power limit the clock that int8 MFMAs on varied
+ * operands allow is lower.  ptq_probe_mfma measures that clock and the
+ * throughput that goes with it, on the GEMM kernel's own instruction mix.
+ * The published HBM bandwidth (8 TB/s) is likewise a ceiling no access
+ * pattern reaches; ptq_probe_stream measures what plain streaming reads, or a
+ * copy, of a buffer much larger than the last-level cache achieve, as the
+ * measured peak of the memory-bound kernels.
  */
 #ifndef PTQ_PROBE_H
 #define PTQ_PROBE_H
@@ -42,7 +46,23 @@ extern "C" {
  * Returns 0, PTQ_PROBE_ERR_ARG (nothing launched; ptq_probe_last_error() says why) or PTQ_PROBE_ERR_HIP. */
 PTQ_PROBE_API int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed, uint64_t* out, void* stream);
 
-/* Message of the last failed ptq_probe_mfma call on this thread. */
+/* Launch the HBM stream probe on `stream` (a hipStream_t, or NULL for the default stream).
+ *   kind    0: read every byte of src once (16-byte loads, 1 KB of consecutive bytes per wave instruction,
+ *              16 loads in flight per lane); out[b] receives block b's xor of the words read (meaningless,
+ *              it keeps the loads live)
+ *           1: copy src to dst (the same loads, then 16-byte stores)
+ *   src     device buffer of `bytes` bytes, 16-byte aligned; read only
+ *   bytes   a non-zero multiple of 16; larger than twice the 256 MB last-level cache for an HBM figure
+ *   dst     kind 1: device buffer of `bytes` bytes, 16-byte aligned, not overlapping src; else ignored (may be NULL)
+ *   blocks  1..65536 blocks of 256 threads (4 per CU: 1024 on MI355X)
+ *   out     kind 0: device buffer of `blocks` uint32, 4-byte aligned; else ignored (may be NULL)
+ * Buffers are owned by the caller.  Time the launch with events around it; the bytes moved are `bytes` (read)
+ * or 2 * `bytes` (copy).  Returns 0, PTQ_PROBE_ERR_ARG (nothing launched; ptq_probe_last_error() says why) or
+ * PTQ_PROBE_ERR_HIP. */
+PTQ_PROBE_API int ptq_probe_stream(int kind, const void* src, uint64_t bytes, void* dst, int blocks, uint32_t* out,
+                                   void* stream);
+
+/* Message of the last failed ptq_probe_mfma or ptq_probe_stream call on this thread. */
 PTQ_PROBE_API const char* ptq_probe_last_error(void);
 
 #ifdef __cplusplus

@@ -26,6 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,9 +44,11 @@ STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE"
 EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
            "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant",
            "w8a8_gemm_fused", "sq_act_scale_ema", "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma",
+           "ptq_probe_stream",
            "ptq_probe_last_error")
 
 PROBE_KINDS = {"mfma16_random": 0, "mfma32_random": 1, "mfma16_lds_random": 2, "mfma16_zero": 3}
+STREAM_KINDS = {"read": 0, "copy": 1}
 PROBE_MACS_PER_BLOCK_ITER = 8 * 64 * 16 * 16 * 64
 
 
@@ -78,6 +81,8 @@ def _load():
     lib.quant_static_i8.argtypes = [vp, ci, i64, i64, vp, ci, vp, vp, vp, vp]
     lib.ptq_probe_mfma.argtypes = [ci, ci, ci, ctypes.c_uint32, vp, vp]
     lib.ptq_probe_mfma.restype = ci
+    lib.ptq_probe_stream.argtypes = [ci, vp, ctypes.c_uint64, vp, ci, vp, vp]
+    lib.ptq_probe_stream.restype = ci
     lib.ptq_probe_last_error.argtypes = []
     lib.ptq_probe_last_error.restype = ctypes.c_char_p
     for fn in ("sq_absmax_calib", "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
@@ -395,3 +400,35 @@ def probe_mfma(kind, blocks=256, iters=2000, seed=1, stream=None):
     return {"kind": k, "us": us, "clock_GHz": float((cycles / (ticks * 10.0)).mean()),
             "wave_cycles": float(cycles.mean()), "TOPS": ops / us / 1e6}
 
+
+def probe_stream(kind, src, dst=None, blocks=1024, stream=None):
+    """HBM stream probe (include/ptq_probe.h): reads every byte of the device tensor `src` once ("read"), or copies
+    it into `dst` ("copy"), on `blocks` blocks of 256 threads; returns the elapsed time and the bytes moved per
+    second (read bytes, or read plus written bytes for a copy)."""
+    k = STREAM_KINDS.get(kind, kind)
+    if k not in (0, 1):
+        raise ValueError(f"unknown stream probe kind {kind!r}")
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("probe_stream takes a torch.cuda.Stream or None")
+    _dev(src, "src")
+    nbytes = src.numel() * src.element_size()
+    if k == 1:
+        _dev(dst, "dst", device=src.device)
+        if dst.numel() * dst.element_size() < nbytes:
+            raise ValueError("dst is smaller than src")
+    out = torch.zeros(blocks, dtype=torch.int32, device=src.device) if k == 0 else None
+    st = _stream(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream() if stream is None else stream
+    e0.record(s)
+    rc = lib.ptq_probe_stream(k, _ptr(src), nbytes, _ptr(dst) if k == 1 else None, blocks, _ptr(out), st)
+    if rc != 0:
+        raise PtqError(rc, lib.ptq_probe_last_error().decode(errors="replace"))
+    e1.record(s)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    moved = nbytes * (2 if k == 1 else 1)
+    res = {"kind": k, "us": us, "bytes": moved, "GBps": moved / us / 1e3}
+    if k == 0:  # the xor of every 32-bit word read (the blocks' partial xors combined)
+        res["xor"] = int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)))
+    return res

@@ -1,4 +1,5 @@
-// probe.hip -- matrix-core clock probe (a measurement aid for the GEMM's roofline, not a step of the method).
+// probe.hip -- matrix-core clock probe and HBM stream probe (measurement aids for the rooflines, not steps of
+// the method).
 //
 // Every block (one per CU: 512 threads, two waves per SIMD, 64 KB of LDS) issues int8 MFMAs back to back into
 // 32 independent accumulators, on operands drawn from a hash of (seed, thread, register), so consecutive
@@ -11,6 +12,11 @@
 //   3  as 0, all operands zero
 // The published dense int8 peak assumes the 2.4 GHz top clock; under a power limit the clock that random
 // operands allow is lower, and kinds 0 and 2 measure what the GEMM's own instruction mix can reach.
+//
+// The HBM stream probe measures the memory bound the same way: the rate at which plain streaming reads (or a
+// copy) of a buffer far larger than the 256 MB last-level cache move bytes, with each wave reading 1 KB of
+// consecutive bytes per load instruction and 16 such loads in flight per lane -- the access pattern of the
+// path's HBM-bound kernels without their arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -21,6 +27,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int hash3(uint32_t seed, uint32_t a, uint32_t b) {
   uint32_t h = seed * 0x9E3779B9u ^ (a * 0x85EBCA6Bu + b * 0xC2B2AE35u + 0x27D4EB2Fu);
@@ -130,6 +137,51 @@ __global__ __launch_bounds__(512) void k_probe_mfma(int iters, uint32_t seed, un
   if (lane == 0 && wave == 0) out[3 * blockIdx.x + 2] = (unsigned long long)(uint32_t)sink;
 }
 
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 16;  // 16-byte loads in flight per lane
+
+// kind 0: read every 16-byte vector of src once (a per-block xor of the words keeps the loads live: out[block]);
+// kind 1: copy src to dst.  Blocks take rounds of 64 KB of consecutive bytes in turn; block 0 takes the tail.
+template <int KIND>
+__global__ __launch_bounds__(kStreamThreads) void k_probe_stream(const u32x4* __restrict__ src, uint64_t n16,
+                                                                 u32x4* __restrict__ dst, uint32_t* __restrict__ out) {
+  constexpr uint64_t R = (uint64_t)kStreamThreads * kStreamUnroll;  // vectors per round
+  __shared__ uint32_t red[kStreamThreads / 64];
+  const int tid = threadIdx.x;
+  const uint64_t rounds = n16 / R;
+  uint32_t x = 0;
+  for (uint64_t r = blockIdx.x; r < rounds; r += gridDim.x) {
+    const uint64_t base = r * R + (uint64_t)tid;
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = __builtin_nontemporal_load(src + base + (uint64_t)u * kStreamThreads);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      if constexpr (KIND == 1) __builtin_nontemporal_store(v[u], dst + base + (uint64_t)u * kStreamThreads);
+      else x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (uint64_t i = rounds * R + (uint64_t)tid; i < n16; i += kStreamThreads) {
+      const u32x4 v = src[i];
+      if constexpr (KIND == 1) dst[i] = v;
+      else x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  if constexpr (KIND == 0) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+    if ((tid & 63) == 0) red[tid >> 6] = x;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kStreamThreads / 64; ++w) t ^= red[w];
+      out[blockIdx.x] = t;
+    }
+  }
+}
+
 thread_local char g_probe_err[256] = "";
 
 }  // namespace
@@ -163,6 +215,34 @@ int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed, uint64_t* out
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_mfma: launch failed: %s", hipGetErrorString(e));
+    return PTQ_PROBE_ERR_HIP;
+  }
+  return 0;
+}
+
+int ptq_probe_stream(int kind, const void* src, uint64_t bytes, void* dst, int blocks, uint32_t* out, void* stream) {
+  if (kind < 0 || kind > 1 || blocks < 1 || blocks > 65536 || bytes == 0 || (bytes & 15u) != 0) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_stream: kind=%d blocks=%d bytes=%llu out of range", kind,
+             blocks, (unsigned long long)bytes);
+    return PTQ_PROBE_ERR_ARG;
+  }
+  if (!src || (kind == 1 && !dst) || (kind == 0 && !out)) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_stream: src, and dst (copy) or out (read), are required");
+    return PTQ_PROBE_ERR_ARG;
+  }
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u ||
+      reinterpret_cast<uintptr_t>(out) & 3u) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_stream: src and dst must be 16-byte aligned, out 4-byte");
+    return PTQ_PROBE_ERR_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const u32x4* sp = reinterpret_cast<const u32x4*>(src);
+  u32x4* dp = reinterpret_cast<u32x4*>(dst);
+  if (kind == 0) k_probe_stream<0><<<blocks, kStreamThreads, 0, s>>>(sp, bytes / 16, dp, out);
+  else k_probe_stream<1><<<blocks, kStreamThreads, 0, s>>>(sp, bytes / 16, dp, out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_stream: launch failed: %s", hipGetErrorString(e));
     return PTQ_PROBE_ERR_HIP;
   }
   return 0;

@@ -73,7 +73,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
                           "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
                           "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused", "sq_act_scale_ema",
-                          "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma", "ptq_probe_last_error"}
+                          "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma", "ptq_probe_stream",
+                          "ptq_probe_last_error"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.ptq_abi_version() == int(header_define("PTQ_ABI_VERSION"))
@@ -333,4 +334,18 @@ def test_probe_rejects_bad_arguments(lib):
                  (0, 256, 1000001, 1, P), (0, 256, 10, 1, None), (0, 256, 10, 1, MIS)]:
         assert f(*args, None) == ARG, args
         assert lib.ptq_probe_last_error().decode().startswith("ptq_probe_mfma")
+
+
+def test_stream_probe_rejects_bad_arguments(lib):
+    """The stream probe validates on the host: nothing is launched for a bad kind, size, block count or buffer."""
+    f = lib.ptq_probe_stream
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    lib.ptq_probe_last_error.restype = ctypes.c_char_p
+    for args in [(2, P, 1024, P, 16, P), (-1, P, 1024, P, 16, P), (0, P, 0, P, 16, P), (0, P, 1000, P, 16, P),
+                 (0, P, 1024, P, 0, P), (0, P, 1024, P, 65537, P), (0, None, 1024, P, 16, P),
+                 (0, P, 1024, None, 16, None), (1, P, 1024, None, 16, P), (0, MIS, 1024, P, 16, P),
+                 (1, P, 1024, MIS, 16, P), (0, P, 1024, None, 16, MIS)]:
+        assert f(*args, None) == ARG, args
+        assert lib.ptq_probe_last_error().decode().startswith("ptq_probe_stream")
 

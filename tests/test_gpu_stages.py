@@ -767,6 +767,22 @@ def test_ssz_asym_same_codes_candidates(pq, K):
     compare_ssz_asym(host(S), host(Z), host(wq), host(it), host(mse), ref, f"asym same codes K={K}")
 
 
+def test_stream_probe_reads_and_copies_every_byte(pq):
+    """The HBM stream probe behind the bench's measured peak touches every byte: a copy reproduces the buffer,
+    and a read's combined xor is the xor of every 32-bit word (whole rounds of 64 KB over two blocks plus a
+    tail)."""
+    n16 = 3 * 256 * 16 + 5
+    g = torch.Generator(device="cuda:0").manual_seed(3)
+    src = torch.randint(0, 256, (16 * n16,), dtype=torch.uint8, device="cuda:0", generator=g)
+    dst = torch.zeros_like(src)
+    announce("probe_stream copy and read")
+    pq.probe_stream("copy", src, dst, blocks=2)
+    assert torch.equal(dst, src)
+    r = pq.probe_stream("read", src, blocks=2)
+    assert r["xor"] == int(np.bitwise_xor.reduce(host(src).view(np.uint32)))
+    assert r["bytes"] == src.numel()
+
+
 @pytest.mark.parametrize("T,K", [(40, 64), (33, 1040), (24, 4096), (9, 16384)])
 @pytest.mark.parametrize("smooth", ["none", "ok", "tiny_s"])
 def test_quant_per_token_domain_edges(pq, T, K, smooth):
