@@ -461,7 +461,16 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
         c.best = err_ival(w2, Sc, c.P, c.R2, hu, per_elem);
         c.best = Ival{uni(c.best.lo), uni(c.best.hi)};
-        const Decision dc = decide(st.best, c.best, thr);
+        Decision dc;
+        const double dlo = st.best.lo - c.best.hi;
+        if (dlo > 0.0 && dlo >= thr && st.best.lo > 0.0 && dlo >= 2.0 * (thr * st.best.hi)) {
+          // (wave-uniform) the common outcome, which decide() reaches through the same comparisons: a definite
+          // improvement of at least thr, absolute and relative, for every error in the intervals
+          dc.keep = kYes;
+          dc.conv = kNo;
+        } else {
+          dc = decide(st.best, c.best, thr);
+        }
         if (dc.keep == kUnk || dc.conv == kUnk) {
           open = true;
           break;
