@@ -171,6 +171,17 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
 // The domain of div_rn for a divisor: r normal and x / s far from overflow for the callers' operands.
 __device__ __forceinline__ bool div_rn_divisor_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
 
+// fl32(1 / s), the IEEE reciprocal, as one Newton-Raphson step with the fused multiply-add from the hardware's
+// approximate reciprocal: r = r0 + r0 (1 - s r0), r0 = v_rcp_f32(s).  It equals the IEEE quotient 1.0f / s for
+// every fp32 s in [2^-100, 2^101) -- every mantissa of every binade, checked on the GPU by
+// tests/division/rcp_check.hip (tests/test_gpu_rcp.py) -- in three instructions instead of the division
+// sequence's ten.  Callers use it only for divisors inside div_rn's domain (the approximation alone differs from
+// the IEEE reciprocal on about a tenth of those values; outside the domain the callers divide).
+__device__ __forceinline__ float rcp_rn(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+
 // A value known to be the same in every lane, moved to scalar registers (frees vector registers in
 // register-bound kernels; the value is unchanged).
 __device__ __forceinline__ float uni(float v) {

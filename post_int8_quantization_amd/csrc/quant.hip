@@ -178,7 +178,7 @@ __device__ __forceinline__ void quant_row(uint4 (&raw)[CPT][Piece<DT>::P], const
   }
   if constexpr (!STATIC) {
     delta = amax > 0.0f ? amax / 127.0f : 1.0f;
-    inv = 1.0f / delta;
+    inv = rcp_rn(delta);  // used only on the fast path: delta in [2^-67, 2^93]
   }
   const bool live = t < T;
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + (live ? t : 0) * K, live ? (uint32_t)K : 0u);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
             const float sj = in ? __uint_as_float(u[i]) : 1.0f;
             cf.sreg[m][e] = sj;
             if constexpr (FOLD == FOLD_DIV) {
-              cf.rreg[m][e] = 1.0f / sj;
+              cf.rreg[m][e] = rcp_rn(sj);  // used only when every s_j is in div_rn's domain
               cols_ok = cols_ok && (sj >= 0x1p-20f && sj <= 0x1p100f);
             }
           }
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(TPR) void k_quant_tok(const void* __restrict__ x, i
   float static_delta = 1.0f, static_inv = 1.0f;
   if constexpr (STATIC) {
     static_delta = scale[0];
-    static_inv = 1.0f / static_delta;
+    static_inv = rcp_rn(static_delta);  // used only on the fast path (scale in [2^-60, 2^100])
   }
   int parity = 0;
   for (int64_t base = blockIdx.x; base < T; base += D * G) {

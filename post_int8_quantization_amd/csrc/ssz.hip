@@ -223,7 +223,7 @@ __device__ __forceinline__ void load_row(const void* __restrict__ w, int64_t n, 
 template <int CPT, bool ASYM>
 __device__ __forceinline__ void lane_pass(const float (&wh)[CPT][16], float S, float zf, float qmax, double& p,
                                           float& r2, float& r1) {
-  const float rS = 1.0f / S;
+  const float rS = rcp_rn(S);  // S in div_rn's domain (the callers check it)
   double a = 0.0;
   float b = 0.0f;  // at most 16*CPT terms of <= 255^2 each: exact in fp32
   float c = 0.0f;
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
     // codes of the kept parameters, and their error summed directly (the reported mse)
     double e_dir = 0.0;
     if (wq || mse) {
-      const float rS = 1.0f / st.S, zf = (float)st.Z;
+      const float rS = rcp_rn(st.S), zf = (float)st.Z;  // st.S passed the domain check of its pass
       const double Sd = (double)st.S;
 #pragma unroll
       for (int c8 = 0; c8 < CPT; ++c8) {
@@ -690,7 +690,7 @@ __global__ __launch_bounds__(kWave) void k_ssz_rows(const void* __restrict__ w, 
     double e_dir = 0.0;
     if (wq || mse) {
       const float Su = div_rn_divisor_ok(S) ? S : 1.0f;
-      const float rS = 1.0f / Su;
+      const float rS = rcp_rn(Su);
       const double Sd = (double)Su;
       const int64_t c = gl;
       float q[16];
