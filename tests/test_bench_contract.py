@@ -42,3 +42,20 @@ def test_every_traffic_record_names_a_known_kernel():
             assert rec["traffic_bytes_per_launch"] > 0 and rec["dispatches"] > 0
             seen += 1
     assert seen > 0
+
+
+def test_traffic_records_are_of_the_current_kernel_sources():
+    """The committed HBM-traffic records were taken on the kernels as they are now (a record whose source hash no
+    longer matches is ignored by the bench, which then reports traffic as null)."""
+    b = _bench()
+    import json
+    import re
+    stale = []
+    for f in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if "counters" not in f:
+            continue
+        for m in re.finditer(r"traffic-record:\s*(\{.*\})", open(os.path.join(ROOT, "profiles", f)).read()):
+            rec = json.loads(m.group(1))
+            if rec["source_sha"] != b.kernel_source_sha(rec["kernel"]):
+                stale.append((f, rec["kernel"], rec["workload"]))
+    assert not stale, stale
