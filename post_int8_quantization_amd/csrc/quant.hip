@@ -12,7 +12,7 @@
 // store ([INT8] 3.1: 16-byte vectorised accesses).  The smoothing fold
 // x_hat = fl32(x / s_j) ([SQ] X diag(s)^-1) is div_rn's corrected product
 // with the per-column reciprocals fl32(1 / s_j), which each thread computes
-// once (IEEE division) for its own columns and keeps in registers, beside
+// once (rcp_rn, the IEEE reciprocal) for its own columns and keeps in registers, beside
 // s_j, across the rows it visits; the grid size trades that reuse against
 // rows in flight.
 //
