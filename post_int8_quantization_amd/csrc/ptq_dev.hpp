@@ -171,6 +171,33 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
 // The domain of div_rn for a divisor: r normal and x / s far from overflow for the callers' operands.
 __device__ __forceinline__ bool div_rn_divisor_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
 
+// 1 / s in fp64 for a normal fp32 s, within 2^-51 relative: the hardware's approximate fp64 reciprocal and two
+// Newton-Raphson steps with the fused multiply-add, r <- r + r (1 - s r), each of which squares the relative error
+// (up to the step's own rounding).  Five instructions against the IEEE division's eleven.  The bound |1 - s r| <=
+// 2^-51 holds for every fp32 s in [2^-100, 2^101): checked one by one on the GPU (tests/division/rcp_check.hip,
+// tests/test_gpu_rcp.py).
+__device__ __forceinline__ double rcp64(float s) {
+  const double d = (double)s;
+  double r = __builtin_amdgcn_rcp(d);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  return r;
+}
+
+// fl32(x / s) for an fp32 value x held in fp64 and r64 within 2^-51 relative of 1 / s (rcp64(s), or fl64(1 / s)),
+// s a normal fp32 number: the fp64 product x r64 rounded to fp32, two instructions.  The product rounds with a
+// relative error of at most 2^-53 (it is a normal fp64 number for every fp32 x), so x r64 lies within 2^-50.6
+// relative of the exact quotient.
+// The rounding to fp32 can pick another value than the IEEE quotient only if a rounding boundary of fp32 -- a
+// midpoint m of two adjacent fp32 numbers, whose significand is odd and 25 bits long -- lies between the two.  An
+// exact quotient is never such a midpoint (m s has an odd significand of at least 25 bits, which no fp32 x has),
+// and it lies at least 2^-49 relative from every one: x - m s is a non-zero multiple of the smaller of the two
+// operands' last-bit weights, and m s has at most 49 significant bits.  So the result is the IEEE quotient
+// whenever that is a normal fp32 number; a smaller quotient comes out within one subnormal step of it.  Checked
+// bit for bit on the GPU over every mantissa of twelve binades of x around each of thousands of divisors
+// (tests/division/rcp_check.hip, tests/test_gpu_rcp.py).
+__device__ __forceinline__ float quot64(double x, double r64) { return (float)(x * r64); }
+
 // fl32(1 / s), the IEEE reciprocal, as one Newton-Raphson step with the fused multiply-add from the hardware's
 // approximate reciprocal: r = r0 + r0 (1 - s r0), r0 = v_rcp_f32(s).  It equals the IEEE quotient 1.0f / s for
 // every fp32 s in [2^-100, 2^101) -- every mantissa of every binade, checked on the GPU by

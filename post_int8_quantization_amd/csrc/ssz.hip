@@ -16,9 +16,11 @@
 // element the code q, its offset-relative value r = q - Z (r = q when
 // symmetric) and accumulates
 //   P = sum w_hat r (fp64),  R2 = sum r^2,  R1 = sum r (exact integers),
-// the sums the least-squares step needs.  The quotient w_hat / S is div_rn's
-// corrected product with the IEEE reciprocal: the IEEE quotient whenever
-// 2^-100 <= S <= 2^100 (an element under 2^-102 then has |w_hat / S| < 1/4 and
+// the sums the least-squares step needs.  The quotient w_hat / S is the IEEE
+// quotient whenever 2^-100 <= S <= 2^100: for rows of up to 64 elements per
+// thread, held in fp64, the fp64 product with an fp64 reciprocal (rcp64)
+// rounded to fp32 (quot64); for longer rows, held in fp32, div_rn's corrected product with
+// the IEEE reciprocal (an element under 2^-102 then has |w_hat / S| < 1/4 and
 // the code 0 either way).
 //
 // Every decision is the one the exact values give:
@@ -182,59 +184,113 @@ __device__ __forceinline__ float rel_code_ieee(float w, float S, float zf, float
   return fminf(fmaxf(t, -qmax), qmax);
 }
 
+// the same code from the fp64 row value and r64 = rcp64(S) (quot64), 2^-100 <= S <= 2^100
+template <bool ASYM>
+__device__ __forceinline__ float rel_code64(double w, double r64, float zf, float qmax) {
+  const float t = __builtin_rintf(quot64(w, r64));
+  if constexpr (ASYM) return fminf(fmaxf(t + zf, -128.0f), 127.0f) - zf;
+  return fminf(fmaxf(t, -qmax), qmax);
+}
+
+template <typename T>
+__device__ __forceinline__ T tmin(T a, T b) {
+  if constexpr (sizeof(T) == 8) return __builtin_fmin(a, b);
+  else return __builtin_fminf(a, b);
+}
+template <typename T>
+__device__ __forceinline__ T tmax(T a, T b) {
+  if constexpr (sizeof(T) == 8) return __builtin_fmax(a, b);
+  else return __builtin_fmaxf(a, b);
+}
+template <typename T>
+__device__ __forceinline__ T tabs(T a) {
+  if constexpr (sizeof(T) == 8) return __builtin_fabs(a);
+  else return __builtin_fabsf(a);
+}
+
+// A row's elements in registers: fp64 (the widening done once, 2 registers per element) up to 64 per thread in
+// blocks of up to 512 threads, else fp32, where the doubles would not fit (1024 threads leave 128 registers).
+template <bool F64>
+struct RowElemOf {
+  using type = double;
+};
+template <>
+struct RowElemOf<false> {
+  using type = float;
+};
+template <int TPR, int CPT>
+using RowElem = RowElemOf<(CPT <= 4 && TPR <= 512)>;
+
 // Row n of w, folded (w_hat = fl32(w * s_j)), into registers: CPT chunks of 16 elements per thread,
 // chunk c8 of thread tid at elements (tid + TPR*c8)*16 ..; chunks past the row are zeros (they add
 // nothing to any sum, have the code r = 0, and never change a max of magnitudes).
-template <int DT, bool HAS_S, int TPR, int CPT>
+template <int DT, bool HAS_S, int TPR, int CPT, typename T>
 __device__ __forceinline__ void load_row(const void* __restrict__ w, int64_t n, int64_t K, const float* __restrict__ s,
-                                         int tid, float (&wh)[CPT][16]) {
+                                         int tid, T (&wh)[CPT][16]) {
   const int64_t nchunk = K / 16;
 #pragma unroll
   for (int c8 = 0; c8 < CPT; ++c8) {
     const int64_t c = tid + (int64_t)TPR * c8;
     if (c < nchunk) {
-      float a8[8], b8[8];
+      float a8[8], b8[8], f[16];
       load8<DT>(w, n * K + c * 16, a8);
       load8<DT>(w, n * K + c * 16 + 8, b8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        wh[c8][e] = a8[e];
-        wh[c8][e + 8] = b8[e];
+        f[e] = a8[e];
+        f[e + 8] = b8[e];
       }
       if constexpr (HAS_S) {
         const float4* sp = reinterpret_cast<const float4*>(s + c * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const float4 sv = sp[q4];
-          wh[c8][4 * q4 + 0] = wh[c8][4 * q4 + 0] * sv.x;
-          wh[c8][4 * q4 + 1] = wh[c8][4 * q4 + 1] * sv.y;
-          wh[c8][4 * q4 + 2] = wh[c8][4 * q4 + 2] * sv.z;
-          wh[c8][4 * q4 + 3] = wh[c8][4 * q4 + 3] * sv.w;
+          f[4 * q4 + 0] = f[4 * q4 + 0] * sv.x;
+          f[4 * q4 + 1] = f[4 * q4 + 1] * sv.y;
+          f[4 * q4 + 2] = f[4 * q4 + 2] * sv.z;
+          f[4 * q4 + 3] = f[4 * q4 + 3] * sv.w;
         }
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wh[c8][e] = (T)f[e];  // the fold in fp32, then widened exactly
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) wh[c8][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) wh[c8][e] = (T)0.0f;
     }
   }
 }
 
-// One pass over a thread's elements for (S, Z): P, R2, R1 of its elements.
-template <int CPT, bool ASYM>
-__device__ __forceinline__ void lane_pass(const float (&wh)[CPT][16], float S, float zf, float qmax, double& p,
+// One pass over a thread's elements for (S, Z): P, R2, R1 of its elements.  S is in div_rn's domain (the callers
+// check it); elements held in fp64 take the fp64 product's quotient, elements in fp32 div_rn's.
+template <int CPT, bool ASYM, typename T>
+__device__ __forceinline__ void lane_pass(const T (&wh)[CPT][16], float S, float zf, float qmax, double& p,
                                           float& r2, float& r1) {
-  const float rS = rcp_rn(S);  // S in div_rn's domain (the callers check it)
   double a = 0.0;
   float b = 0.0f;  // at most 16*CPT terms of <= 255^2 each: exact in fp32
   float c = 0.0f;
+  if constexpr (sizeof(T) == 8) {
+    const double r64 = rcp64(S);
 #pragma unroll
-  for (int m = 0; m < CPT; ++m) {
+    for (int m = 0; m < CPT; ++m) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float r = rel_code<ASYM>(wh[m][k], S, rS, zf, qmax);
-      a = __builtin_fma((double)wh[m][k], (double)r, a);
-      b = __builtin_fmaf(r, r, b);
-      if constexpr (ASYM) c += r;
+      for (int k = 0; k < 16; ++k) {
+        const float r = rel_code64<ASYM>(wh[m][k], r64, zf, qmax);
+        a = __builtin_fma(wh[m][k], (double)r, a);
+        b = __builtin_fmaf(r, r, b);
+        if constexpr (ASYM) c += r;
+      }
+    }
+  } else {
+    const float rS = rcp_rn(S);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float r = rel_code<ASYM>(wh[m][k], S, rS, zf, qmax);
+        a = __builtin_fma((double)wh[m][k], (double)r, a);
+        b = __builtin_fmaf(r, r, b);
+        if constexpr (ASYM) c += r;
+      }
     }
   }
   p = a;
@@ -331,11 +387,12 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
   const double hu = (double)(CPT * 16 + 6 + NW + 8) * kU * (1.0 + 0x1p-20);
 
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-    float wh[CPT][16];
+    using T = typename RowElem<TPR, CPT>::type;
+    T wh[CPT][16];
     load_row<DT, HAS_S, TPR, CPT>(w, n, K, s, tid, wh);
 
     // row statistics: W2 = sum w_hat^2 (fp64); the max magnitude (symmetric) or min and max; W1 = sum w_hat
-    float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
+    T lo_t = (T)__builtin_huge_valf(), hi_t = (T)(ASYM ? -__builtin_huge_valf() : 0.0f);
     double w2 = 0.0;
     DD w1dd{0.0, 0.0};
 #pragma unroll
@@ -343,18 +400,19 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
       const bool in = tid + (int64_t)TPR * c8 < nchunk;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float v = wh[c8][e];
+        const T v = wh[c8][e];
         if constexpr (ASYM) {
-          lo = fminf(lo, in ? v : lo);
-          hi = fmaxf(hi, in ? v : hi);
+          lo_t = tmin(lo_t, in ? v : lo_t);
+          hi_t = tmax(hi_t, in ? v : hi_t);
           w1dd = dd_add_d(w1dd, (double)v);
         } else {
-          hi = fmaxf(hi, fabsf(v));
+          hi_t = tmax(hi_t, tabs(v));
         }
         const double x = (double)v;
         w2 = __builtin_fma(x, x, w2);
       }
     }
+    float lo = (float)lo_t, hi = (float)hi_t;  // fp32 values: exact
     if constexpr (ASYM) lo = -wave_max(-lo);
     hi = wave_max(hi);
     w2 = wave_sum(w2);
@@ -501,7 +559,9 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
     // codes of the kept parameters, and their error summed directly (the reported mse)
     double e_dir = 0.0;
     if (wq || mse) {
-      const float rS = rcp_rn(st.S), zf = (float)st.Z;  // st.S passed the domain check of its pass
+      // st.S passed the domain check of its pass
+      const float rS = sizeof(T) == 8 ? 0.0f : rcp_rn(st.S), zf = (float)st.Z;
+      const double r64 = sizeof(T) == 8 ? rcp64(st.S) : 0.0;
       const double Sd = (double)st.S;
 #pragma unroll
       for (int c8 = 0; c8 < CPT; ++c8) {
@@ -509,7 +569,9 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
         float q[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float r = rel_code<ASYM>(wh[c8][e], st.S, rS, zf, QMAX);
+          float r;
+          if constexpr (sizeof(T) == 8) r = rel_code64<ASYM>(wh[c8][e], r64, zf, QMAX);
+          else r = rel_code<ASYM>(wh[c8][e], st.S, rS, zf, QMAX);
           q[e] = ASYM ? r + zf : r;
           const double dd = __builtin_fma(-Sd, (double)r, (double)wh[c8][e]);  // S r is exact in fp64
           e_dir = __builtin_fma(dd, dd, e_dir);
