@@ -216,6 +216,19 @@ def _code_only(text):
     return " ".join(text.split())
 
 
+def valu_probe(pq):
+    """The VALU probe's three kinds on two waves per SIMD (2048 one-wave blocks), each after one warm-up launch:
+    the SSZ pass loop alone (element-passes per second) and plain fp32 / fp64 multiply-adds (per second), with the
+    SIMD cycles per wave instruction group and the shader clock the probe read."""
+    res = {}
+    for kind, iters in (("ssz_loop", 2000), ("fma_f32", 8000), ("fma_f64", 8000)):
+        pq.probe_valu(kind, iters=iters)
+        r = pq.probe_valu(kind, iters=iters)
+        res[kind] = {"lane_ops_per_s": r["lane_ops_per_s"], "simd_cycles_per_wave_op": r["simd_cycles_per_wave_op"],
+                     "clock_GHz": r["clock_GHz"]}
+    return res
+
+
 def kernel_source_sha(kernel_tag):
     """Hash of the code a kernel is built from (its .hip file and the shared device header, comments and
     layout ignored), so a traffic record stays valid across comment edits and no longer once the code changes."""
@@ -502,6 +515,19 @@ def main():
             probe[kind] = {"TOPS": r["TOPS"], "clock_GHz": r["clock_GHz"]}
         stages["gemm"]["mfma_probe"] = probe
         stages["gemm"]["frac_of_probe_lds"] = gemm_tops / probe["mfma16_lds_random"]["TOPS"]
+    if wl == "opt67b" or dom == "ssz":
+        # the vector ALUs on the SSZ search's own pass loop, without its reductions, decisions and memory traffic
+        # (after the timed region): the rate its instruction mix reaches, beside the datasheet-derived peak
+        vp = valu_probe(pq)
+        loop = vp["ssz_loop"]["lane_ops_per_s"]  # element-passes per second
+        stages["ssz"]["valu_probe"] = vp
+        stages["ssz"]["loop_probe_frac_alu"] = SSZ_OPS_PER_ELEM_PASS * loop / PEAK_ALU
+        stages["ssz"]["frac_of_loop_probe"] = elem_passes / sec("ssz") / loop
+        if graph_stage.get("ssz"):
+            stages["ssz"]["graph_frac_of_loop_probe"] = elem_passes / (graph_stage["ssz"] / 1e3) / loop
+        if dom == "ssz":
+            roof["measured_peak"] = SSZ_OPS_PER_ELEM_PASS * loop / 1e12
+            roof["frac_of_measured_peak"] = roof["achieved"] / roof["measured_peak"]
     # the measured HBM peak (after the timed region): the memory-bound stages against it as well as the datasheet
     hp = hbm_probe(torch, pq)
     out["hbm_probe"] = hp
@@ -808,6 +834,10 @@ def ssz_scale(args):
     rec = load_counters("k_ssz", "ssz_scale")
     roof["traffic"] = None if rec is None else rec.get("traffic_bytes_per_launch")
     roof["avg_launch_us"] = v["ms"] * 1e3 / len(mats)
+    vp = valu_probe(pq)
+    roof["measured_peak"] = SSZ_OPS_PER_ELEM_PASS * vp["ssz_loop"]["lane_ops_per_s"] / 1e12
+    roof["frac_of_measured_peak"] = roof["achieved"] / roof["measured_peak"]
+    stages["int8"]["valu_probe"] = vp
     out = {
         "metric": METRIC, "value": v["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

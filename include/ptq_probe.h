@@ -1,4 +1,4 @@
-/* ptq_probe.h -- matrix-core clock probe and HBM stream probe exported by libptq.so.
+/* ptq_probe.h -- matrix-core clock probe, VALU probe and HBM stream probe exported by libptq.so.
  *
  * Measurement aids for the rooflines, not steps of the quantization method.
  * The published dense int8 peak of the chip assumes its 2.4 GHz top shader
@@ -8,7 +8,10 @@
  * The published HBM bandwidth (8 TB/s) is likewise a ceiling no access
  * pattern reaches; ptq_probe_stream measures what plain streaming reads, or a
  * copy, of a buffer much larger than the last-level cache achieve, as the
- * measured peak of the memory-bound kernels.
+ * measured peak of the memory-bound kernels.  The weight quantizer's search is bound by the vector ALUs, whose
+ * issue rate depends on the instruction mix (fp32 and fp64 operations take different numbers of cycles);
+ * ptq_probe_valu measures the rate of the search's own pass loop without its reductions and decisions, and of
+ * plain fp32 and fp64 multiply-adds.
  */
 #ifndef PTQ_PROBE_H
 #define PTQ_PROBE_H
@@ -46,6 +49,25 @@ extern "C" {
  * Returns 0, PTQ_PROBE_ERR_ARG (nothing launched; ptq_probe_last_error() says why) or PTQ_PROBE_ERR_HIP. */
 PTQ_PROBE_API int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed, uint64_t* out, void* stream);
 
+/* Element-passes per lane and iteration of kinds 0 and 1 (the SSZ search's loop over 64 values). */
+#define PTQ_PROBE_VALU_ELEMS_PER_ITER 64
+/* Multiply-adds per lane and iteration of kinds 2 and 3: 16 x 8 independent chains. */
+#define PTQ_PROBE_VALU_FMAS_PER_ITER 128
+
+/* Launch the VALU probe on `stream` (a hipStream_t, or NULL for the default stream): `blocks` blocks of one wave
+ * (64 threads) each, so blocks / (4 * number of CUs) waves per SIMD (2048 blocks: two per SIMD on MI355X).
+ *   kind    0: the SSZ search's pass loop alone: per lane 64 fp32 values held in fp64 and, per iteration, the fp64
+ *              reciprocal of a scale, then per value the fp64 product rounded to fp32, round, clamp to [-127, 127],
+ *              widening of the code, the fp64 multiply-add of sum w q and the fp32 one of sum q^2
+ *           1: kind 0 plus the per-iteration 64-lane butterflies of both sums (fp64 and integer)
+ *           2: fp32 multiply-adds only, 8 independent chains per lane
+ *           3: fp64 multiply-adds only, 8 independent chains per lane
+ *   blocks  1..65536;  iters 1..1000000;  seed: operand hash seed
+ *   out     device buffer of 3*blocks uint64, 8-byte aligned, written by the kernel as for ptq_probe_mfma: per block
+ *           the shader-clock cycles and 100 MHz ticks wave 0 spent in the loop, then a meaningless sink value.
+ * Returns 0, PTQ_PROBE_ERR_ARG (nothing launched; ptq_probe_last_error() says why) or PTQ_PROBE_ERR_HIP. */
+PTQ_PROBE_API int ptq_probe_valu(int kind, int blocks, int iters, uint32_t seed, uint64_t* out, void* stream);
+
 /* Launch the HBM stream probe on `stream` (a hipStream_t, or NULL for the default stream).
  *   kind    0: read every byte of src once (16-byte loads, 1 KB of consecutive bytes per wave instruction,
  *              16 loads in flight per lane); out[b] receives block b's xor of the words read (meaningless,
@@ -62,7 +84,7 @@ PTQ_PROBE_API int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed,
 PTQ_PROBE_API int ptq_probe_stream(int kind, const void* src, uint64_t bytes, void* dst, int blocks, uint32_t* out,
                                    void* stream);
 
-/* Message of the last failed ptq_probe_mfma or ptq_probe_stream call on this thread. */
+/* Message of the last failed ptq_probe_mfma, ptq_probe_valu or ptq_probe_stream call on this thread. */
 PTQ_PROBE_API const char* ptq_probe_last_error(void);
 
 #ifdef __cplusplus

@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
 
 Measurement aid (include/ptq_probe.h, not a step of the method):
   probe_mfma(kind, blocks=256, iters=2000, seed=1) -> dict with the loop's shader clock and int8 throughput
+  probe_valu(kind, blocks=2048, iters=2000, seed=1) -> dict with the VALU loop's clock and lane-operation rate
+  probe_stream(kind, src, dst=None, blocks=1024) -> dict with the bytes read (or copied) per second
 """
 from __future__ import annotations
 
@@ -44,11 +46,14 @@ STATUS = {0: "PTQ_OK", 1: "PTQ_ERR_NULL", 2: "PTQ_ERR_SHAPE", 3: "PTQ_ERR_DTYPE"
 EXPORTS = ("ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib", "sq_smooth_factors",
            "ssz_weight_qparams", "ssz_weight_qparams_asym", "quant_per_token_i8", "w8a8_gemm_dequant",
            "w8a8_gemm_fused", "sq_act_scale_ema", "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma",
-           "ptq_probe_stream",
+           "ptq_probe_stream", "ptq_probe_valu",
            "ptq_probe_last_error")
 
 PROBE_KINDS = {"mfma16_random": 0, "mfma32_random": 1, "mfma16_lds_random": 2, "mfma16_zero": 3}
 STREAM_KINDS = {"read": 0, "copy": 1}
+VALU_KINDS = {"ssz_loop": 0, "ssz_loop_reduce": 1, "fma_f32": 2, "fma_f64": 3}
+VALU_ELEMS_PER_ITER = 64   # kinds 0, 1: element-passes per lane and iteration
+VALU_FMAS_PER_ITER = 128   # kinds 2, 3: multiply-adds per lane and iteration
 PROBE_MACS_PER_BLOCK_ITER = 8 * 64 * 16 * 16 * 64
 
 
@@ -81,6 +86,8 @@ def _load():
     lib.quant_static_i8.argtypes = [vp, ci, i64, i64, vp, ci, vp, vp, vp, vp]
     lib.ptq_probe_mfma.argtypes = [ci, ci, ci, ctypes.c_uint32, vp, vp]
     lib.ptq_probe_mfma.restype = ci
+    lib.ptq_probe_valu.argtypes = [ci, ci, ci, ctypes.c_uint32, vp, vp]
+    lib.ptq_probe_valu.restype = ci
     lib.ptq_probe_stream.argtypes = [ci, vp, ctypes.c_uint64, vp, ci, vp, vp]
     lib.ptq_probe_stream.restype = ci
     lib.ptq_probe_last_error.argtypes = []
@@ -407,6 +414,37 @@ def probe_mfma(kind, blocks=256, iters=2000, seed=1, stream=None):
     ops = 2.0 * PROBE_MACS_PER_BLOCK_ITER * iters * blocks
     return {"kind": k, "us": us, "clock_GHz": float((cycles / (ticks * 10.0)).mean()),
             "wave_cycles": float(cycles.mean()), "TOPS": ops / us / 1e6}
+
+
+def probe_valu(kind, blocks=2048, iters=2000, seed=1, stream=None):
+    """VALU probe (include/ptq_probe.h): runs `kind` ("ssz_loop", "ssz_loop_reduce", "fma_f32", "fma_f64" or its
+    code) on `blocks` one-wave blocks and returns the elapsed time, the mean shader clock wave 0 of each block saw,
+    the lane operations per second (element-passes for the SSZ loop kinds, multiply-adds for the others) and the
+    SIMD cycles one wave's unit of work took on average (all SIMDs of the device busy)."""
+    k = VALU_KINDS.get(kind, kind)
+    if k not in (0, 1, 2, 3):
+        raise ValueError(f"unknown VALU probe kind {kind!r}")
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("probe_valu takes a torch.cuda.Stream or None")
+    out = torch.zeros(3 * blocks, dtype=torch.int64, device="cuda")
+    st = _stream(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream() if stream is None else stream
+    e0.record(s)
+    rc = lib.ptq_probe_valu(k, blocks, iters, seed, _ptr(out), st)
+    if rc != 0:
+        raise PtqError(rc, lib.ptq_probe_last_error().decode(errors="replace"))
+    e1.record(s)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    rec = out.view(blocks, 3).cpu().double()
+    cycles, ticks = rec[:, 0], rec[:, 1]
+    clock = float((cycles / (ticks * 10.0)).mean())
+    per_lane = VALU_ELEMS_PER_ITER if k <= 1 else VALU_FMAS_PER_ITER
+    lane_ops = float(blocks) * 64 * iters * per_lane
+    simds = 4 * torch.cuda.get_device_properties(out.device).multi_processor_count
+    return {"kind": k, "us": us, "clock_GHz": clock, "lane_ops_per_s": lane_ops / (us * 1e-6),
+            "simd_cycles_per_wave_op": us * 1e-6 * clock * 1e9 * simds / (lane_ops / 64)}
 
 
 def probe_stream(kind, src, dst=None, blocks=1024, stream=None):

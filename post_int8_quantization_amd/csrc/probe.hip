@@ -1,5 +1,5 @@
-// probe.hip -- matrix-core clock probe and HBM stream probe (measurement aids for the rooflines, not steps of
-// the method).
+// probe.hip -- matrix-core clock probe, VALU probe and HBM stream probe (measurement aids for the rooflines, not
+// steps of the method).
 //
 // Every block (one per CU: 512 threads, two waves per SIMD, 64 KB of LDS) issues int8 MFMAs back to back into
 // 32 independent accumulators, on operands drawn from a hash of (seed, thread, register), so consecutive
@@ -13,6 +13,16 @@
 // The published dense int8 peak assumes the 2.4 GHz top clock; under a power limit the clock that random
 // operands allow is lower, and kinds 0 and 2 measure what the GEMM's own instruction mix can reach.
 //
+// The VALU probe measures the ALU bound of the SSZ search the same way, one wave per block (64 threads) so the
+// caller sets the waves per SIMD by the block count, wave 0 timing its loop as above.  Kinds:
+//   0  the SSZ pass loop alone: 64 fp32 row values per lane held in fp64, per pass the fp64 reciprocal of the
+//      scale, then per element the fp64 product rounded to fp32, round, clamp to [-127, 127], widening of the code,
+//      the fp64 multiply-add of sum w q and the fp32 one of sum q^2 -- the search's own instructions, without its
+//      reductions, decisions or memory traffic
+//   1  as 0, plus the per-pass 64-lane butterflies of both sums (fp64 and integer)
+//   2  fp32 multiply-adds only (8 independent chains per lane)
+//   3  fp64 multiply-adds only (8 independent chains per lane)
+//
 // The HBM stream probe measures the memory bound the same way: the rate at which plain streaming reads (or a
 // copy) of a buffer far larger than the 256 MB last-level cache move bytes, with each wave reading 1 KB of
 // consecutive bytes per load instruction and 16 such loads in flight per lane -- the access pattern of the
@@ -22,6 +32,7 @@
 #include <stdio.h>
 
 #include "../../include/ptq_probe.h"
+#include "ptq_dev.hpp"
 
 namespace {
 
@@ -137,6 +148,81 @@ __global__ __launch_bounds__(512) void k_probe_mfma(int iters, uint32_t seed, un
   if (lane == 0 && wave == 0) out[3 * blockIdx.x + 2] = (unsigned long long)(uint32_t)sink;
 }
 
+template <int KIND>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_probe_valu(
+    int iters, uint32_t seed, unsigned long long* __restrict__ out) {
+  const int lane = threadIdx.x;
+  const uint32_t t = blockIdx.x * 64u + lane;
+  unsigned long long c0 = 0, r0 = 0;
+  double sink = 0.0;
+  if constexpr (KIND <= 1) {
+    // row values in [-1/8, 1/8), as fp32 then widened; scales near max / 127, alternating between two values
+    double wh[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) wh[i] = (double)((float)(hash3(seed, t, i) >> 8) * 0x1p-26f);
+    const float s0 = 0.125f / 127.0f, s1 = s0 * 1.0009765625f;
+    double P = 0.0;
+    float R2 = 0.0f;
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+      const double r64 = ptq::rcp64((it & 1) ? s1 : s0);
+      double a = 0.0;
+      float b = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float q = fminf(fmaxf(__builtin_rintf(ptq::quot64(wh[i], r64)), -127.0f), 127.0f);
+        a = __builtin_fma(wh[i], (double)q, a);
+        b = __builtin_fmaf(q, q, b);
+      }
+      if constexpr (KIND == 1) {
+        a = ptq::wave_sum(a);
+        b = (float)ptq::wave_sum((int)b);
+      }
+      P += a;
+      R2 += b;
+    }
+    sink = P + (double)R2;
+  } else if constexpr (KIND == 2) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)(hash3(seed, t, i) & 0xFFFF) * 0x1p-16f;
+    const float m = 0.99998f, c = (float)(hash3(seed, t, 99) & 0xFF) * 0x1p-20f;
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = __builtin_fmaf(f[i], m, c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sink += (double)f[i];
+  } else {
+    double d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = (double)(hash3(seed, t, i) & 0xFFFF) * 0x1p-16;
+    const double m = 0.99998, c = (double)(hash3(seed, t, 99) & 0xFF) * 0x1p-20;
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = __builtin_fma(d[i], m, c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sink += d[i];
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) {
+    out[3 * blockIdx.x] = c1 - c0;
+    out[3 * blockIdx.x + 1] = r1 - r0;
+    out[3 * blockIdx.x + 2] = (unsigned long long)__double_as_longlong(sink);  // keeps the loop live; meaningless
+  }
+}
+
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 16;  // 16-byte loads in flight per lane
 
@@ -215,6 +301,36 @@ int ptq_probe_mfma(int kind, int blocks, int iters, uint32_t seed, uint64_t* out
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_mfma: launch failed: %s", hipGetErrorString(e));
+    return PTQ_PROBE_ERR_HIP;
+  }
+  return 0;
+}
+
+int ptq_probe_valu(int kind, int blocks, int iters, uint32_t seed, uint64_t* out, void* stream) {
+  if (!out) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_valu: out is required");
+    return PTQ_PROBE_ERR_ARG;
+  }
+  if (kind < 0 || kind > 3 || blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_valu: kind=%d blocks=%d iters=%d out of range", kind, blocks,
+             iters);
+    return PTQ_PROBE_ERR_ARG;
+  }
+  if (reinterpret_cast<uintptr_t>(out) & 7u) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_valu: out must be 8-byte aligned");
+    return PTQ_PROBE_ERR_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
+  switch (kind) {
+    case 0: k_probe_valu<0><<<blocks, 64, 0, s>>>(iters, seed, o); break;
+    case 1: k_probe_valu<1><<<blocks, 64, 0, s>>>(iters, seed, o); break;
+    case 2: k_probe_valu<2><<<blocks, 64, 0, s>>>(iters, seed, o); break;
+    default: k_probe_valu<3><<<blocks, 64, 0, s>>>(iters, seed, o); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_probe_err, sizeof g_probe_err, "ptq_probe_valu: launch failed: %s", hipGetErrorString(e));
     return PTQ_PROBE_ERR_HIP;
   }
   return 0;

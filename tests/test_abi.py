@@ -73,7 +73,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"ptq_abi_version", "ptq_last_error", "ptq_status_string", "sq_absmax_calib",
                           "sq_smooth_factors", "ssz_weight_qparams", "ssz_weight_qparams_asym",
                           "quant_per_token_i8", "w8a8_gemm_dequant", "w8a8_gemm_fused", "sq_act_scale_ema",
-                          "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma", "ptq_probe_stream",
+                          "weight_scale_per_tensor", "quant_static_i8", "ptq_probe_mfma", "ptq_probe_stream", "ptq_probe_valu",
                           "ptq_probe_last_error"}
     for n in names:
         assert hasattr(lib, n), n
@@ -334,6 +334,17 @@ def test_probe_rejects_bad_arguments(lib):
                  (0, 256, 1000001, 1, P), (0, 256, 10, 1, None), (0, 256, 10, 1, MIS)]:
         assert f(*args, None) == ARG, args
         assert lib.ptq_probe_last_error().decode().startswith("ptq_probe_mfma")
+
+
+def test_valu_probe_rejects_bad_arguments(lib):
+    """The VALU probe validates on the host: nothing is launched for a bad kind, size, count or buffer."""
+    f = lib.ptq_probe_valu
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ptq_probe_last_error.restype = ctypes.c_char_p
+    for args in [(4, 2048, 10, 1, P), (-1, 2048, 10, 1, P), (0, 0, 10, 1, P), (0, 65537, 10, 1, P), (0, 2048, 0, 1, P),
+                 (0, 2048, 1000001, 1, P), (0, 2048, 10, 1, None), (0, 2048, 10, 1, MIS)]:
+        assert f(*args, None) == ARG, args
+        assert lib.ptq_probe_last_error().decode().startswith("ptq_probe_valu")
 
 
 def test_stream_probe_rejects_bad_arguments(lib):

@@ -767,6 +767,47 @@ def test_ssz_asym_same_codes_candidates(pq, K):
     compare_ssz_asym(host(S), host(Z), host(wq), host(it), host(mse), ref, f"asym same codes K={K}")
 
 
+def _hash3(seed, a, b):
+    """The probes' operand hash, on the host (uint32 arithmetic)."""
+    m = 0xFFFFFFFF
+    h = ((seed * 0x9E3779B9) & m) ^ ((a * 0x85EBCA6B + b * 0xC2B2AE35 + 0x27D4EB2F) & m)
+    h ^= h >> 15
+    h = (h * 0x2C1B3C6D) & m
+    h ^= h >> 12
+    h = (h * 0x297A2D39) & m
+    h ^= h >> 15
+    return h - (1 << 32) if h & 0x80000000 else h
+
+
+def test_valu_probe_runs_the_search_loop(pq):
+    """The VALU probe's SSZ-loop kind computes what it claims: lane 0 of each block returns P + R2 summed over the
+    iterations, P = sum w q (exact in fp64), R2 = sum q^2, q = clamp(rint(fl32(w / s))) -- recomputed here with
+    numpy's fp32 division.  The other kinds run and report plausible rates."""
+    seed, iters, blocks = 7, 5, 3
+    r = pq.probe_valu("ssz_loop", blocks=blocks, iters=iters, seed=seed)
+    out = torch.zeros(3 * blocks, dtype=torch.int64, device="cuda")
+    assert pq.lib.ptq_probe_valu(0, blocks, iters, seed, out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    got = out.view(blocks, 3)[:, 2].cpu().numpy().view(np.float64)
+    s0 = np.float32(np.float32(0.125) / np.float32(127.0))
+    s1 = np.float32(s0 * np.float32(1.0009765625))
+    for b in range(blocks):
+        t = b * 64
+        w = np.array([np.float32(np.float32(_hash3(seed, t, i) >> 8) * np.float32(2.0 ** -26)) for i in range(64)],
+                     dtype=np.float32)
+        P, R2 = 0.0, np.float32(0.0)
+        for it in range(iters):
+            q = np.clip(np.rint(w / (s1 if it & 1 else s0)), -127, 127).astype(np.float32)
+            P += float(np.sum(w.astype(np.float64) * q.astype(np.float64)))
+            R2 = np.float32(R2 + np.float32(np.sum(q.astype(np.float64) ** 2)))
+        assert got[b] == P + float(R2), (b, got[b], P + float(R2))
+    assert r["lane_ops_per_s"] > 0 and r["clock_GHz"] > 0.5
+    for kind in ("ssz_loop_reduce", "fma_f32", "fma_f64"):
+        announce(f"probe_valu {kind}")
+        q = pq.probe_valu(kind, blocks=2048, iters=200)  # two waves per SIMD: every SIMD busy
+        assert q["lane_ops_per_s"] > 0 and 1.0 < q["simd_cycles_per_wave_op"] < 64.0, q
+
+
 def test_stream_probe_reads_and_copies_every_byte(pq):
     """The HBM stream probe behind the bench's measured peak touches every byte: a copy reproduces the buffer,
     and a read's combined xor is the xor of every 32-bit word (whole rounds of 64 KB over two blocks plus a
