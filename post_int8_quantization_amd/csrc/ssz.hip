@@ -17,11 +17,11 @@
 // symmetric) and accumulates
 //   P = sum w_hat r (fp64),  R2 = sum r^2,  R1 = sum r (exact integers),
 // the sums the least-squares step needs.  The quotient w_hat / S is the IEEE
-// quotient whenever 2^-100 <= S <= 2^100: for rows of up to 64 elements per
-// thread, held in fp64, the fp64 product with an fp64 reciprocal (rcp64)
-// rounded to fp32 (quot64); for longer rows, held in fp32, div_rn's corrected product with
-// the IEEE reciprocal (an element under 2^-102 then has |w_hat / S| < 1/4 and
-// the code 0 either way).
+// quotient whenever 2^-100 <= S <= 2^100: for rows of up to 32768 elements
+// (at most 64 per thread), held in fp64, the fp64 product with an fp64
+// reciprocal (rcp64) rounded to fp32 (quot64); for longer rows, held in fp32,
+// div_rn's corrected product with the IEEE reciprocal (an element under
+// 2^-102 then has |w_hat / S| < 1/4 and the code 0 either way).
 //
 // Every decision is the one the exact values give:
 //  * P is exact.  A non-zero r needs |w_hat / S| > 1/2, so every non-zero term
