@@ -1,7 +1,9 @@
 // ssz.hip -- MinMax + SSZ per-output-channel weight quantization (gfx950):
 // symmetric int8/int4 and asymmetric int8 (k_ssz), short symmetric rows of at
 // most 512 elements, several rows per wave (k_ssz_rows), and the exact search
-// for the rows those two defer (k_ssz_exact).
+// (exact_row) for the rows those two cannot certify: inside the symmetric
+// k_ssz instances of up to 128 threads, else in a launch of its own
+// (k_ssz_exact).
 //
 // [SSZ] flow: MinMax initial parameters, then least-squares refits for the
 // current codes, a refit kept only when it lowers the quantization error,
@@ -44,12 +46,14 @@
 //    without a pass.
 // A row for which any of this fails -- a scale outside div_rn's range, a P
 // the certificate does not cover, a decision the intervals leave open (none
-// in 330,000 passes over the workloads' weights) -- is deferred: the kernel
-// writes a NaN scale and nothing else for it, and k_ssz_exact, launched next
-// on the same stream, searches those rows again with the IEEE division and
-// every sum in double-double, rounded once.  Its roundings of the exact sums
-// give the correctly rounded fp64 value unless an exact sum lies within about
-// 2^-90 relative of an fp64 rounding boundary.
+// in 330,000 passes over the workloads' weights) -- is searched again with the
+// IEEE division and every sum in double-double, rounded once: by the same
+// block, right away, in the k_ssz instances that can (ssz_inline_exact); the
+// others and k_ssz_rows write a NaN scale and nothing else for it, and
+// k_ssz_exact, launched next on the same stream, searches the rows so marked.
+// The exact search's roundings of the exact sums give the correctly rounded
+// fp64 value unless an exact sum lies within about 2^-90 relative of an fp64
+// rounding boundary.
 // Sums are reduced with butterflies in which both lanes of a pair combine the
 // same two operands, and across waves through LDS in wave order, so every
 // lane of a row holds identical bits and every decision is uniform.
@@ -362,8 +366,173 @@ __device__ __forceinline__ void minmax_init(float lo, float hi, float qmax, floa
   }
 }
 
+constexpr int kExactTpr = 256;
+
+template <int DT, bool HAS_S>
+__device__ __forceinline__ float load_folded(const void* __restrict__ w, const float* __restrict__ s, int64_t n,
+                                             int64_t K, int64_t k) {
+  float v;
+  if constexpr (DT == PTQ_BF16)
+    v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(w)[n * K + k] << 16);
+  else
+    v = reinterpret_cast<const float*>(w)[n * K + k];
+  if constexpr (HAS_S) v = v * s[k];
+  return v;
+}
+
+// The exact search of row n by a block of NT threads, reading the row from memory on every pass: codes by the
+// IEEE division, P, the error and the asymmetric W1 summed in double-double and rounded once, R2 and R1 exact;
+// then the plain greedy rule and convergence test on those values.  Writes all of the row's outputs.  Every
+// thread of the block calls it (it synchronises the block); xd holds 4 NT/64 doubles and xf 2 NT/64 floats of LDS.
+template <int DT, bool HAS_S, int BITS, bool ASYM, int NT>
+__device__ __forceinline__ void exact_row(const void* __restrict__ w, int64_t n, int64_t K, const float* __restrict__ s,
+                                          int max_iter, double thr, float min_scale, float* __restrict__ scale,
+                                          int32_t* __restrict__ zero_point, void* __restrict__ wq,
+                                          int32_t* __restrict__ iters, double* __restrict__ mse, double* xd, float* xf,
+                                          int tid) {
+  constexpr int NW = NT / kWave;
+  constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
+  const double Kd = (double)K;
+  const DivK per_elem = make_divk(K);
+
+  // sums over the block (every thread gets the same bits)
+  auto bsum_dd = [&](DD v) -> double {
+    v = group_sum_dd<64>(v);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+      xd[tid / kWave] = v.hi;
+      xd[NW + tid / kWave] = v.lo;
+    }
+    __syncthreads();
+    DD t{xd[0], xd[NW]};
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t = dd_add(t, DD{xd[i], xd[NW + i]});
+    return t.hi + t.lo;
+  };
+  auto bsum = [&](double v) -> double {  // exact integer sums
+    v = wave_sum(v);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) xd[2 * NW + tid / kWave] = v;
+    __syncthreads();
+    double t = xd[2 * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t += xd[2 * NW + i];
+    return t;
+  };
+  auto bminmax = [&](float& lo, float& hi) {
+    lo = -wave_max(-lo);
+    hi = wave_max(hi);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+      xf[tid / kWave] = lo;
+      xf[NW + tid / kWave] = hi;
+    }
+    __syncthreads();
+    lo = xf[0];
+    hi = xf[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      lo = fminf(lo, xf[i]);
+      hi = fmaxf(hi, xf[NW + i]);
+    }
+  };
+
+  float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
+  DD w1{0.0, 0.0};
+  for (int64_t k = tid; k < K; k += NT) {
+    const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+    if constexpr (ASYM) {
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+      w1 = dd_add_d(w1, (double)v);
+    } else {
+      hi = fmaxf(hi, fabsf(v));
+    }
+  }
+  bminmax(lo, hi);
+  const double W1 = ASYM ? bsum_dd(w1) : 0.0;
+
+  // P, R2, R1 and the mean error of (S, Z), every sum exact
+  auto pass = [&](float S, int Z, double& P, double& R2, double& R1) -> double {
+    const float zf = (float)Z;
+    const double Sd = (double)S;
+    DD p{0.0, 0.0}, e{0.0, 0.0};
+    double r2 = 0.0, r1 = 0.0;
+    for (int64_t k = tid; k < K; k += NT) {
+      const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+      const float r = rel_code_ieee<ASYM>(v, S, zf, QMAX);
+      p = dd_add_d(p, (double)v * (double)r);  // exact product
+      double dh, dl;
+      two_sum((double)v, -(Sd * (double)r), dh, dl);  // S r is exact in fp64
+      DD t = two_sqr(dh);
+      t.lo += dh * (2.0 * dl) + dl * dl;
+      e = dd_add(e, t);
+      r2 += (double)r * (double)r;
+      r1 += (double)r;
+    }
+    P = bsum_dd(p);
+    R2 = bsum(r2);
+    R1 = ASYM ? bsum(r1) : 0.0;
+    return per_elem(bsum_dd(e));
+  };
+
+  RowState st;
+  minmax_init<ASYM>(lo, hi, QMAX, min_scale, st.S, st.Z);
+  const double b0 = pass(st.S, st.Z, st.P, st.R2, st.R1);
+  double best = b0;
+  int it = 0;
+  for (int i = 1; i <= max_iter; ++i) {
+    it = i;
+    float Sc;
+    int Zc;
+    if (!refit<ASYM>(st, Kd, W1, per_elem, min_scale, Sc, Zc)) break;
+    RowState c;
+    c.S = Sc;
+    c.Z = Zc;
+    const double cur = pass(Sc, Zc, c.P, c.R2, c.R1);
+    const double d = best - cur;
+    const bool conv = (best == 0.0) || (fabs(d) < thr) || (d / best < thr);
+    if (cur < best) {
+      st = c;
+      best = cur;
+    }
+    if (conv) break;
+  }
+
+  // codes of the kept parameters
+  if (wq) {
+    const float zf = (float)st.Z;
+    for (int64_t k = tid; k < K; k += NT) {
+      const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
+      const float q = rel_code_ieee<ASYM>(v, st.S, zf, QMAX) + (ASYM ? zf : 0.0f);
+      if constexpr (BITS == 8) {
+        reinterpret_cast<int8_t*>(wq)[n * K + k] = (int8_t)(int)q;
+      } else {
+        // two codes per byte: the thread of the even element writes the pair
+        const float v1 = load_folded<DT, HAS_S>(w, s, n, K, k ^ 1);
+        const float q1 = rel_code_ieee<false>(v1, st.S, 0.0f, QMAX);
+        if ((k & 1) == 0)
+          reinterpret_cast<uint8_t*>(wq)[n * (K / 2) + k / 2] =
+              (uint8_t)(((uint32_t)(int)q & 0xFu) | (((uint32_t)(int)q1 & 0xFu) << 4));
+      }
+    }
+  }
+  if (tid == 0) {
+    scale[n] = st.S;
+    if constexpr (ASYM) zero_point[n] = st.Z;
+    if (iters) iters[n] = it;
+    if (mse) mse[n] = best;
+  }
+}
+
+// Whether k_ssz searches the rows it cannot certify itself (exact_row, by the same block, right away), which
+// spares the launch of k_ssz_exact: the symmetric instances of up to 128 threads (rows of up to 8192 elements).
+// The others mark such rows with a NaN scale (and no other output) for k_ssz_exact: the asymmetric and
+// 1024-thread instances have no registers to spare, and the 256-thread one ran ~1% slower with the search inside.
+constexpr bool ssz_inline_exact(bool asym, int tpr) { return !asym && tpr <= 128; }
+
 // MinMax + SSZ, symmetric (ASYM = false; qmax 127 or 7) or asymmetric int8; one row per block of TPR threads.
-// Rows it cannot certify get a NaN scale (and no other output) for k_ssz_exact.  Register use is capped at two waves
+// Rows it cannot certify are searched exactly (see ssz_inline_exact).  Register use is capped at two waves
 // per SIMD (256 registers): left free, the asymmetric variant takes more and runs one wave per SIMD.
 template <int DT, bool HAS_S, int BITS, bool ASYM, int TPR, int CPT>
 __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k_ssz(
@@ -375,7 +544,7 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr int NW = TPR / kWave;
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
   __shared__ double ring[2][3 * NW];  // pass sums, alternating halves
-  __shared__ double xd[2 * NW];
+  __shared__ double xd[4 * NW];  // (also the exact search's block sums)
   __shared__ float xf[2 * NW];
   int par = 0;
   const int tid = threadIdx.x;
@@ -553,7 +722,12 @@ __global__ __launch_bounds__(TPR) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 
     if (!ok) {
-      if (tid == 0) scale[n] = __builtin_nanf("");
+      // a row this search cannot certify: the exact search
+      if constexpr (ssz_inline_exact(ASYM, TPR))
+        exact_row<DT, HAS_S, BITS, ASYM, TPR>(w, n, K, s, max_iter, thr, min_scale, scale, zero_point, wq, iters, mse,
+                                              xd, xf, tid);
+      else if (tid == 0)
+        scale[n] = __builtin_nanf("");
       continue;
     }
     // codes of the kept parameters, and their error summed directly (the reported mse)
@@ -774,24 +948,8 @@ __global__ __launch_bounds__(kWave) void k_ssz_rows(const void* __restrict__ w, 
 }
 
 // ---------------------------------------------------------------------------
-// The exact search for deferred rows (scale[n] is NaN), one row per block of 256 threads, reading the row from
-// memory on every pass: codes by the IEEE division, P, the error and the asymmetric W1 summed in
-// double-double and rounded once, R2 and R1 exact; then the plain greedy rule and convergence test on those
-// values.  Rows with a finite scale are left as they are.
-
-constexpr int kExactTpr = 256;
-
-template <int DT, bool HAS_S>
-__device__ __forceinline__ float load_folded(const void* __restrict__ w, const float* __restrict__ s, int64_t n,
-                                             int64_t K, int64_t k) {
-  float v;
-  if constexpr (DT == PTQ_BF16)
-    v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(w)[n * K + k] << 16);
-  else
-    v = reinterpret_cast<const float*>(w)[n * K + k];
-  if constexpr (HAS_S) v = v * s[k];
-  return v;
-}
+// The exact search (exact_row) for the rows k_ssz_rows and the k_ssz instances without the inline search defer
+// (scale[n] is NaN), one row at a time per block of 256 threads.  Rows with a finite scale are left as they are.
 
 template <int DT, bool HAS_S, int BITS, bool ASYM>
 __global__ __launch_bounds__(kExactTpr) void k_ssz_exact(const void* __restrict__ w, int64_t N, int64_t K,
@@ -800,56 +958,11 @@ __global__ __launch_bounds__(kExactTpr) void k_ssz_exact(const void* __restrict_
                                                          int32_t* __restrict__ zero_point, void* __restrict__ wq,
                                                          int32_t* __restrict__ iters, double* __restrict__ mse) {
   constexpr int NW = kExactTpr / kWave;
-  constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
   __shared__ double xd[4 * NW];
   __shared__ float xf[2 * NW];
   __shared__ int flag;                // deferred rows in the current chunk
   __shared__ int list[kExactTpr];     // and their indices in the chunk
   const int tid = threadIdx.x;
-  const double Kd = (double)K;
-  const DivK per_elem = make_divk(K);
-
-  // sums over the block (every thread gets the same bits)
-  auto bsum_dd = [&](DD v) -> double {
-    v = group_sum_dd<64>(v);
-    __syncthreads();
-    if ((tid & (kWave - 1)) == 0) {
-      xd[tid / kWave] = v.hi;
-      xd[NW + tid / kWave] = v.lo;
-    }
-    __syncthreads();
-    DD t{xd[0], xd[NW]};
-#pragma unroll
-    for (int i = 1; i < NW; ++i) t = dd_add(t, DD{xd[i], xd[NW + i]});
-    return t.hi + t.lo;
-  };
-  auto bsum = [&](double v) -> double {  // exact integer sums
-    v = wave_sum(v);
-    __syncthreads();
-    if ((tid & (kWave - 1)) == 0) xd[2 * NW + tid / kWave] = v;
-    __syncthreads();
-    double t = xd[2 * NW];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) t += xd[2 * NW + i];
-    return t;
-  };
-  auto bminmax = [&](float& lo, float& hi) {
-    lo = -wave_max(-lo);
-    hi = wave_max(hi);
-    __syncthreads();
-    if ((tid & (kWave - 1)) == 0) {
-      xf[tid / kWave] = lo;
-      xf[NW + tid / kWave] = hi;
-    }
-    __syncthreads();
-    lo = xf[0];
-    hi = xf[NW];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) {
-      lo = fminf(lo, xf[i]);
-      hi = fmaxf(hi, xf[NW + i]);
-    }
-  };
 
   // chunks of kExactTpr rows: every thread reads one row's scale, the deferred rows of the chunk are listed in
   // LDS (in any order), then searched one at a time by the whole block
@@ -861,96 +974,9 @@ __global__ __launch_bounds__(kExactTpr) void k_ssz_exact(const void* __restrict_
     if (mine < N && __builtin_isnan(scale[mine])) list[atomicAdd(&flag, 1)] = (int)tid;
     __syncthreads();
     const int count = flag;
-    for (int li = 0; li < count; ++li) {
-      const int64_t n = ch * kExactTpr + list[li];
-
-      float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
-      DD w1{0.0, 0.0};
-      for (int64_t k = tid; k < K; k += kExactTpr) {
-        const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
-        if constexpr (ASYM) {
-          lo = fminf(lo, v);
-          hi = fmaxf(hi, v);
-          w1 = dd_add_d(w1, (double)v);
-        } else {
-          hi = fmaxf(hi, fabsf(v));
-        }
-      }
-      bminmax(lo, hi);
-      const double W1 = ASYM ? bsum_dd(w1) : 0.0;
-
-      // P, R2, R1 and the mean error of (S, Z), every sum exact
-      auto pass = [&](float S, int Z, double& P, double& R2, double& R1) -> double {
-        const float zf = (float)Z;
-        const double Sd = (double)S;
-        DD p{0.0, 0.0}, e{0.0, 0.0};
-        double r2 = 0.0, r1 = 0.0;
-        for (int64_t k = tid; k < K; k += kExactTpr) {
-          const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
-          const float r = rel_code_ieee<ASYM>(v, S, zf, QMAX);
-          p = dd_add_d(p, (double)v * (double)r);  // exact product
-          double dh, dl;
-          two_sum((double)v, -(Sd * (double)r), dh, dl);  // S r is exact in fp64
-          DD t = two_sqr(dh);
-          t.lo += dh * (2.0 * dl) + dl * dl;
-          e = dd_add(e, t);
-          r2 += (double)r * (double)r;
-          r1 += (double)r;
-        }
-        P = bsum_dd(p);
-        R2 = bsum(r2);
-        R1 = ASYM ? bsum(r1) : 0.0;
-        return per_elem(bsum_dd(e));
-      };
-
-      RowState st;
-      minmax_init<ASYM>(lo, hi, QMAX, min_scale, st.S, st.Z);
-      const double b0 = pass(st.S, st.Z, st.P, st.R2, st.R1);
-      double best = b0;
-      int it = 0;
-      for (int i = 1; i <= max_iter; ++i) {
-        it = i;
-        float Sc;
-        int Zc;
-        if (!refit<ASYM>(st, Kd, W1, per_elem, min_scale, Sc, Zc)) break;
-        RowState c;
-        c.S = Sc;
-        c.Z = Zc;
-        const double cur = pass(Sc, Zc, c.P, c.R2, c.R1);
-        const double d = best - cur;
-        const bool conv = (best == 0.0) || (fabs(d) < thr) || (d / best < thr);
-        if (cur < best) {
-          st = c;
-          best = cur;
-        }
-        if (conv) break;
-      }
-
-      // codes of the kept parameters
-      if (wq) {
-        const float zf = (float)st.Z;
-        for (int64_t k = tid; k < K; k += kExactTpr) {
-          const float v = load_folded<DT, HAS_S>(w, s, n, K, k);
-          const float q = rel_code_ieee<ASYM>(v, st.S, zf, QMAX) + (ASYM ? zf : 0.0f);
-          if constexpr (BITS == 8) {
-            reinterpret_cast<int8_t*>(wq)[n * K + k] = (int8_t)(int)q;
-          } else {
-            // two codes per byte: the thread of the even element writes the pair
-            const float v1 = load_folded<DT, HAS_S>(w, s, n, K, k ^ 1);
-            const float q1 = rel_code_ieee<false>(v1, st.S, 0.0f, QMAX);
-            if ((k & 1) == 0)
-              reinterpret_cast<uint8_t*>(wq)[n * (K / 2) + k / 2] =
-                  (uint8_t)(((uint32_t)(int)q & 0xFu) | (((uint32_t)(int)q1 & 0xFu) << 4));
-          }
-        }
-      }
-      if (tid == 0) {
-        scale[n] = st.S;
-        if constexpr (ASYM) zero_point[n] = st.Z;
-        if (iters) iters[n] = it;
-        if (mse) mse[n] = best;
-      }
-    }
+    for (int li = 0; li < count; ++li)
+      exact_row<DT, HAS_S, BITS, ASYM, kExactTpr>(w, ch * kExactTpr + list[li], K, s, max_iter, thr, min_scale, scale,
+                                                  zero_point, wq, iters, mse, xd, xf, tid);
     __syncthreads();  // the chunk's list is read by all before the next chunk rebuilds it
   }
 }
@@ -974,6 +1000,7 @@ hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max
     PTQ_SR(1) PTQ_SR(2) PTQ_SR(4) PTQ_SR(8) PTQ_SR(16) PTQ_SR(32)
 #undef PTQ_SR
   }
+  bool exact_launch = launched;  // the short-row kernel leaves its deferred rows to k_ssz_exact
   if (!launched) {
     // longer rows: about 64 elements per thread; one wave per row up to K = 4096
     int tpr = 64;
@@ -984,6 +1011,7 @@ hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max
     k_ssz<DT, HAS_S, BITS, ASYM, TPR_, CPT_><<<(unsigned)N, TPR_, 0, stream>>>(                           \
         w, N, K, s, max_iter, thr, min_scale, scale, zp, wq, iters, mse);                                 \
     launched = true;                                                                                      \
+    exact_launch = !ssz_inline_exact(ASYM, TPR_);                                                         \
   }
     PTQ_S(64, 1) PTQ_S(64, 2) PTQ_S(64, 4)
     PTQ_S(128, 4) PTQ_S(256, 4) PTQ_S(512, 4) PTQ_S(1024, 4) PTQ_S(1024, 8)
@@ -991,7 +1019,7 @@ hipError_t dispatch(const void* w, int64_t N, int64_t K, const float* s, int max
   }
   if (!launched) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !exact_launch) return e;
   // the deferred rows, if any: a block per chunk of kExactTpr rows (up to 1024 blocks), which reads the chunk's
   // scales first, so a launch with nothing deferred costs one load per row
   const int64_t nchunks = (N + kExactTpr - 1) / kExactTpr;
