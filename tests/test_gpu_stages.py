@@ -664,13 +664,14 @@ def _scaled_rows(rng, N, K, scales):
     return (w * np.resize(np.asarray(scales, np.float64), N)[:, None]).astype(np.float32)
 
 
-@pytest.mark.parametrize("K", [64, 320, 1024, 4096, 8192, 16384])
+@pytest.mark.parametrize("K", [64, 320, 1024, 2048, 4096, 8192, 16384])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_ssz_deferred_scales(pq, K, bits):
     """Rows whose scale leaves [2^-100, 2^100] (tiny rows under a tiny floor, huge rows) mixed with ordinary
     rows: those rows are searched again exactly, the others keep the fast path; every row as the oracle.  K spans
-    the short-row kernel (64, 320), the row kernels that search such rows themselves (1024 to 8192) and one that
-    leaves them to the separate exact launch (16384)."""
+    the short-row kernel (64, 320), the row kernels that search such rows themselves (1024 to 8192: one, two and
+    four chunks per lane, one and two waves per row) and one that leaves them to the separate exact launch
+    (16384)."""
     rng = np.random.default_rng(K + bits)
     w = _scaled_rows(rng, 96, K, [1.0, 1e-33, 3.0, 1e32, 0.5])
     w[7] = 0.0
